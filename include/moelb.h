@@ -1,0 +1,239 @@
+/*
+ * moelb -- MoE routing-and-balancing hot path for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer step on one GPU, with the expert-parallel group's G ranks kept
+ * as integer bookkeeping:
+ *
+ *   moelb_gate_topk   router GEMM + softmax + top-k, and the lookahead router
+ *   moelb_histogram   per-rank token-expert counts
+ *   moelb_plan        locality-aware replication plan (Phase 1, Phase 2)
+ *   moelb_split       all-integer pairwise-halving split of remote pools
+ *   moelb_permute     local/remote, rank- and expert-sorted pair order (+ rows)
+ *   moelb_grouped_ffn masked grouped SwiGLU expert GEMMs
+ *   moelb_combine     top-k weighted sum of expert outputs (+ shared expert)
+ *
+ * Conventions for every entry point:
+ *  - Plain C ABI.  Every pointer argument is DEVICE memory owned by the caller
+ *    (e.g. a PyTorch tensor's data pointer), unless stated otherwise; the
+ *    library keeps no pointer after the call returns and allocates nothing.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting; outputs are valid once the stream has
+ *    reached that point.
+ *  - Arguments are checked on the host before anything is launched.  A bad
+ *    argument returns MOELB_EINVAL and launches nothing.  Sizes must be exact
+ *    multiples where stated: unsupported shapes are errors, never fallbacks.
+ *  - Contents of device buffers cannot be checked on the host; for each entry
+ *    point the behaviour on out-of-range device values is stated and is memory
+ *    safe.
+ *  - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16); fp32 is IEEE
+ *    binary32.  Matrices are row-major.
+ *  - Thread safety: calls keep no state and may be made from several threads.
+ */
+#ifndef MOELB_H
+#define MOELB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moelb_status {
+  MOELB_OK = 0,
+  MOELB_EINVAL = 1,     /* bad argument; nothing was launched                  */
+  MOELB_ELAUNCH = 2,    /* a kernel launch or runtime call failed              */
+  MOELB_EWORKSPACE = 3  /* workspace pointer NULL or smaller than required     */
+};
+
+enum moelb_dtype {
+  MOELB_F32 = 0,        /* fp32 storage and fp32 arithmetic                    */
+  MOELB_BF16 = 1        /* bf16 storage, fp32 accumulation (MFMA)             */
+};
+
+/* Limits checked by every entry point. */
+#define MOELB_MAX_E 256   /* experts                  */
+#define MOELB_MAX_K 16    /* experts per token        */
+#define MOELB_MAX_G 64    /* virtual EP ranks         */
+#define MOELB_MAX_N 8     /* replica slots per rank   */
+
+int moelb_version(void);                  /* major*10000 + minor*100 + patch */
+const char* moelb_status_string(int status);
+
+/*
+ * Router of the current layer and lookahead router of the next layer.
+ *
+ * Computes, per token t (FreeBalance, "FreeBalance: Pre-Routing Online MoE Load
+ * Balancing via Residual Workload Prediction", section 2.1 and eq. 2-4; Libra
+ * README "Key Ideas", lookahead predictor):
+ *   z[t,e]   = h[t,:] . w_cur[e,:] + b_cur[e]           (fp32 accumulation)
+ *   idx[t,:] = the k experts with the largest z, by descending z, ties to the
+ *              lower expert id
+ *   wts[t,j] = softmax over all E of z[t,:], at expert idx[t,j] (no
+ *              renormalisation over the top-k)
+ *   gap[t]   = z_(k) - z_(k+1), k-th minus (k+1)-th largest (+inf if k == E)
+ *   idx_next = the same top-k rule on h[t,:] . w_next[e,:] + b_next[e]
+ *
+ *  h       [T,d]  dtype          hidden states of the current layer
+ *  w_cur   [E,d]  dtype          router weight, one row per expert
+ *  b_cur   [E]    fp32           router bias
+ *  w_next  [E,d]  dtype or NULL  next layer's router (NULL: no lookahead,
+ *  b_next  [E]    fp32 or NULL                        idx_next must be NULL)
+ *  idx     [T,k]  int32  out
+ *  wts     [T,k]  fp32   out
+ *  gap     [T]    fp32   out, may be NULL
+ *  idx_next[T,k]  int32  out, NULL iff w_next is NULL
+ * Requires 1 <= k <= min(E, 16), E <= 256, d % 8 == 0, T >= 0.
+ */
+int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dtype,
+                    const void* w_cur, const float* b_cur,
+                    const void* w_next, const float* b_next,
+                    int32_t* idx, float* wts, float* gap, int32_t* idx_next,
+                    void* stream);
+
+/*
+ * Per-rank histogram (Libra "Key Ideas": demand of each GPU's own tokens;
+ * FreeBalance eq. 5: the workload vector n_e is the column sum).
+ *   counts[s,e] = #{(t,j) : t div (T/G) == s, idx[t,j] == e}
+ *  idx          [T,k] int32
+ *  counts       [G,E] int32 out (overwritten)
+ *  expert_total [E]   int32 out or NULL: column sums of counts
+ * Ids outside [0,E) are not counted.  Requires T % G == 0, G <= 64, E <= 256.
+ */
+int moelb_histogram(const int32_t* idx, int T, int k, int E, int G,
+                    int32_t* counts, int32_t* expert_total, void* stream);
+
+/*
+ * Locality-aware replication plan (Libra README "Key Ideas": Phase 1 imports
+ * the L = N*alpha non-resident experts most requested by each GPU's own
+ * tokens; Phase 2 repeatedly replicates the hottest expert of the most-loaded
+ * GPU to the least-loaded eligible GPU).  Exact rules:
+ *  Phase 1: per rank r, experts e with home[e] != r and counts[r,e] > 0, by
+ *    counts[r,e] descending then e ascending; the first min(L, N) are imported.
+ *  Load model: a host of e serves its own tokens of e plus its share of e's
+ *    remote pool R(e) (pairs of e owned by non-hosts), split evenly in whole
+ *    tokens over the hosts by ascending rank (R div m each, the first R mod m
+ *    hosts one more).
+ *  Phase 2, while some rank has a free slot: a = most-loaded rank (ties: lower
+ *    rank).  Among experts hosted at a with R(e) > 0, walk by a's load of e
+ *    descending (ties: lower e); b = least-loaded rank (ties: lower) that does
+ *    not host e and has a free slot; take the first move with
+ *    max(load_a', load_b') < load_a.  Stop when a has no such move.
+ *  counts    [G,E] int32   (predicted counts, e.g. from the lookahead)
+ *  home      [E]   int32   resident rank of each expert, in [0,G)
+ *  replica   [G,N] int32 out: imports of each rank in import order, -1 padded
+ *  plan_load [G]   int32 out or NULL: modeled loads of the final plan
+ * Requires 0 <= L <= N <= 8, G <= 64, E <= 256.  home entries outside [0,G)
+ * are read as rank 0.  Counts must be >= 0 and their total below 2^31.
+ */
+int moelb_plan(const int32_t* counts, const int32_t* home, int G, int E, int N, int L,
+               int32_t* replica, int32_t* plan_load, void* stream);
+
+/*
+ * All-integer per-step split (Relief, "A Per-Step Load-Balancing Engine for
+ * Expert-Parallel MoE Serving", "The Relief Algorithm", Algorithm 1).
+ *  Hosts H(e) = home[e] plus every rank whose replica row lists e (entries -1,
+ *  outside [0,E) or equal to the home are ignored; repeats count once).
+ *  Fixed load: each host serves its own tokens of e; an unreplicated expert's
+ *  whole remote pool goes to its home.  A replicated expert's pool starts
+ *  evenly split (as in moelb_plan).  One transfer (home(e), v, e) per replica
+ *  rank v, listed by e then v ascending; greedy edge colouring (smallest
+ *  colour free at both ranks) gives rank-disjoint rounds.  `passes` times, for
+ *  every round in colour order, every transfer of the round does
+ *    gap = load[u]-load[v]; delta = min(|gap| >> 1, mass of the heavier side);
+ *    if delta > eps, move delta pairs from the heavier to the lighter rank,
+ *  and the next round reads the updated loads.
+ *  counts     [G,E] int32   actual counts of this step
+ *  home       [E]   int32
+ *  replica    [G,N] int32   placement in force for this step
+ *  host_count [E,G] int32 out: remote pairs of e served by rank r (0 at
+ *                            non-hosts; the whole pool at home if unreplicated)
+ *  load       [G]   int32 out: rank loads after the split
+ * Requires 0 <= passes <= 1024, eps >= 0, G <= 64, N <= 8, E <= 256.
+ */
+int moelb_split(const int32_t* counts, const int32_t* home, const int32_t* replica,
+                int G, int E, int N, int passes, int eps,
+                int32_t* host_count, int32_t* load, void* stream);
+
+/*
+ * Local/remote permutation (Libra README "Key Ideas": two-stage locality-aware
+ * execution, MoE_local on the token's own GPU, MoE_remote on the others).
+ *  Pair p = t*k + j, expert e = idx[t,j], owner s = t div (T/G).  Local
+ *  (segment 0, destination s) if s hosts e; otherwise remote (segment 1): with
+ *  rho = number of remote pairs of e with a smaller pair id, the destination is
+ *  the first host h (ascending rank) with rho < sum_{h' <= h} host_count[e,h']
+ *  (negative entries read as 0); pairs past that sum go to the highest host.
+ *  Group key (segment*G + destination)*E + e.  perm lists pair ids by (key,
+ *  pair id); pos is its inverse; group_off is the exclusive prefix of the
+ *  2*G*E group sizes.  Pairs whose id is outside [0,E) are left out: pos = -1,
+ *  and group_off[2GE] counts only valid pairs.
+ *  h          [T,d]    dtype         rows to gather (may be NULL iff x_perm is NULL)
+ *  idx        [T,k]    int32
+ *  home       [E], replica [G,N], host_count [E,G]   int32 (from moelb_split)
+ *  ws         workspace of moelb_permute_workspace_bytes(T,k,E,G) bytes
+ *  group_off  [2*G*E+1] int32 out
+ *  perm, pos  [T*k]     int32 out
+ *  x_perm     [T*k,d]   dtype out or NULL: x_perm[q] = h[perm[q] div k]
+ * Requires T % G == 0, k <= 16, E <= 256, G <= 64, N <= 8, d % 8 == 0.
+ */
+size_t moelb_permute_workspace_bytes(int T, int k, int E, int G);
+int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                  int dtype, const int32_t* home, const int32_t* replica,
+                  const int32_t* host_count, void* ws, size_t ws_bytes,
+                  int32_t* group_off, int32_t* perm, int32_t* pos, void* x_perm,
+                  void* stream);
+
+/*
+ * Masked grouped SwiGLU expert FFN (Libra README "Repository Layout": FusedMoE
+ * over masked tokens; FreeBalance section 2.1: expert_i(h)).
+ *  Group g covers rows [group_off[g], group_off[g+1]) and uses expert g mod E
+ *  (replicas alias the expert's weights).  With rank >= 0 only groups whose
+ *  rank (g div E) mod G equals `rank` are computed (one virtual rank's share);
+ *  rank = -1 computes all groups.  For each computed row q:
+ *    a = SiLU(x_q . W13[e, 0:I]^T) * (x_q . W13[e, I:2I]^T)   (rounded to dtype)
+ *    y[q] = a . W2[e]^T                                       (rounded to dtype)
+ *  with fp32 accumulation.  x_q is x[q], or x[gather[q] div gather_k] when
+ *  `gather` is given (the rows are read straight from the unpermuted hidden
+ *  states: pass moelb_permute's perm and the top-k).  Rows outside every
+ *  computed group are not written.
+ *  x          [rows_x,d]  dtype    rows (X_perm, or h when gather is given)
+ *  group_off  [num_groups+1] int32 non-decreasing offsets, <= rows
+ *  gather     [rows] int32 or NULL; gather_k >= 1
+ *  w13        [E,2*inter,d] dtype  gate rows then up rows, K-contiguous
+ *  w2         [E,d,inter]   dtype  K-contiguous
+ *  ws         workspace of moelb_grouped_ffn_workspace_bytes(...) bytes
+ *  y          [rows,d]      dtype out
+ *  events     NULL or 4 hipEvent_t recorded on `stream`: before the schedule
+ *             kernel, before the gate/up GEMM, before the down GEMM, after it.
+ *  Device offsets outside [0, rows] are clamped into it; gather entries
+ *  outside [0, rows_x*gather_k) read row 0.
+ * Requires rows >= 0, d % 8 == 0, inter % 8 == 0, E <= 256,
+ * num_groups % E == 0 when rank >= 0, num_groups <= 32768.
+ */
+size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, int E, int d, int inter,
+                                         int dtype);
+int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_off,
+                      int num_groups, int E, int G, int rank,
+                      const int32_t* gather, int gather_k,
+                      int d, int inter, int dtype, const void* w13, const void* w2,
+                      void* ws, size_t ws_bytes, void* y, void* stream, void* const* events);
+
+/*
+ * Top-k weighted combine (FreeBalance section 2.1: MoE(h) = sum_i W_i
+ * expert_i(h); Libra "Repository Layout": the combine kernel).
+ *   out[t] = sum_{j=0..k-1, ascending} wts[t,j] * y[pos[t*k+j]]  (+ shared[t])
+ *  accumulated in fp32 and rounded to dtype.  Pairs with pos < 0 or
+ *  pos >= rows_y contribute nothing.
+ *  y      [rows_y,d] dtype
+ *  pos    [T*k] int32, wts [T*k] fp32
+ *  shared [T,d] dtype or NULL (added unweighted)
+ *  out    [T,d] dtype out
+ * Requires d % 8 == 0, 1 <= k <= 16.
+ */
+int moelb_combine(const void* y, int rows_y, const int32_t* pos, const float* wts, int T, int k,
+                  int d, int dtype, const void* shared, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOELB_H */

@@ -483,16 +483,15 @@ def moe_via_groups(h64: np.ndarray, idx: np.ndarray, w: np.ndarray, expert: Expe
     out[t] = sum_j w[t,j] * Y[pos[t*k+j]] with j ascending.  Returns (out, Y)."""
     T, k = idx.shape
     Y = np.zeros((len(perm), h64.shape[1]))
-    cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
-    for g in range(len(group_off) - 1):
-        a, b = int(group_off[g]), int(group_off[g + 1])
-        if a == b:
+    ngroups = len(group_off) - 1
+    for e in range(E):
+        # every group of expert e (rows are independent, so they run together)
+        rows = [np.arange(int(group_off[g]), int(group_off[g + 1])) for g in range(e, ngroups, E)]
+        rows = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+        if len(rows) == 0:
             continue
-        e = g % E
-        if e not in cache:
-            cache = {e: expert(e)}
-        w13, w2 = cache[e]
-        Y[a:b] = swiglu(h64[np.asarray(perm[a:b]) // k], w13, w2)
+        w13, w2 = expert(e)
+        Y[rows] = swiglu(h64[np.asarray(perm)[rows] // k], w13, w2)
     return combine(Y, pos, w, T, k), Y
 
 

@@ -1,0 +1,74 @@
+// Shared device helpers for the moelb kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moelb.h"
+
+#define MOELB_WAVE 64
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even.  NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float silu_f32(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (MOELB_WAVE - 1); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOELB_WAVE);
+  return v;
+}
+
+// ---------------------------------------------------------------- host helpers
+
+#define MOELB_CHECK_LAUNCH()                                   \
+  do {                                                         \
+    if (hipGetLastError() != hipSuccess) return MOELB_ELAUNCH; \
+  } while (0)
+
+static inline size_t moelb_align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+static inline bool moelb_dtype_ok(int dtype) { return dtype == MOELB_F32 || dtype == MOELB_BF16; }
+static inline size_t moelb_elem_bytes(int dtype) { return dtype == MOELB_F32 ? 4 : 2; }
+
+// Kernels that use more than 64 KiB of dynamic LDS must opt in (gfx950 has 160 KiB per CU).
+template <typename Kern>
+static inline bool moelb_allow_lds(Kern kernel, size_t bytes) {
+  if (bytes <= 65536) return true;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(bytes)) == hipSuccess;
+}

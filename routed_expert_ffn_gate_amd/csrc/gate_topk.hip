@@ -1,0 +1,359 @@
+// Router GEMM of the current layer and the lookahead router of the next layer,
+// with softmax, top-k and the k-th/(k+1)-th logit gap fused into the epilogue.
+//
+// Definition: FreeBalance ("FreeBalance: Pre-Routing Online MoE Load Balancing
+// via Residual Workload Prediction"), section 2.1 (W,I = topk(G(h))) and
+// eq. 2-4 (the same linear router g(X) = XW + 1b^T applied to the previous
+// layer's hidden states); Libra README "Key Ideas" (layer i+1's gate on layer
+// i's hidden states).
+//
+// Design (gfx950): one GEMM with N = 2E columns (current router rows, then the
+// lookahead router's rows), so h -- the only large operand -- is read from HBM
+// once.  A workgroup owns 128 tokens and all N columns, so every logit of a
+// token ends up in one workgroup for the epilogue.  8 waves: 2 (token halves) x
+// 4 (column quarters); each wave runs bf16 MFMA 16x16x32 on a 64 x (16*NF)
+// tile.  h tiles are staged through LDS (double buffered, one barrier per K
+// step); router rows go straight from global/L2 into registers, since each
+// wave needs only its own columns.  The epilogue writes biased fp32 logits to
+// LDS (one token half at a time) and 4 lanes per token and direction select
+// the top-(k+1) with a register insertion list, merged across the 4 lanes with
+// two xor shuffles.
+#include "common.h"
+
+namespace {
+
+constexpr int GATE_BM = 128;       // tokens per workgroup
+constexpr int GATE_BK = 64;        // K per pipeline step
+constexpr int GATE_THREADS = 512;  // 8 waves
+constexpr int A_STRIDE = GATE_BK + 8;  // bf16 elements per LDS row (16 B pad)
+
+__device__ __forceinline__ bool better(float v, int id, float v2, int id2) {
+  // bitwise, not short-circuit: keeps the unrolled merge branch-free
+  return (v > v2) | ((v == v2) & (id < id2));
+}
+
+// Sorted (descending, ties lower id) insertion into a register list of length KL.
+template <int KL>
+__device__ __forceinline__ void list_insert(float (&lv)[KL], int (&li)[KL], float x, int xi) {
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    const bool b = better(x, xi, lv[i], li[i]);
+    const float tv = b ? x : lv[i];
+    const int ti = b ? xi : li[i];
+    x = b ? lv[i] : x;
+    xi = b ? li[i] : xi;
+    lv[i] = tv;
+    li[i] = ti;
+  }
+}
+
+// Epilogue over `ntok` tokens whose logits (bias included) sit in LDS rows of
+// `stride` floats: columns [0,E) current, [E,2E) lookahead (if has_next).
+// 512 threads: direction = tid / 256, token = (tid % 256) / 4, sub = tid % 4.
+template <int KL>
+__device__ void topk_epilogue(const float* z, int stride, int ntok, int tok0, int T, int E, int k,
+                              bool has_next, int32_t* __restrict__ idx, float* __restrict__ wts,
+                              float* __restrict__ gap, int32_t* __restrict__ idx_next) {
+  const int tid = threadIdx.x;
+  const int dir = tid >> 8;
+  const int tl = (tid & 255) >> 2;
+  const int sub = tid & 3;
+  const bool active = tl < ntok && (dir == 0 || has_next);
+  const int t = tok0 + tl;
+  float lv[KL];
+  int li[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) {
+    lv[i] = -INFINITY;
+    li[i] = 0x7fffffff;
+  }
+  const float* row = z + tl * stride + dir * E;
+  if (active) {
+    for (int e = sub; e < E; e += 4) list_insert<KL>(lv, li, row[e], e);
+  }
+  // merge the four partial lists (lanes sub ^ 1, then sub ^ 2)
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {
+    float pv[KL];
+    int pi[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      pv[i] = __shfl_xor(lv[i], m, MOELB_WAVE);
+      pi[i] = __shfl_xor(li[i], m, MOELB_WAVE);
+    }
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list_insert<KL>(lv, li, pv[i], pi[i]);
+  }
+  if (dir == 0) {
+    // softmax denominator over all E logits of this token
+    const float mx = lv[0];
+    float s = 0.f;
+    if (active)
+      for (int e = sub; e < E; e += 4) s += __expf(row[e] - mx);
+    s += __shfl_xor(s, 1, MOELB_WAVE);
+    s += __shfl_xor(s, 2, MOELB_WAVE);
+    if (active && sub == 0 && t < T) {
+      const float inv = 1.0f / s;
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        if (j < k) {
+          idx[(size_t)t * k + j] = li[j];
+          wts[(size_t)t * k + j] = __expf(lv[j] - mx) * inv;
+        }
+      }
+      if (gap) {
+        float g = INFINITY;
+#pragma unroll
+        for (int j = 1; j < KL; ++j)
+          if (j == k && k < E) g = lv[j - 1] - lv[j];
+        gap[t] = g;
+      }
+    }
+  } else if (active && sub == 0 && t < T) {
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      if (j < k) idx_next[(size_t)t * k + j] = li[j];
+  }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA kernel
+
+template <int NF, int KL>
+__global__ __launch_bounds__(GATE_THREADS) void gate_topk_bf16_kernel(
+    const uint16_t* __restrict__ h, int T, int d, int E, int k, const uint16_t* __restrict__ w_cur,
+    const float* __restrict__ b_cur, const uint16_t* __restrict__ w_next, const float* __restrict__ b_next,
+    int32_t* __restrict__ idx, float* __restrict__ wts, float* __restrict__ gap, int32_t* __restrict__ idx_next,
+    int zstride) {
+  extern __shared__ __align__(16) char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [2][GATE_BM][A_STRIDE]
+  float* Z = reinterpret_cast<float*>(smem);          // [64][zstride], after the K loop
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tok0 = blockIdx.x * GATE_BM;
+  const bool has_next = w_next != nullptr;
+  const int N = has_next ? 2 * E : E;
+
+  // A staging: 128 rows x 64 k = 1024 chunks of 16 B, two per thread.
+  int a_row[2], a_kc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid * 2 + i;
+    a_row[i] = c >> 3;
+    a_kc[i] = (c & 7) * 8;
+  }
+  // B: wave's columns, fragment ni covers columns colbase + ni*16 + (lane % 16).
+  const int colbase = wn * NF * 16;
+  const uint16_t* brow[NF];
+  bool bvalid[NF];
+#pragma unroll
+  for (int ni = 0; ni < NF; ++ni) {
+    const int col = colbase + ni * 16 + (lane & 15);
+    bvalid[ni] = col < N;
+    const uint16_t* base = col < E ? w_cur + (size_t)col * d : w_next + (size_t)(col - E) * d;
+    brow[ni] = bvalid[ni] ? base : w_cur;
+  }
+  const int bk = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide k step
+
+  f32x4_t acc[4][NF];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 areg[2];
+  bf16x8_t breg[2][NF];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = tok0 + a_row[i];
+      const int kk = k0 + a_kc[i];
+      areg[i] = (t < T && kk < d) ? *reinterpret_cast<const uint4*>(h + (size_t)t * d + kk) : zero4;
+    }
+  };
+  auto load_b = [&](int k0) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) {
+        const int kk = k0 + ks * 32 + bk;
+        const uint4 v = (bvalid[ni] && kk < d) ? *reinterpret_cast<const uint4*>(brow[ni] + kk) : zero4;
+        breg[ks][ni] = __builtin_bit_cast(bf16x8_t, v);
+      }
+  };
+
+  const int KT = (d + GATE_BK - 1) / GATE_BK;
+  load_a(0);
+  load_b(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    uint16_t* Ab = As + (kt & 1) * GATE_BM * A_STRIDE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Ab + a_row[i] * A_STRIDE + a_kc[i]) = areg[i];
+    bf16x8_t bcur[2][NF];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) bcur[ks][ni] = breg[ks][ni];
+    if (kt + 1 < KT) {
+      load_a((kt + 1) * GATE_BK);
+      load_b((kt + 1) * GATE_BK);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ab + r * A_STRIDE + ks * 32 + bk);
+#pragma unroll
+        for (int ni = 0; ni < NF; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bcur[ks][ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // LDS is reused for the logits
+
+  // Epilogue, one token half (64 rows) at a time.
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) {
+        const int col = colbase + ni * 16 + (lane & 15);
+        if (col < N) {
+          const float bias = col < E ? b_cur[col] : b_next[col - E];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = mi * 16 + (lane >> 4) * 4 + i;
+              Z[r * zstride + col] = acc[mi][ni][i] + bias;
+            }
+        }
+      }
+    }
+    __syncthreads();
+    const int t0 = tok0 + half * 64;
+    const int ntok = min(64, T - t0);
+    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, t0, T, E, k, has_next, idx, wts, gap, idx_next);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- fp32 kernel
+
+template <int KL>
+__global__ __launch_bounds__(GATE_THREADS) void gate_topk_f32_kernel(
+    const float* __restrict__ h, int T, int d, int E, int k, const float* __restrict__ w_cur,
+    const float* __restrict__ b_cur, const float* __restrict__ w_next, const float* __restrict__ b_next,
+    int32_t* __restrict__ idx, float* __restrict__ wts, float* __restrict__ gap, int32_t* __restrict__ idx_next,
+    int zstride) {
+  extern __shared__ __align__(16) char smem[];
+  float* Z = reinterpret_cast<float*>(smem);  // [64][zstride]
+  const int tok0 = blockIdx.x * 64;
+  const bool has_next = w_next != nullptr;
+  const int N = has_next ? 2 * E : E;
+  const int ntok = min(64, T - tok0);
+  for (int o = threadIdx.x; o < 64 * N; o += blockDim.x) {
+    const int tl = o / N, col = o % N;
+    if (tl >= ntok) continue;
+    const float* hr = h + (size_t)(tok0 + tl) * d;
+    const float* wr = col < E ? w_cur + (size_t)col * d : w_next + (size_t)(col - E) * d;
+    float s = 0.f;
+    for (int kk = 0; kk < d; kk += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(hr + kk);
+      const float4 b = *reinterpret_cast<const float4*>(wr + kk);
+      s = fmaf(a.x, b.x, s);
+      s = fmaf(a.y, b.y, s);
+      s = fmaf(a.z, b.z, s);
+      s = fmaf(a.w, b.w, s);
+    }
+    Z[tl * zstride + col] = s + (col < E ? b_cur[col] : b_next[col - E]);
+  }
+  __syncthreads();
+  topk_epilogue<KL>(Z, zstride, ntok, tok0, T, E, k, has_next, idx, wts, gap, idx_next);
+}
+
+int zstride_for(int N) { return ((N + 63) / 64) * 64 + 4; }
+
+template <int KL>
+int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
+                const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap,
+                int32_t* idx_next, hipStream_t s) {
+  const int N = w_next ? 2 * E : E;
+  const int zs = zstride_for(N);
+  const size_t lds_a = 2ull * GATE_BM * A_STRIDE * 2;
+  const size_t lds_z = 64ull * zs * 4;
+  const size_t lds = lds_a > lds_z ? lds_a : lds_z;
+  const dim3 grid((T + GATE_BM - 1) / GATE_BM);
+  const auto* hh = static_cast<const uint16_t*>(h);
+  const auto* wc = static_cast<const uint16_t*>(w_cur);
+  const auto* wx = static_cast<const uint16_t*>(w_next);
+#define MOELB_GATE_CASE(nf)                                                                        \
+  case nf:                                                                                         \
+    if (!moelb_allow_lds(gate_topk_bf16_kernel<nf, KL>, lds)) return MOELB_ELAUNCH;                \
+    hipLaunchKernelGGL((gate_topk_bf16_kernel<nf, KL>), grid, dim3(GATE_THREADS), lds, s, hh, T, d, E, k, \
+                       wc, b_cur, wx, b_next, idx, wts, gap, idx_next, zs);                        \
+    break;
+  switch (NF) {
+    MOELB_GATE_CASE(1)
+    MOELB_GATE_CASE(2)
+    MOELB_GATE_CASE(3)
+    MOELB_GATE_CASE(4)
+    MOELB_GATE_CASE(5)
+    MOELB_GATE_CASE(6)
+    MOELB_GATE_CASE(7)
+    MOELB_GATE_CASE(8)
+    default:
+      return MOELB_EINVAL;
+  }
+#undef MOELB_GATE_CASE
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+template <int KL>
+int launch_f32(const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
+               const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap,
+               int32_t* idx_next, hipStream_t s) {
+  const int N = w_next ? 2 * E : E;
+  const int zs = zstride_for(N);
+  const size_t lds = 64ull * zs * 4;
+  if (!moelb_allow_lds(gate_topk_f32_kernel<KL>, lds)) return MOELB_ELAUNCH;
+  hipLaunchKernelGGL((gate_topk_f32_kernel<KL>), dim3((T + 63) / 64), dim3(GATE_THREADS), lds, s,
+                     static_cast<const float*>(h), T, d, E, k, static_cast<const float*>(w_cur), b_cur,
+                     static_cast<const float*>(w_next), b_next, idx, wts, gap, idx_next, zs);
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+}  // namespace
+
+extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dtype, const void* w_cur,
+                               const float* b_cur, const void* w_next, const float* b_next, int32_t* idx,
+                               float* wts, float* gap, int32_t* idx_next, void* stream) {
+  if (T < 0 || d <= 0 || d % 8 != 0 || E < 1 || E > MOELB_MAX_E || k < 1 || k > MOELB_MAX_K || k > E)
+    return MOELB_EINVAL;
+  if (!moelb_dtype_ok(dtype)) return MOELB_EINVAL;
+  if (!w_cur || !b_cur || (w_next == nullptr) != (b_next == nullptr)) return MOELB_EINVAL;
+  if (T > 0 && (!h || !idx || !wts || (w_next == nullptr) != (idx_next == nullptr))) return MOELB_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(w_cur) |
+       reinterpret_cast<uintptr_t>(w_next)) & 15)
+    return MOELB_EINVAL;
+  if (T == 0) return MOELB_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MOELB_BF16) {
+    const int N = w_next ? 2 * E : E;
+    const int NF = (N + 63) / 64;
+    if (k <= 2) return launch_bf16<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    if (k <= 4) return launch_bf16<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    if (k <= 8) return launch_bf16<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    return launch_bf16<17>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  }
+  if (k <= 2) return launch_f32<3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  if (k <= 4) return launch_f32<5>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  if (k <= 8) return launch_f32<9>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  return launch_f32<17>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+}

@@ -1,0 +1,515 @@
+// Masked grouped SwiGLU expert FFN.
+//
+// Definition: FreeBalance ("FreeBalance: Pre-Routing Online MoE Load Balancing
+// via Residual Workload Prediction") section 2.1 -- each selected expert runs
+// on the token and the outputs are combined with the router weights; Libra
+// README "Repository Layout" -- a FusedMoE over masked tokens, with replicas
+// aliasing their expert's weights.  SwiGLU: a = SiLU(x W_gate^T) * (x W_up^T),
+// y = a W2^T.
+//
+// Design (gfx950):
+//  * Schedule kernel: rows of every selected group are renumbered
+//    expert-major ("virtual rows"): all groups of expert e (its local and
+//    remote groups on every rank) become one contiguous range, tiled by BM
+//    rows.  Replica groups of one expert therefore share M tiles, the weights
+//    of an expert stream through each M block once, and tail waste is per
+//    expert rather than per group.  Tile tables and the virtual->physical row
+//    map live in the caller's workspace; nothing is read back to the host.
+//  * Gate/up GEMM: M tile of 256 virtual rows gathered through the row map
+//    (optionally straight from h through the permutation, so X_perm need not
+//    exist), N tile = 128 gate rows + the matching 128 up rows of W13, so the
+//    SwiGLU is fused into the epilogue; writes a[v, :] in bf16, virtual-row
+//    order (contiguous for the next GEMM).
+//  * Down GEMM: a (contiguous) x W2^T, N tile 256, scatters y rows back to
+//    their physical (permuted) rows.
+//  * Both GEMMs: 512 threads (8 waves, 2 x 4), wave tile 128 x 64 on bf16
+//    MFMA 32x32x16 with fp32 accumulators, A and B tiles of 256 x 64 staged
+//    through LDS (double buffered, 144 KiB, one barrier per K step, rows padded
+//    by 16 B against bank conflicts), global loads for step k+1 in flight
+//    while step k computes.  Tile ids are remapped so each XCD (workgroups go
+//    round-robin over the 8 XCDs) works on a contiguous tile range, keeping A
+//    blocks and weight slices in its own L2.
+//  * fp32 storage uses a SIMT fp32 GEMM with the same schedule.
+#include "common.h"
+
+namespace {
+
+constexpr int MF_BM = 256;  // MFMA path M tile
+constexpr int MF_BN = 256;  // B rows per tile
+constexpr int MF_BK = 64;
+constexpr int MF_THREADS = 256;
+constexpr int MF_LDS_STRIDE = MF_BK + 8;  // bf16 elements per LDS row
+constexpr size_t MF_LDS_BYTES = 2ull * 2 * MF_BM * MF_LDS_STRIDE * sizeof(uint16_t);
+
+constexpr int SF_BM = 64;  // SIMT fp32 path
+constexpr int SF_BN = 64;
+constexpr int SF_BK = 16;
+
+constexpr int SCHED_MIN_BM = 64;
+
+struct FfnSched {
+  int32_t* eoff;      // [E+1]   virtual row offset of each expert
+  int32_t* gvb;       // [num_groups] virtual row base of each group, -1 if not computed
+  int32_t* mt_e;      // [max_mtiles] expert of each M tile
+  int32_t* mt_v0;     // [max_mtiles] first virtual row of each M tile
+  int32_t* n_mtiles;  // [1]
+  int32_t* rowmap;    // [rows] physical row of each virtual row
+  void* amid;         // [rows][inter] SwiGLU activations, virtual row order
+};
+
+inline size_t max_mtiles(int rows, int E) { return (size_t)(rows + SCHED_MIN_BM - 1) / SCHED_MIN_BM + E; }
+
+inline size_t sched_layout(int rows, int num_groups, int E, int inter, int dtype, FfnSched* s, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += moelb_align256(bytes);
+    return p;
+  };
+  const size_t mt = max_mtiles(rows, E);
+  char* p_eoff = take((size_t)(E + 1) * 4);
+  char* p_gvb = take((size_t)num_groups * 4);
+  char* p_mte = take(mt * 4);
+  char* p_mtv = take(mt * 4);
+  char* p_n = take(4);
+  char* p_rm = take((size_t)rows * 4);
+  char* p_am = take((size_t)rows * inter * moelb_elem_bytes(dtype));
+  if (s) {
+    s->eoff = reinterpret_cast<int32_t*>(p_eoff);
+    s->gvb = reinterpret_cast<int32_t*>(p_gvb);
+    s->mt_e = reinterpret_cast<int32_t*>(p_mte);
+    s->mt_v0 = reinterpret_cast<int32_t*>(p_mtv);
+    s->n_mtiles = reinterpret_cast<int32_t*>(p_n);
+    s->rowmap = reinterpret_cast<int32_t*>(p_rm);
+    s->amid = p_am;
+  }
+  return off;
+}
+
+// ---------------------------------------------------------------- schedule
+
+__global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ group_off, int num_groups, int E, int G,
+                                                    int rank, int rows, int BM, FfnSched s) {
+  __shared__ int ecount[MOELB_MAX_E];
+  __shared__ int eoff[MOELB_MAX_E + 1];
+  __shared__ int toff[MOELB_MAX_E + 1];
+  const int e = threadIdx.x;
+  if (e < E) {
+    int n = 0;
+    for (int g = e; g < num_groups; g += E) {
+      const bool sel = rank < 0 || ((g / E) % G) == rank;
+      const int lo = min(max(group_off[g], 0), rows);
+      const int hi = min(max(group_off[g + 1], lo), rows);
+      s.gvb[g] = sel ? n : -1;
+      if (sel) n += hi - lo;
+    }
+    ecount[e] = n;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long run = 0;
+    int trun = 0;
+    for (int x = 0; x < E; ++x) {
+      eoff[x] = (int)min(run, (long long)rows);
+      toff[x] = trun;
+      run += ecount[x];
+      const int nx = (int)min(run, (long long)rows) - eoff[x];
+      trun += (nx + BM - 1) / BM;
+    }
+    eoff[E] = (int)min(run, (long long)rows);
+    toff[E] = trun;
+    *s.n_mtiles = trun;
+  }
+  __syncthreads();
+  if (e < E) s.eoff[e] = eoff[e];
+  if (e == 0) s.eoff[E] = eoff[E];
+  if (e < E) {
+    for (int g = e; g < num_groups; g += E)
+      if (s.gvb[g] >= 0) s.gvb[g] += eoff[e];
+    for (int i = toff[e]; i < toff[e + 1]; ++i) {
+      s.mt_e[i] = e;
+      s.mt_v0[i] = eoff[e] + (i - toff[e]) * BM;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__ group_off, int E, int rows,
+                                                     FfnSched s) {
+  const int g = blockIdx.x;
+  const int vb = s.gvb[g];
+  if (vb < 0) return;
+  const int e = g % E;
+  const int vend = s.eoff[e + 1];
+  const int lo = min(max(group_off[g], 0), rows);
+  const int hi = min(max(group_off[g + 1], lo), rows);
+  for (int q = lo + threadIdx.x; q < hi; q += blockDim.x) {
+    const int v = vb + (q - lo);
+    if (v < vend) s.rowmap[v] = q;
+  }
+}
+
+// XCD-aware tile id: workgroups go round-robin over 8 XCDs; give each XCD a
+// contiguous range of tiles.  Returns -1 for workgroups with no tile.
+__device__ __forceinline__ int xcd_tile(int total) {
+  const int per = (total + 7) / 8;
+  const int bid = blockIdx.x;
+  const int t = (bid & 7) * per + (bid >> 3);
+  return ((bid >> 3) < per && t < total) ? t : -1;
+}
+
+// ---------------------------------------------------------------- bf16 MFMA GEMM
+
+// MODE 0: gate/up GEMM with SwiGLU epilogue -> amid (virtual rows, K = d).
+// MODE 1: down GEMM amid x W2^T -> y (physical rows, K = inter).
+//
+// 256 threads = 4 waves in a 2 x 2 grid; wave tile 128 x 128 = 4 x 4 MFMA
+// 32x32x16 fragments (256 fp32 accumulators per lane).  Global loads: lane
+// (tid & 7) takes one 16-byte chunk of rows (tid >> 3) + 32 i, so 8 lanes read
+// a 128-byte row segment.  Rows outside the tile's expert range read a valid
+// row (their results are discarded); only the K tail is zero-filled.
+template <int MODE>
+__global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __restrict__ x, int rows_x,
+                                                               const int32_t* __restrict__ gather, int gather_k,
+                                                               const uint16_t* __restrict__ w, FfnSched s, int d,
+                                                               int inter, int ntn, uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) char smem[];
+  const int tile = xcd_tile(*s.n_mtiles * ntn);
+  if (tile < 0) return;
+  const int mt = tile / ntn, nt = tile % ntn;
+  const int e = s.mt_e[mt];
+  const int v0 = s.mt_v0[mt];
+  const int vend = s.eoff[e + 1];
+  const int K = MODE == 0 ? d : inter;
+  const uint16_t* amid = static_cast<const uint16_t*>(s.amid);
+
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Bs = As + 2 * MF_BM * MF_LDS_STRIDE;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lc = (tid & 7) * 8;  // element offset of this lane's 16-byte chunk
+  const int lr0 = tid >> 3;       // first of its rows (then + 32 i)
+
+  // uniform bases; per-row 32-bit element offsets (the host checks they fit)
+  const uint16_t* abase = MODE == 0 ? x : amid;
+  const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = lr0 + 32 * i;
+    int v = v0 + r;
+    v = v < vend ? v : v0;  // tiles always start with a valid row
+    if (MODE == 0) {
+      const int q = s.rowmap[v];
+      int src = gather ? gather[q] / gather_k : q;
+      src = (src >= 0 && src < rows_x) ? src : 0;
+      aoff[i] = (uint32_t)src * (uint32_t)d;
+      int c = nt * 128 + (r & 127);
+      c = c < inter ? c : 0;
+      boff[i] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d;
+    } else {
+      aoff[i] = (uint32_t)v * (uint32_t)inter;
+      int c = nt * 256 + r;
+      c = c < d ? c : 0;
+      boff[i] = (uint32_t)c * (uint32_t)inter;
+    }
+  }
+
+  int nb[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+    nb[ni] = MODE == 0 ? (wn * 64 + (ni & 1) * 32 + (ni >> 1) * 128)  // gate 0, gate 1, up 0, up 1
+                       : (wn * 128 + ni * 32);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  uint4 ra[8], rb[8];
+  const int KT = (K + MF_BK - 1) / MF_BK;
+  const int fr = lane & 31;        // row (A) / column (B) of this lane in a fragment
+  const int fk = (lane >> 5) * 8;  // k offset inside a 16-wide k step
+
+  // full K step: no masks
+#define MOELB_FFN_GLOAD(K0)                                                       \
+  do {                                                                            \
+    const uint32_t kk_ = (uint32_t)((K0) + lc);                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                               \
+      ra[i] = *reinterpret_cast<const uint4*>(abase + (aoff[i] + kk_));           \
+      rb[i] = *reinterpret_cast<const uint4*>(bbase + (boff[i] + kk_));           \
+    }                                                                             \
+  } while (0)
+  // last, partial K step: every load stays inside its row; lanes past K zero
+#define MOELB_FFN_GLOAD_TAIL(K0)                                                  \
+  do {                                                                            \
+    const int kk_ = (K0) + lc;                                                    \
+    const bool ok_ = kk_ < K;                                                     \
+    const uint32_t ko_ = ok_ ? (uint32_t)kk_ : 0u;                                \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                               \
+      const uint4 ta = *reinterpret_cast<const uint4*>(abase + (aoff[i] + ko_));  \
+      const uint4 tb = *reinterpret_cast<const uint4*>(bbase + (boff[i] + ko_));  \
+      ra[i].x = ok_ ? ta.x : 0u;                                                  \
+      ra[i].y = ok_ ? ta.y : 0u;                                                  \
+      ra[i].z = ok_ ? ta.z : 0u;                                                  \
+      ra[i].w = ok_ ? ta.w : 0u;                                                  \
+      rb[i].x = ok_ ? tb.x : 0u;                                                  \
+      rb[i].y = ok_ ? tb.y : 0u;                                                  \
+      rb[i].z = ok_ ? tb.z : 0u;                                                  \
+      rb[i].w = ok_ ? tb.w : 0u;                                                  \
+    }                                                                             \
+  } while (0)
+  const int KTF = K / MF_BK;  // full K steps
+
+  if (KTF > 0)
+    MOELB_FFN_GLOAD(0);
+  else
+    MOELB_FFN_GLOAD_TAIL(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    uint16_t* Ab = As + (kt & 1) * MF_BM * MF_LDS_STRIDE;
+    uint16_t* Bb = Bs + (kt & 1) * MF_BM * MF_LDS_STRIDE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint4*>(Ab + (lr0 + 32 * i) * MF_LDS_STRIDE + lc) = ra[i];
+      *reinterpret_cast<uint4*>(Bb + (lr0 + 32 * i) * MF_LDS_STRIDE + lc) = rb[i];
+    }
+    if (kt + 1 < KTF)
+      MOELB_FFN_GLOAD((kt + 1) * MF_BK);
+    else if (kt + 1 < KT)
+      MOELB_FFN_GLOAD_TAIL((kt + 1) * MF_BK);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < MF_BK / 16; ++ks) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(Ab + (wm * 128 + mi * 32 + fr) * MF_LDS_STRIDE + ks * 16 + fk);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bb + (nb[ni] + fr) * MF_LDS_STRIDE + ks * 16 + fk);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+#undef MOELB_FFN_GLOAD
+#undef MOELB_FFN_GLOAD_TAIL
+
+  // Epilogue: stage the output tile in LDS as bf16, then write 16-byte chunks
+  // of whole row segments.  Accumulator layout: lane holds column (lane % 32)
+  // of each fragment, rows (r / 4) * 8 + (lane / 32) * 4 + r % 4.
+  constexpr int BN_OUT = MODE == 0 ? 128 : 256;
+  constexpr int CS = BN_OUT + 8;
+  uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      if (MODE == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float g = acc[mi][f][r], u = acc[mi][f + 2][r];
+          Cs[row * CS + wn * 64 + f * 32 + fr] = f32_to_bf16(silu_f32(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) Cs[row * CS + wn * 128 + ni * 32 + fr] = f32_to_bf16(acc[mi][ni][r]);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = BN_OUT / 8;  // 16-byte chunks per row
+  const int n0 = nt * BN_OUT;
+  const int nout = MODE == 0 ? inter : d;
+  for (int c = tid; c < MF_BM * CPR; c += MF_THREADS) {
+    const int row = c / CPR, ch = c % CPR;
+    const int v = v0 + row;
+    const int col = n0 + ch * 8;
+    if (v >= vend || col >= nout) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(Cs + row * CS + ch * 8);
+    if (MODE == 0) {
+      *reinterpret_cast<uint4*>(y + (size_t)v * inter + col) = val;
+    } else {
+      const int prow = min(max(s.rowmap[v], 0), rows_x - 1);
+      *reinterpret_cast<uint4*>(y + (size_t)prow * d + col) = val;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 SIMT GEMM
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_simt_kernel(const float* __restrict__ x, int rows_x,
+                                                       const int32_t* __restrict__ gather, int gather_k,
+                                                       const float* __restrict__ w, FfnSched s, int d, int inter,
+                                                       int ntn, float* __restrict__ y) {
+  __shared__ float As[SF_BK][SF_BM + 1];
+  __shared__ float Bs[SF_BK][SF_BN + 1];
+  __shared__ const float* arow[SF_BM];
+  __shared__ const float* brow[SF_BN];
+  const int tile = xcd_tile(*s.n_mtiles * ntn);
+  if (tile < 0) return;
+  const int mt = tile / ntn, nt = tile % ntn;
+  const int e = s.mt_e[mt];
+  const int v0 = s.mt_v0[mt];
+  const int vend = s.eoff[e + 1];
+  const int K = MODE == 0 ? d : inter;
+  const float* amid = static_cast<const float*>(s.amid);
+  const int tid = threadIdx.x;
+  if (tid < SF_BM) {
+    const int v = v0 + tid;
+    const float* p = nullptr;
+    if (v < vend) {
+      if (MODE == 0) {
+        const int q = s.rowmap[v];
+        int src = gather ? gather[q] / gather_k : q;
+        src = (src >= 0 && src < rows_x) ? src : 0;
+        p = x + (size_t)src * d;
+      } else {
+        p = amid + (size_t)v * inter;
+      }
+    }
+    arow[tid] = p;
+  } else if (tid < SF_BM + SF_BN) {
+    const int j = tid - SF_BM;
+    const float* p = nullptr;
+    if (MODE == 0) {
+      const int c = nt * 32 + (j & 31);
+      if (c < inter) p = w + ((size_t)e * 2 * inter + (j < 32 ? c : inter + c)) * d;
+    } else {
+      const int c = nt * 64 + j;
+      if (c < d) p = w + ((size_t)e * d + c) * inter;
+    }
+    brow[j] = p;
+  }
+  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += SF_BK) {
+    for (int i = tid; i < SF_BK * SF_BM; i += 256) {
+      const int r = i / SF_BK, kk = i % SF_BK;
+      const float* pa = arow[r];
+      As[kk][r] = (pa && k0 + kk < K) ? pa[k0 + kk] : 0.f;
+      const float* pb = brow[r];
+      Bs[kk][r] = (pb && k0 + kk < K) ? pb[k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < SF_BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      b[0] = Bs[kk][tx * 2];
+      b[1] = Bs[kk][tx * 2 + 1];
+      b[2] = Bs[kk][32 + tx * 2];
+      b[3] = Bs[kk][32 + tx * 2 + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = v0 + ty * 4 + i;
+    if (v >= vend) continue;
+    if (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = nt * 32 + tx * 2 + j;
+        if (c < inter) y[(size_t)v * inter + c] = silu_f32(acc[i][j]) * acc[i][j + 2];
+      }
+    } else {
+      const size_t prow = (size_t)min(max(s.rowmap[v], 0), rows_x - 1) * d;
+      const int cols[4] = {tx * 2, tx * 2 + 1, 32 + tx * 2, 32 + tx * 2 + 1};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = nt * 64 + cols[j];
+        if (c < d) y[prow + c] = acc[i][j];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, int E, int d, int inter, int dtype) {
+  (void)d;
+  if (rows < 0 || num_groups < 1 || E < 1 || inter < 1 || !moelb_dtype_ok(dtype)) return 0;
+  return sched_layout(rows, num_groups, E, inter, dtype, nullptr, nullptr);
+}
+
+extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_off, int num_groups, int E,
+                                 int G, int rank, const int32_t* gather, int gather_k, int d, int inter, int dtype,
+                                 const void* w13, const void* w2, void* ws, size_t ws_bytes, void* y, void* stream,
+                                 void* const* events) {
+  if (rows < 0 || rows_x < 0 || num_groups < 1 || num_groups > 32768 || E < 1 || E > MOELB_MAX_E) return MOELB_EINVAL;
+  if (d <= 0 || d % 8 != 0 || inter <= 0 || inter % 8 != 0 || !moelb_dtype_ok(dtype)) return MOELB_EINVAL;
+  if (rank >= 0 && (G < 1 || rank >= G || num_groups % E != 0)) return MOELB_EINVAL;
+  if (gather && gather_k < 1) return MOELB_EINVAL;
+  if (!group_off || !w13 || !w2 || (rows > 0 && (!x || !y))) return MOELB_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w13) | reinterpret_cast<uintptr_t>(w2) |
+       reinterpret_cast<uintptr_t>(y)) & 15)
+    return MOELB_EINVAL;
+  // 32-bit element offsets inside the GEMM kernels
+  if ((size_t)rows_x * d >= (1ull << 32) || (size_t)rows * inter >= (1ull << 32) ||
+      (size_t)2 * inter * d >= (1ull << 32))
+    return MOELB_EINVAL;
+  const size_t need = sched_layout(rows, num_groups, E, inter, dtype, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return MOELB_EWORKSPACE;
+  FfnSched sc;
+  sched_layout(rows, num_groups, E, inter, dtype, &sc, static_cast<char*>(ws));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto rec = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  };
+  const bool bf = dtype == MOELB_BF16;
+  const int BM = bf ? MF_BM : SF_BM;
+  rec(0);
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows, BM,
+                     sc);
+  MOELB_CHECK_LAUNCH();
+  hipLaunchKernelGGL(rowmap_kernel, dim3(num_groups), dim3(256), 0, s, group_off, E, rows, sc);
+  MOELB_CHECK_LAUNCH();
+  const size_t mtiles = (size_t)(rows + BM - 1) / BM + E;
+  if (bf) {
+    if (!moelb_allow_lds(ffn_mfma_kernel<0>, MF_LDS_BYTES) || !moelb_allow_lds(ffn_mfma_kernel<1>, MF_LDS_BYTES))
+      return MOELB_ELAUNCH;
+    const int ntn0 = (inter + 127) / 128;
+    const int ntn1 = (d + 255) / 256;
+    rec(1);
+    hipLaunchKernelGGL(ffn_mfma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                       static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13), sc,
+                       d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
+    MOELB_CHECK_LAUNCH();
+    rec(2);
+    hipLaunchKernelGGL(ffn_mfma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                       static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
+                       d, inter, ntn1, static_cast<uint16_t*>(y));
+    MOELB_CHECK_LAUNCH();
+  } else {
+    const int ntn0 = (inter + 31) / 32;
+    const int ntn1 = (d + 63) / 64;
+    rec(1);
+    hipLaunchKernelGGL(ffn_simt_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(256), 0, s, static_cast<const float*>(x),
+                       rows_x, gather, gather_k, static_cast<const float*>(w13), sc, d, inter, ntn0,
+                       static_cast<float*>(sc.amid));
+    MOELB_CHECK_LAUNCH();
+    rec(2);
+    hipLaunchKernelGGL(ffn_simt_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(256), 0, s,
+                       static_cast<const float*>(sc.amid), rows, nullptr, 1, static_cast<const float*>(w2), sc, d,
+                       inter, ntn1, static_cast<float*>(y));
+    MOELB_CHECK_LAUNCH();
+  }
+  rec(3);
+  return MOELB_OK;
+}

@@ -1,0 +1,201 @@
+"""One MoE layer step on one GPU, driven through the libmoelb C ABI.
+
+PyTorch only allocates device memory and supplies the stream; every stage
+runs in the HIP library:
+
+  gate_topk (current + lookahead) -> histogram x2 -> plan (next layer)
+  -> split (this step, with the plan made one step earlier) -> permute
+  -> grouped SwiGLU FFN (+ shared expert) -> combine
+
+The hidden-state rows are read by the gate/up GEMM straight from ``h``
+through the permutation (``gather_rows=True``, the default; the permutation
+then moves indices only), or from a materialised ``x_perm``
+(``gather_rows=False``).  ``materialize_x`` only allocates ``x_perm``.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import moelb as M
+
+STAGES = ["gate_topk", "histogram", "plan", "split", "permute", "grouped_ffn", "combine"]
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload an input array unchanged: bf16 bit patterns (uint16) become a
+    bfloat16 tensor with the same bits; fp32 stays fp32."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Download a tensor; bfloat16 comes back as uint16 bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class HipEvents:
+    """hipEvent_t handles from libamdhip64 (the events the library records)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = [ctypes.c_void_p() for _ in range(n)]
+        for e in self.ev:
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def handles(self, i0: int, n: int):
+        return [self.ev[i].value for i in range(i0, i0 + n)]
+
+    def record(self, i: int, stream) -> None:
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream)
+        if self.hip.hipEventRecord(self.ev[i], s) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        self.hip.hipEventSynchronize(self.ev[b])
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+@dataclass
+class StepOut:
+    idx: torch.Tensor
+    wts: torch.Tensor
+    gap: torch.Tensor
+    idx_next: torch.Tensor
+    counts: torch.Tensor
+    counts_next: torch.Tensor
+    replica_next: torch.Tensor
+    plan_load_next: torch.Tensor
+    host_count: torch.Tensor
+    load: torch.Tensor
+    group_off: torch.Tensor
+    perm: torch.Tensor
+    pos: torch.Tensor
+    x_perm: Optional[torch.Tensor]
+    y: torch.Tensor
+    shared: Optional[torch.Tensor]
+    out: torch.Tensor
+
+
+class MoELayer:
+    """Device buffers and the stage sequence of one layer step.
+
+    Shapes: T tokens, d hidden, E experts, top-k, inter, G virtual ranks, N
+    replica slots, L locality imports; ``dtype`` "bf16" or "f32"."""
+
+    def __init__(self, T, d, E, k, inter, G, N, L, dtype, device="cuda", shared_inter=0, passes=12,
+                 gather_rows=True, materialize_x=False):
+        self.T, self.d, self.E, self.k, self.inter = T, d, E, k, inter
+        self.G, self.N, self.L, self.passes = G, N, L, passes
+        self.dtype = dtype
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.dev = torch.device(device)
+        self.gather_rows = gather_rows
+        self.materialize_x = materialize_x or not gather_rows
+        P = T * k
+        i32 = dict(dtype=torch.int32, device=self.dev)
+        self.P = P
+        self.idx = torch.empty((T, k), **i32)
+        self.idx_next = torch.empty((T, k), **i32)
+        self.wts = torch.empty((T, k), dtype=torch.float32, device=self.dev)
+        self.gap = torch.empty((T,), dtype=torch.float32, device=self.dev)
+        self.counts = torch.empty((G, E), **i32)
+        self.counts_next = torch.empty((G, E), **i32)
+        self.replica_next = torch.empty((G, N), **i32)
+        self.plan_load_next = torch.empty((G,), **i32)
+        self.host_count = torch.empty((E, G), **i32)
+        self.load = torch.empty((G,), **i32)
+        self.group_off = torch.empty((2 * G * E + 1,), **i32)
+        self.perm = torch.empty((P,), **i32)
+        self.pos = torch.empty((P,), **i32)
+        self.x_perm = torch.empty((P, d), dtype=self.tdtype, device=self.dev) if self.materialize_x else None
+        self.y = torch.empty((P, d), dtype=self.tdtype, device=self.dev)
+        self.out = torch.empty((T, d), dtype=self.tdtype, device=self.dev)
+        self.shared_inter = shared_inter
+        self.shared = torch.empty((T, d), dtype=self.tdtype, device=self.dev) if shared_inter > 0 else None
+        self.shared_off = torch.tensor([0, T], **i32) if shared_inter > 0 else None
+        code = M.MOELB_BF16 if dtype == "bf16" else M.MOELB_F32
+        self.ws_perm = torch.empty((max(1, M.moelb_permute_workspace_bytes(T, k, E, G)),), dtype=torch.uint8,
+                                   device=self.dev)
+        self.ws_ffn = torch.empty((max(1, M.moelb_grouped_ffn_workspace_bytes(P, 2 * G * E, E, d, inter, code)),),
+                                  dtype=torch.uint8, device=self.dev)
+        self.ws_shared = None
+        if shared_inter > 0:
+            self.ws_shared = torch.empty((M.moelb_grouped_ffn_workspace_bytes(T, 1, 1, d, shared_inter, code),),
+                                         dtype=torch.uint8, device=self.dev)
+
+    # -- stages ---------------------------------------------------------------
+
+    def predict_plan(self, h_prev, w_cur, b_cur, home, replica_out, stream=None):
+        """Prologue: the previous step's lookahead for this layer (gate of this
+        layer on the previous hidden states), its histogram and plan."""
+        M.moelb_gate_topk(h_prev, w_cur, b_cur, None, None, self.idx_next, self.wts, None, None, stream=stream)
+        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
+        M.moelb_plan(self.counts_next, home, self.L, replica_out, None, stream=stream)
+
+    def step(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None, shared_w2=None,
+             stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
+        """One layer step.  With ``events``, marks ev_base+0..7 bracket the
+        seven stages and ev_base+8..11 are recorded inside the grouped FFN
+        (before its schedule, gate/up GEMM and down GEMM kernels, and after)."""
+        ev = events
+
+        def mark(i):
+            if ev is not None:
+                ev.record(ev_base + i, stream)
+
+        mark(0)
+        M.moelb_gate_topk(h, w_cur, b_cur, w_next, b_next, self.idx, self.wts, self.gap, self.idx_next, stream=stream)
+        mark(1)
+        M.moelb_histogram(self.idx, self.G, self.counts, stream=stream)
+        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
+        mark(2)
+        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=stream)
+        mark(3)
+        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes, stream=stream)
+        mark(4)
+        copy_rows = not self.gather_rows  # the gather GEMM reads h through perm instead
+        M.moelb_permute(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
+                        self.ws_perm, self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None,
+                        d=self.d, dtype=M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32, stream=stream)
+        mark(5)
+        ffn_ev = ev.handles(ev_base + 8, 4) if ev is not None else None
+        if self.gather_rows:
+            M.moelb_grouped_ffn(h, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
+                                gather=self.perm, gather_k=self.k, stream=stream, events=ffn_ev)
+        else:
+            M.moelb_grouped_ffn(self.x_perm, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
+                                stream=stream, events=ffn_ev)
+        if self.shared is not None:
+            M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
+                                stream=stream)
+        mark(6)
+        M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=stream)
+        mark(7)
+        return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
+                       self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
+                       self.x_perm, self.y, self.shared, self.out)
+
+
+def stage_times_ms(ev: HipEvents, base: int = 0) -> Dict[str, float]:
+    """Per-stage times of a step recorded with ``events`` at ``base``."""
+    t = {name: ev.elapsed_ms(base + i, base + i + 1) for i, name in enumerate(STAGES)}
+    t["ffn_schedule"] = ev.elapsed_ms(base + 8, base + 9)
+    t["ffn_gate_up_gemm"] = ev.elapsed_ms(base + 9, base + 10)
+    t["ffn_down_gemm"] = ev.elapsed_ms(base + 10, base + 11)
+    return t

@@ -1,0 +1,79 @@
+"""The C-ABI library loads, exports every entry point include/moelb.h
+declares, and rejects bad arguments on the host before launching anything
+(CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moelb.h")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moelb_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from routed_expert_ffn_gate_amd import moelb as M
+    if not os.path.exists(M.LIB_PATH):
+        pytest.fail("libmoelb.so is not built (run python -m routed_expert_ffn_gate_amd.build)")
+    return M.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_entry_points()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    from routed_expert_ffn_gate_amd import moelb as M
+    assert set(names) == set(M.SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moelb_version() == 100
+    assert lib.moelb_status_string(0) == b"ok"
+    assert lib.moelb_status_string(1) == b"invalid argument"
+    assert lib.moelb_status_string(3) == b"workspace missing or too small"
+
+
+def test_invalid_arguments_rejected_before_launch(lib):
+    P = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    N = None
+    # k > E
+    assert lib.moelb_gate_topk(P, 4, 8, 2, 3, 1, P, P, N, N, P, P, N, N, N) == 1
+    # d not a multiple of 8
+    assert lib.moelb_gate_topk(P, 4, 12, 8, 2, 1, P, P, N, N, P, P, N, N, N) == 1
+    # lookahead weight without its bias / output
+    assert lib.moelb_gate_topk(P, 4, 8, 8, 2, 1, P, P, P, N, P, P, N, N, N) == 1
+    # bad dtype
+    assert lib.moelb_gate_topk(P, 4, 8, 8, 2, 7, P, P, N, N, P, P, N, N, N) == 1
+    # T not a multiple of G; G above the limit
+    assert lib.moelb_histogram(P, 10, 2, 8, 4, P, N, N) == 1
+    assert lib.moelb_histogram(P, 128, 2, 8, 65, P, N, N) == 1
+    # L > N; N above the limit
+    assert lib.moelb_plan(P, P, 4, 8, 1, 2, P, N, N) == 1
+    assert lib.moelb_plan(P, P, 4, 8, 9, 2, P, N, N) == 1
+    # negative passes / eps
+    assert lib.moelb_split(P, P, P, 4, 8, 1, -1, 0, P, P, N) == 1
+    assert lib.moelb_split(P, P, P, 4, 8, 1, 12, -1, P, P, N) == 1
+    # permute: workspace too small
+    need = lib.moelb_permute_workspace_bytes(64, 2, 8, 4)
+    assert need > 0
+    assert lib.moelb_permute(N, P, 64, 8, 2, 8, 4, 1, 1, P, P, P, P, need - 1, P, P, P, N, N) == 3
+    # grouped ffn: rank filter needs num_groups % E == 0; workspace too small
+    assert lib.moelb_grouped_ffn(P, 8, 8, P, 7, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P, N, N) == 1
+    assert lib.moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 16, P, N, N) == 3
+    # combine: k out of range; misaligned output
+    assert lib.moelb_combine(P, 8, P, P, 4, 17, 8, 1, N, P, N) == 1
+    assert lib.moelb_combine(P, 8, P, P, 4, 2, 8, 1, N, ctypes.c_void_p(18), N) == 1
+
+
+def test_workspace_sizes_monotone(lib):
+    a = lib.moelb_grouped_ffn_workspace_bytes(1024, 64, 8, 256, 512, 1)
+    b = lib.moelb_grouped_ffn_workspace_bytes(2048, 64, 8, 256, 512, 1)
+    assert 0 < a < b
+    assert lib.moelb_grouped_ffn_workspace_bytes(2048, 64, 8, 256, 512, 0) > b   # fp32 activations

@@ -1,0 +1,203 @@
+"""GPU parity: every stage of the layer step, through the C ABI, against the
+CPU oracle on identical seeded inputs.
+
+Integer stages (histograms, plan, split, permutation) must be bit-exact when
+fed the GPU's top-k indices; top-k must match except on near-ties (k-th minus
+(k+1)-th logit < 1e-3); floats within 2e-2 (bf16) / 1e-4 (fp32) relative to an
+fp64 oracle (per row, max-norm).
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+from tests.gpu_layer import (check_float_stages, check_gate, check_integer_stages, log, run_layer,
+                             sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(cfg, tokens=None, **kw):
+    log(f"[layer] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} I={cfg.inter} G={cfg.G} N={cfg.N} "
+        f"{cfg.dtype} {kw}")
+    run = run_layer(cfg, **kw)
+    r1 = check_gate(run)
+    r2 = check_integer_stages(run)
+    r3 = check_float_stages(run, tokens)
+    log(f"  gate {r1}\n  int {r2}\n  float {r3}")
+    return run
+
+
+RAGGED = dict(T=200, d=200, E=24, k=3, inter=200, G=4, N=2, L=1)
+
+
+def test_tiny_fp32_config(moelb):
+    _full_check(W.config("c1_tiny_f32"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(moelb, dtype):
+    # tails everywhere: T not a multiple of the 128-token gate tile, d not a
+    # multiple of the 64-wide K step, inter not a multiple of the 128-column
+    # tile, E not a multiple of 32, odd k
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), dtype=dtype, steps=1, **RAGGED)
+    _full_check(cfg)
+
+
+def test_gather_equals_materialized(moelb):
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, **RAGGED)
+    a = run_layer(cfg, gather_rows=True, materialize_x=False)
+    b = run_layer(cfg, gather_rows=False, materialize_x=True)
+    assert b.x_perm_ok
+    for key in ["y", "out", "perm", "pos", "group_off"]:
+        assert np.array_equal(a.out[key], b.out[key]), key
+
+
+def test_decode_steps_qwen3_30b_shape(moelb):
+    cfg = W.config("c2_qwen3_30b_decode")
+    weights = W.expert_weights_stacked(cfg, 1)
+    for step in range(cfg.steps):
+        log(f"[decode step {step}]")
+        run = run_layer(cfg, step=step, weights=weights)
+        check_gate(run)
+        r = check_integer_stages(run)
+        f = check_float_stages(run, sample_tokens(cfg.T, 96, seed=step))
+        log(f"  {r} {f}")
+
+
+def test_prefill_qwen3_235b_shape(moelb):
+    cfg = W.config("c3_qwen3_235b_prefill")
+    _full_check(cfg, tokens=sample_tokens(cfg.T, 40))
+
+
+def test_prefill_glm45_shape_with_shared_expert(moelb):
+    cfg = W.config("c4_glm45_prefill")
+    _full_check(cfg, tokens=sample_tokens(cfg.T, 40))
+
+
+def test_drift_olmoe_shape_eight_layers(moelb):
+    cfg = W.config("c5_olmoe_drift")
+    hs = W.hidden_states(cfg, cfg.layers)
+    for layer in range(1, cfg.layers + 1):
+        log(f"[drift layer {layer}]")
+        run = run_layer(cfg, layer=layer, hs=hs)
+        check_gate(run)
+        r = check_integer_stages(run)
+        f = check_float_stages(run, sample_tokens(cfg.T, 12, seed=layer))
+        log(f"  {r} {f}")
+
+
+def test_zero_router_single_hot_set(moelb):
+    # W = 0: every token picks the same k experts (by bias), so a few groups
+    # hold every pair -- the most skewed case the method has.
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=256, d=256, inter=256)
+    import synth.workloads as SW
+    orig = SW.gate_params
+
+    def zero_gate(c, gate_layer, step=0):
+        w, b = orig(c, gate_layer, step)
+        return np.zeros_like(w), b
+
+    SW.gate_params = zero_gate
+    try:
+        run = run_layer(cfg)
+    finally:
+        SW.gate_params = orig
+    check_gate(run)
+    check_integer_stages(run)
+    check_float_stages(run, sample_tokens(cfg.T, 32))
+    assert len(np.unique(run.out["idx"])) == cfg.k
+
+
+def test_limits_E256_k16_G64_N8(moelb):
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=512, d=128, E=256, k=16, inter=64, G=64, N=8, L=4)
+    _full_check(cfg)
+
+
+def test_rank_share_covers_exactly_its_groups(moelb):
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import MoELayer, to_device
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, **RAGGED)
+    run = run_layer(cfg, gather_rows=False, materialize_x=True)
+    dev = torch.device("cuda")
+    off = run.out["group_off"]
+    G, E = cfg.G, cfg.E
+    x = torch.from_numpy(np.ascontiguousarray(run.li.h).view(np.int16)).to(dev).view(torch.bfloat16)
+    perm = torch.from_numpy(run.out["perm"]).to(dev)
+    goff = torch.from_numpy(off).to(dev)
+    w13 = to_device(run.w13, cfg.dtype, dev)
+    w2 = to_device(run.w2, cfg.dtype, dev)
+    P = cfg.T * cfg.k
+    ws = torch.empty(M.moelb_grouped_ffn_workspace_bytes(P, 2 * G * E, E, cfg.d, cfg.inter, M.MOELB_BF16),
+                     dtype=torch.uint8, device=dev)
+    covered = np.zeros(P, dtype=bool)
+    for r in range(G):
+        y = torch.zeros((P, cfg.d), dtype=torch.bfloat16, device=dev)
+        M.moelb_grouped_ffn(x, P, goff, E, w13, w2, ws, y, G=G, rank=r, gather=perm, gather_k=cfg.k)
+        torch.cuda.synchronize()
+        yh = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        mine = np.zeros(P, dtype=bool)
+        for seg in range(2):
+            for e in range(E):
+                g = (seg * G + r) * E + e
+                mine[off[g]:off[g + 1]] = True
+        assert np.array_equal(yh[mine], run.out["y"][mine])
+        assert not np.any(yh[~mine])
+        covered |= mine
+    assert covered.all()
+
+
+def test_plan_and_split_random_instances(moelb):
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(11)
+    for trial in range(120):
+        G = int(rng.choice([2, 3, 4, 8, 16]))
+        E = G * int(rng.choice([1, 2, 4, 8]))
+        N = int(rng.integers(0, 5))
+        L = int(rng.integers(0, N + 1))
+        pop = 1.0 / (1 + rng.permutation(E)) ** rng.uniform(0.5, 1.6)
+        c = np.stack([rng.multinomial(int(rng.integers(0, 400)), pop / pop.sum()) for _ in range(G)]).astype(np.int32)
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        ct = torch.from_numpy(c).to(dev)
+        ht = torch.from_numpy(home).to(dev)
+        rep = torch.full((G, max(N, 1)), -7, dtype=torch.int32, device=dev)
+        pl = torch.empty(G, dtype=torch.int32, device=dev)
+        if N > 0:
+            M.moelb_plan(ct, ht, L, rep, pl)
+            ref, loads = O.plan(c, home, G, E, N, L, return_loads=True)
+            assert np.array_equal(rep.cpu().numpy(), ref), (trial, G, E, N, L)
+            assert np.array_equal(pl.cpu().numpy(), loads)
+            rep_in = ref
+        else:
+            rep_in = None
+        passes = int(rng.choice([0, 1, 3, 12]))
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        rt = torch.from_numpy(rep_in if rep_in is not None else np.full((G, 1), -1, np.int32)).to(dev)
+        M.moelb_split(ct, ht, rt, hc, ld, passes=passes)
+        hc_o, ld_o = O.split(c, home, rep_in, G, E, passes=passes)
+        assert np.array_equal(hc.cpu().numpy(), hc_o), (trial, G, E, N, passes)
+        assert np.array_equal(ld.cpu().numpy(), ld_o)
+
+
+def test_empty_batch(moelb):
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    E, k, d, G = 8, 2, 64, 4
+    h = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((E, d), dtype=torch.bfloat16, device=dev)
+    b = torch.zeros(E, dtype=torch.float32, device=dev)
+    idx = torch.empty((0, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((0, k), dtype=torch.float32, device=dev)
+    M.moelb_gate_topk(h, w, b, None, None, idx, wts)
+    counts = torch.full((G, E), 5, dtype=torch.int32, device=dev)
+    M.moelb_histogram(idx, G, counts)
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0
+    out = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    pos = torch.empty((0,), dtype=torch.int32, device=dev)
+    M.moelb_combine(y, pos, wts, out)
+    torch.cuda.synchronize()
