@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
+                    help="gate/up GEMM reads h rows through the permutation, or a copied x_perm")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("this build measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
@@ -115,7 +117,7 @@ def main():
     if shared is not None:
         S13, S2 = up(shared[0]), up(shared[1])
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
-                     shared_inter=cfg.shared_inter, gather_rows=True, materialize_x=True)
+                     shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True)
     replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
     layer.predict_plan(h_prev, wc, bc, home, replica_cur)
     torch.cuda.synchronize()
@@ -191,7 +193,8 @@ def main():
         "data": "synthetic (seeded; shapes of the workload, random-init router and experts)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "inter": cfg.inter, "shared_inter": cfg.shared_inter, "virtual_ranks": cfg.G,
-                   "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12},
+                   "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
+                   "ffn_rows": args.rows},
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
         "roofline": {"bound": "mfma", "kernel": "ffn_mfma_kernel<0> (gate/up GEMM + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -157,6 +157,20 @@ __device__ __forceinline__ int xcd_tile(int total) {
   return ((bid >> 3) < per && t < total) ? t : -1;
 }
 
+// Grouped tile order: GROUP_M consecutive M tiles x every N tile, M fastest.
+// The ~32 tiles an XCD runs at once then share a few A row blocks and weight
+// slices, which its L2 serves, instead of streaming a whole expert's weights
+// per M tile.
+constexpr int GROUP_M = 8;
+__device__ __forceinline__ void grouped_tile(int t, int n_mtiles, int ntn, int& mt, int& nt) {
+  const int group = t / (GROUP_M * ntn);
+  const int first = group * GROUP_M;
+  const int gm = min(GROUP_M, n_mtiles - first);
+  const int local = t - group * GROUP_M * ntn;
+  nt = local / gm;
+  mt = first + local % gm;
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
 // MODE 0: gate/up GEMM with SwiGLU epilogue -> amid (virtual rows, K = d).
@@ -173,9 +187,11 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
                                                                const uint16_t* __restrict__ w, FfnSched s, int d,
                                                                int inter, int ntn, uint16_t* __restrict__ y) {
   extern __shared__ __align__(16) char smem[];
-  const int tile = xcd_tile(*s.n_mtiles * ntn);
+  const int n_mtiles = *s.n_mtiles;
+  const int tile = xcd_tile(n_mtiles * ntn);
   if (tile < 0) return;
-  const int mt = tile / ntn, nt = tile % ntn;
+  int mt, nt;
+  grouped_tile(tile, n_mtiles, ntn, mt, nt);
   const int e = s.mt_e[mt];
   const int v0 = s.mt_v0[mt];
   const int vend = s.eoff[e + 1];
@@ -344,6 +360,214 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
   }
 }
 
+// ---------------------------------------------------------------- bf16 MFMA GEMM, direct-to-LDS
+
+// Same tile, waves and epilogue as ffn_mfma_kernel, for K % 64 == 0.  Tiles
+// of A and B stream global -> LDS with global_load_lds_dwordx4 (no staging
+// registers, no ds_write), 64-wide K steps (a whole 128-byte line per row and
+// request), two LDS stages.  Each wave-instruction fills 1 KiB of LDS (8 rows
+// x 128 B), swizzled as below.  The 4 sixteen-wide k sub-steps of a stage are
+// software-pipelined over two fragment register sets: sub-step j+1 is read
+// while sub-step j's MFMAs run.  The barrier that publishes the next stage sits
+// behind the third sub-step's queued MFMAs; after it the stage just consumed
+// (all its fragments are in registers) is refilled with step kt+2, and the
+// next stage's first sub-step is read while the last MFMAs of step kt run.
+// Waits are explicit (s_waitcnt vmcnt + a bare s_barrier: a fence would drain
+// every outstanding load).
+constexpr int DL_BK = 64;
+constexpr int DL_STAGES = 2;
+constexpr int DL_STAGE_ELEMS = 2 * MF_BM * DL_BK;  // A then B
+constexpr size_t DL_LDS_MAIN = (size_t)DL_STAGES * DL_STAGE_ELEMS * sizeof(uint16_t);
+constexpr size_t DL_LDS_EPI = (size_t)MF_BM * (256 + 8) * sizeof(uint16_t);
+constexpr size_t DL_LDS_BYTES = DL_LDS_MAIN > DL_LDS_EPI ? DL_LDS_MAIN : DL_LDS_EPI;
+
+// 16-byte chunk c (0..7) of LDS row r sits in slot c ^ (((r >> 1) ^ (r << 2)) & 7):
+// conflict-free fragment reads whether the LDS serves 8 or 16 lanes per pass.
+__device__ __forceinline__ int dl_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row << 2)) & 7); }
+
+template <int MODE>
+__global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t* __restrict__ x, int rows_x,
+                                                                   const int32_t* __restrict__ gather, int gather_k,
+                                                                   const uint16_t* __restrict__ w, FfnSched s,
+                                                                   int d, int inter, int ntn,
+                                                                   uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) char smem[];
+  const int n_mtiles = *s.n_mtiles;
+  const int tile = xcd_tile(n_mtiles * ntn);
+  if (tile < 0) return;
+  int mt, nt;
+  grouped_tile(tile, n_mtiles, ntn, mt, nt);
+  const int e = s.mt_e[mt];
+  const int v0 = s.mt_v0[mt];
+  const int vend = s.eoff[e + 1];
+  const int K = MODE == 0 ? d : inter;
+  const uint16_t* amid = static_cast<const uint16_t*>(s.amid);
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // DMA rows of this lane: block (wave*8 + j) of 8 rows, row (lane >> 3) in it,
+  // slot (lane & 7) <- global chunk dl_slot(row, slot)
+  const uint16_t* abase = MODE == 0 ? x : amid;
+  const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wave * 8 + j) * 8 + (lane >> 3);
+    const int chunk = dl_slot(r, lane & 7);
+    int v = v0 + r;
+    v = v < vend ? v : v0;
+    if (MODE == 0) {
+      const int q = s.rowmap[v];
+      int src = gather ? gather[q] / gather_k : q;
+      src = (src >= 0 && src < rows_x) ? src : 0;
+      aoff[j] = (uint32_t)src * (uint32_t)d + chunk * 8;
+      int c = nt * 128 + (r & 127);
+      c = c < inter ? c : 0;
+      boff[j] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8;
+    } else {
+      aoff[j] = (uint32_t)v * (uint32_t)inter + chunk * 8;
+      int c = nt * 256 + r;
+      c = c < d ? c : 0;
+      boff[j] = (uint32_t)c * (uint32_t)inter + chunk * 8;
+    }
+  }
+
+  int nb[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+    nb[ni] = MODE == 0 ? (wn * 64 + (ni & 1) * 32 + (ni >> 1) * 128) : (wn * 128 + ni * 32);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int KT = K / DL_BK;
+#define DL_ISSUE(KTI)                                                                                  \
+  {                                                                                                    \
+    uint16_t* st_ = lds + ((KTI) & (DL_STAGES - 1)) * DL_STAGE_ELEMS;                                  \
+    const uint32_t k0_ = (uint32_t)(KTI) * DL_BK;                                                      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                    \
+      const int blk = wave * 8 + j;                                                                    \
+      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + k0_), st_ + blk * 8 * DL_BK, 16, 0, 0);      \
+      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + k0_), st_ + MF_BM * DL_BK + blk * 8 * DL_BK,  \
+                                       16, 0, 0);                                                      \
+    }                                                                                                  \
+  }
+  // LDS element offsets of this lane's fragments, per 16-wide k sub-step
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  int aro[4][4], bro[4][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 128 + i * 32 + fr;
+      const int rb = nb[i] + fr;
+      aro[ks][i] = ra * DL_BK + dl_slot(ra, ks * 2 + fh) * 8;
+      bro[ks][i] = MF_BM * DL_BK + rb * DL_BK + dl_slot(rb, ks * 2 + fh) * 8;
+    }
+  bf16x8_t xa[4], xb[4], ya[4], yb[4];
+#define DL_READ(FA, FB, ST, KS)                                    \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                  \
+    FA[i] = *reinterpret_cast<const bf16x8_t*>((ST) + aro[KS][i]); \
+    FB[i] = *reinterpret_cast<const bf16x8_t*>((ST) + bro[KS][i]); \
+  }
+#define DL_MMA(FA, FB)                                         \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)             \
+  _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)             \
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
+#define DL_INTERLEAVE()                                        \
+  _Pragma("unroll") for (int g = 0; g < 8; ++g) {              \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         \
+  }                                                            \
+  __builtin_amdgcn_sched_barrier(0);
+
+  DL_ISSUE(0)
+  if (KT > 1) DL_ISSUE(1)
+  // 16 DMA instructions per K step and wave: wait for step 0 only
+  if (KT > 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  DL_READ(xa, xb, lds, 0)
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint16_t* st = lds + (kt & (DL_STAGES - 1)) * DL_STAGE_ELEMS;
+    DL_READ(ya, yb, st, 1)
+    DL_MMA(xa, xb)
+    DL_INTERLEAVE()
+    DL_READ(xa, xb, st, 2)
+    DL_MMA(ya, yb)
+    DL_INTERLEAVE()
+    DL_READ(ya, yb, st, 3)
+    DL_MMA(xa, xb)
+    DL_INTERLEAVE()
+    if (kt + 1 < KT) {
+      // only step kt+1 is outstanding here
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // step kt's stage is fully in registers on every wave: refill it
+      if (kt + 2 < KT) DL_ISSUE(kt + 2)
+      DL_READ(xa, xb, lds + ((kt + 1) & (DL_STAGES - 1)) * DL_STAGE_ELEMS, 0)
+    }
+    DL_MMA(ya, yb)
+    DL_INTERLEAVE()
+  }
+#undef DL_ISSUE
+#undef DL_READ
+#undef DL_MMA
+#undef DL_INTERLEAVE
+
+  constexpr int BN_OUT = MODE == 0 ? 128 : 256;
+  constexpr int CS = BN_OUT + 8;
+  uint16_t* Cs = lds;
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      if (MODE == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float g = acc[mi][f][r], u = acc[mi][f + 2][r];
+          Cs[row * CS + wn * 64 + f * 32 + fr] = f32_to_bf16(silu_f32(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) Cs[row * CS + wn * 128 + ni * 32 + fr] = f32_to_bf16(acc[mi][ni][r]);
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = BN_OUT / 8;
+  const int n0 = nt * BN_OUT;
+  const int nout = MODE == 0 ? inter : d;
+  for (int c = tid; c < MF_BM * CPR; c += MF_THREADS) {
+    const int row = c / CPR, ch = c % CPR;
+    const int v = v0 + row;
+    const int col = n0 + ch * 8;
+    if (v >= vend || col >= nout) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(Cs + row * CS + ch * 8);
+    if (MODE == 0) {
+      *reinterpret_cast<uint4*>(y + (size_t)v * inter + col) = val;
+    } else {
+      const int prow = min(max(s.rowmap[v], 0), rows_x - 1);
+      *reinterpret_cast<uint4*>(y + (size_t)prow * d + col) = val;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
 template <int MODE>
@@ -486,15 +710,30 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
       return MOELB_ELAUNCH;
     const int ntn0 = (inter + 127) / 128;
     const int ntn1 = (d + 255) / 256;
+    // direct-to-LDS pipeline when K is a multiple of its 32-wide step
+    const bool dma0 = d % DL_BK == 0, dma1 = inter % DL_BK == 0;  // else the register-staged kernel
+    if ((dma0 && !moelb_allow_lds(ffn_mfma_dma_kernel<0>, DL_LDS_BYTES)) ||
+        (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)))
+      return MOELB_ELAUNCH;
     rec(1);
-    hipLaunchKernelGGL(ffn_mfma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
-                       static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13), sc,
-                       d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
+    if (dma0)
+      hipLaunchKernelGGL(ffn_mfma_dma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13),
+                         sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
+    else
+      hipLaunchKernelGGL(ffn_mfma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13),
+                         sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
     MOELB_CHECK_LAUNCH();
     rec(2);
-    hipLaunchKernelGGL(ffn_mfma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
-                       static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
-                       d, inter, ntn1, static_cast<uint16_t*>(y));
+    if (dma1)
+      hipLaunchKernelGGL(ffn_mfma_dma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
+                         d, inter, ntn1, static_cast<uint16_t*>(y));
+    else
+      hipLaunchKernelGGL(ffn_mfma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
+                         d, inter, ntn1, static_cast<uint16_t*>(y));
     MOELB_CHECK_LAUNCH();
   } else {
     const int ntn0 = (inter + 31) / 32;
