@@ -41,6 +41,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def _check_kernel_stubs(lib_path: str) -> None:
+    """A kernel whose host launch stub was not emitted only shows up as an
+    undefined symbol when the library is loaded: fail the build instead."""
+    p = subprocess.run(["nm", "-u", lib_path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    missing = [l.split()[-1] for l in p.stdout.splitlines() if "_kernel" in l or "__device_stub__" in l]
+    if missing:
+        raise RuntimeError(f"{lib_path}: kernels without a host stub: {missing[:4]}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -56,6 +65,7 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

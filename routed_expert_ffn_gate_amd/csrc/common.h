@@ -18,12 +18,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest, ties to even.  NaN stays NaN.
+// Round to nearest, ties to even.  NaN stays NaN.  Branch-free (one compare
+// and a select), so unrolled epilogues stay straight-line code.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 
 // Element access for the two storage types.

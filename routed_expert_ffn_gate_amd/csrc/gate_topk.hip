@@ -242,6 +242,161 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 MFMA kernel, direct-to-LDS
+
+// The same workgroup tile, waves and epilogue as gate_topk_bf16_kernel, for
+// N = 64 * NF columns and d % 64 == 0.  The h tile (128 x 64) and the router
+// rows (N x 64) of each 64-wide K step stream global -> LDS with
+// global_load_lds_dwordx4 into S swizzled stages (16-byte chunk c of row r in
+// slot c ^ (((r >> 1) ^ (r << 2)) & 7): conflict-free 16-row fragment reads),
+// so S-1 K steps are in flight while one computes; fragment reads are
+// software-pipelined against the MFMAs over two register sets; waits are
+// explicit vmcnt + a bare s_barrier.
+__device__ __forceinline__ int gt_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row << 2)) & 7); }
+
+template <int NF, int KL, int S>
+__global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
+    const uint16_t* __restrict__ h, int T, int d, int E, int k, const uint16_t* __restrict__ w_cur,
+    const float* __restrict__ b_cur, const uint16_t* __restrict__ w_next, const float* __restrict__ b_next,
+    int32_t* __restrict__ idx, float* __restrict__ wts, float* __restrict__ gap, int32_t* __restrict__ idx_next,
+    int zstride) {
+  constexpr int BK = 64;
+  constexpr int N = 64 * NF;
+  constexpr int STAGE = (GATE_BM + N) * BK;  // elements: A rows, then B rows
+  constexpr int VPS = 2 + NF;                // DMA instructions per wave and K step
+  extern __shared__ __align__(16) char smem[];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  float* Z = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tok0 = blockIdx.x * GATE_BM;
+  const bool has_next = w_next != nullptr;
+  const int KT = d / BK;
+
+  // DMA rows of this lane: 8-row blocks, row (lane >> 3), slot (lane & 7)
+  uint32_t aoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 8 + (lane >> 3);
+    const int t = min(tok0 + r, T - 1);  // rows past T are computed and dropped
+    aoff[j] = (uint32_t)t * (uint32_t)d + gt_slot(r, lane & 7) * 8;
+  }
+  const uint16_t* bptr[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int r = (wave * NF + j) * 8 + (lane >> 3);
+    const uint16_t* base = r < E ? w_cur + (size_t)r * d : w_next + (size_t)(r - E) * d;
+    bptr[j] = base + gt_slot(r, lane & 7) * 8;
+  }
+#define GT_ISSUE(KTI)                                                                              \
+  {                                                                                                \
+    uint16_t* st_ = lds + ((KTI) % S) * STAGE;                                                     \
+    const uint32_t k0_ = (uint32_t)(KTI) * BK;                                                     \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+      __builtin_amdgcn_global_load_lds((const void*)(h + (aoff[j] + k0_)),                          \
+                                       (void*)(st_ + (wave * 2 + j) * 8 * BK), 16, 0, 0);           \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j)                                                 \
+      __builtin_amdgcn_global_load_lds((const void*)(bptr[j] + k0_),                                \
+                                       (void*)(st_ + (GATE_BM + (wave * NF + j) * 8) * BK), 16, 0, 0); \
+  }
+
+  // fragment rows are (multiple of 16) + (lane % 16): one lane term per 32-wide k sub-step
+  const int fr = lane & 15;
+  const int swz = ((fr >> 1) ^ (fr << 2)) & 7;
+  int kofs[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) kofs[ks] = fr * BK + (((ks * 4 + (lane >> 4)) ^ swz) * 8);
+  const int arow0 = wm * 64 * BK;
+  const int brow0 = (GATE_BM + wn * NF * 16) * BK;
+
+  f32x4_t acc[4][NF];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t xa[4], xb[NF], ya[4], yb[NF];
+#define GT_READ(FA, FB, ST, KS)                                                                    \
+  {                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
+      FA[i] = *reinterpret_cast<const bf16x8_t*>((ST) + arow0 + i * 16 * BK + kofs[KS]);           \
+    _Pragma("unroll") for (int i = 0; i < NF; ++i)                                                 \
+      FB[i] = *reinterpret_cast<const bf16x8_t*>((ST) + brow0 + i * 16 * BK + kofs[KS]);           \
+  }
+#define GT_MMA(FA, FB)                                                                             \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                                 \
+  _Pragma("unroll") for (int ni = 0; ni < NF; ++ni)                                                \
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
+#define GT_FENCE() __builtin_amdgcn_sched_barrier(0);
+
+  for (int t = 0; t < S; ++t)
+    if (t < KT) GT_ISSUE(t)
+  {
+    const int after = min(S, KT) - 1;  // steps issued after step 0
+    if (after >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * VPS) : "memory");
+    else if (after == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  GT_READ(xa, xb, lds, 0)
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint16_t* st = lds + (kt % S) * STAGE;
+    GT_READ(ya, yb, st, 1)
+    GT_MMA(xa, xb)
+    GT_FENCE()
+    if (kt + 1 < KT) {
+      // steps issued after kt+1 may stay in flight
+      const int after = min(kt + S - 1, KT - 1) - (kt + 1);
+      // lgkmcnt(0): this wave's reads of step kt's stage have landed before
+      // any wave refills it
+      if (after >= 1)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VPS) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // step kt's stage is in registers on every wave: refill it with step kt+S
+      if (kt + S < KT) GT_ISSUE(kt + S)
+      GT_READ(xa, xb, lds + ((kt + 1) % S) * STAGE, 0)
+    }
+    GT_MMA(ya, yb)
+    GT_FENCE()
+  }
+#undef GT_ISSUE
+#undef GT_READ
+#undef GT_MMA
+#undef GT_FENCE
+  __syncthreads();  // LDS is reused for the logits
+
+  const int colbase = wn * NF * 16;
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int ni = 0; ni < NF; ++ni) {
+        const int col = colbase + ni * 16 + (lane & 15);
+        const float bias = col < E ? b_cur[col] : b_next[col - E];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mi * 16 + (lane >> 4) * 4 + i;
+            Z[r * zstride + col] = acc[mi][ni][i] + bias;
+          }
+      }
+    }
+    __syncthreads();
+    const int t0 = tok0 + half * 64;
+    const int ntok = min(64, T - t0);
+    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, t0, T, E, k, has_next, idx, wts, gap, idx_next);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- fp32 kernel
 
 template <int KL>
@@ -314,6 +469,39 @@ int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w
   return MOELB_OK;
 }
 
+template <int NF, int KL, int S>
+int launch_dma_nf(const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur, const void* w_next,
+                  const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next, hipStream_t s) {
+  const int N = 64 * NF;
+  const int zs = zstride_for(N);
+  const size_t lds_main = (size_t)S * (GATE_BM + N) * 64 * 2;
+  const size_t lds_z = 64ull * zs * 4;
+  const size_t lds = lds_main > lds_z ? lds_main : lds_z;
+  if (!moelb_allow_lds(gate_topk_dma_kernel<NF, KL, S>, lds)) return MOELB_ELAUNCH;
+  hipLaunchKernelGGL((gate_topk_dma_kernel<NF, KL, S>), dim3((T + GATE_BM - 1) / GATE_BM), dim3(GATE_THREADS), lds, s,
+                     static_cast<const uint16_t*>(h), T, d, E, k, static_cast<const uint16_t*>(w_cur), b_cur,
+                     static_cast<const uint16_t*>(w_next), b_next, idx, wts, gap, idx_next, zs);
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+// Direct-to-LDS variant: N = 64 * NF columns (NF <= 7), d % 64 == 0.
+template <int KL>
+int launch_dma(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
+               const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next,
+               hipStream_t s) {
+  switch (NF) {
+    case 1: return launch_dma_nf<1, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 2: return launch_dma_nf<2, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 3: return launch_dma_nf<3, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 4: return launch_dma_nf<4, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 5: return launch_dma_nf<5, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 6: return launch_dma_nf<6, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 7: return launch_dma_nf<7, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    default: return MOELB_EINVAL;
+  }
+}
+
 template <int KL>
 int launch_f32(const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
                const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap,
@@ -347,6 +535,12 @@ extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dt
   if (dtype == MOELB_BF16) {
     const int N = w_next ? 2 * E : E;
     const int NF = (N + 63) / 64;
+    if (N % 64 == 0 && NF <= (k <= 8 ? 7 : 6) && d % 64 == 0 && (size_t)T * d < (1ull << 32)) {
+      if (k <= 2) return launch_dma<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+      if (k <= 4) return launch_dma<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+      if (k <= 8) return launch_dma<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+      return launch_dma<17>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    }
     if (k <= 2) return launch_bf16<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
     if (k <= 4) return launch_bf16<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
     if (k <= 8) return launch_bf16<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);

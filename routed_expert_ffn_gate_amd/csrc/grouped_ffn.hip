@@ -54,6 +54,7 @@ struct FfnSched {
   int32_t* mt_v0;     // [max_mtiles] first virtual row of each M tile
   int32_t* n_mtiles;  // [1]
   int32_t* rowmap;    // [rows] physical row of each virtual row
+  int32_t* asrc;      // [rows] row of x the gate/up GEMM reads for each virtual row
   void* amid;         // [rows][inter] SwiGLU activations, virtual row order
 };
 
@@ -73,6 +74,7 @@ inline size_t sched_layout(int rows, int num_groups, int E, int inter, int dtype
   char* p_mtv = take(mt * 4);
   char* p_n = take(4);
   char* p_rm = take((size_t)rows * 4);
+  char* p_as = take((size_t)rows * 4);
   char* p_am = take((size_t)rows * inter * moelb_elem_bytes(dtype));
   if (s) {
     s->eoff = reinterpret_cast<int32_t*>(p_eoff);
@@ -81,6 +83,7 @@ inline size_t sched_layout(int rows, int num_groups, int E, int inter, int dtype
     s->mt_v0 = reinterpret_cast<int32_t*>(p_mtv);
     s->n_mtiles = reinterpret_cast<int32_t*>(p_n);
     s->rowmap = reinterpret_cast<int32_t*>(p_rm);
+    s->asrc = reinterpret_cast<int32_t*>(p_as);
     s->amid = p_am;
   }
   return off;
@@ -133,7 +136,10 @@ __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Virtual -> physical row map, and the row of x each virtual row reads (through
+// the gather, when the rows come straight from the unpermuted hidden states).
 __global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__ group_off, int E, int rows,
+                                                     const int32_t* __restrict__ gather, int gather_k, int rows_x,
                                                      FfnSched s) {
   const int g = blockIdx.x;
   const int vb = s.gvb[g];
@@ -144,7 +150,11 @@ __global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__
   const int hi = min(max(group_off[g + 1], lo), rows);
   for (int q = lo + threadIdx.x; q < hi; q += blockDim.x) {
     const int v = vb + (q - lo);
-    if (v < vend) s.rowmap[v] = q;
+    if (v < vend) {
+      s.rowmap[v] = q;
+      const int src = gather ? gather[q] / gather_k : q;
+      s.asrc[v] = (src >= 0 && src < rows_x) ? src : 0;
+    }
   }
 }
 
@@ -217,10 +227,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
     int v = v0 + r;
     v = v < vend ? v : v0;  // tiles always start with a valid row
     if (MODE == 0) {
-      const int q = s.rowmap[v];
-      int src = gather ? gather[q] / gather_k : q;
-      src = (src >= 0 && src < rows_x) ? src : 0;
-      aoff[i] = (uint32_t)src * (uint32_t)d;
+      aoff[i] = (uint32_t)s.asrc[v] * (uint32_t)d;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
       boff[i] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d;
@@ -420,10 +427,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     int v = v0 + r;
     v = v < vend ? v : v0;
     if (MODE == 0) {
-      const int q = s.rowmap[v];
-      int src = gather ? gather[q] / gather_k : q;
-      src = (src >= 0 && src < rows_x) ? src : 0;
-      aoff[j] = (uint32_t)src * (uint32_t)d + chunk * 8;
+      aoff[j] = (uint32_t)s.asrc[v] * (uint32_t)d + chunk * 8;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
       boff[j] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8;
@@ -512,8 +516,9 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     DL_MMA(xa, xb)
     DL_INTERLEAVE()
     if (kt + 1 < KT) {
-      // only step kt+1 is outstanding here
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // only step kt+1 is outstanding here; lgkmcnt(0): this wave's reads of
+      // step kt's stage have landed before any wave refills it
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       // step kt's stage is fully in registers on every wave: refill it
@@ -702,7 +707,8 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows, BM,
                      sc);
   MOELB_CHECK_LAUNCH();
-  hipLaunchKernelGGL(rowmap_kernel, dim3(num_groups), dim3(256), 0, s, group_off, E, rows, sc);
+  hipLaunchKernelGGL(rowmap_kernel, dim3(num_groups), dim3(256), 0, s, group_off, E, rows, gather, gather_k, rows_x,
+                     sc);
   MOELB_CHECK_LAUNCH();
   const size_t mtiles = (size_t)(rows + BM - 1) / BM + E;
   if (bf) {
@@ -710,7 +716,7 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
       return MOELB_ELAUNCH;
     const int ntn0 = (inter + 127) / 128;
     const int ntn1 = (d + 255) / 256;
-    // direct-to-LDS pipeline when K is a multiple of its 32-wide step
+    // direct-to-LDS pipeline when K is a multiple of its 64-wide step
     const bool dma0 = d % DL_BK == 0, dma1 = inter % DL_BK == 0;  // else the register-staged kernel
     if ((dma0 && !moelb_allow_lds(ffn_mfma_dma_kernel<0>, DL_LDS_BYTES)) ||
         (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)))
