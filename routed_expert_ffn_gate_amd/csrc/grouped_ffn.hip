@@ -369,28 +369,43 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM, direct-to-LDS
 
-// Same tile, waves and epilogue as ffn_mfma_kernel, for K % 64 == 0.  Tiles
-// of A and B stream global -> LDS with global_load_lds_dwordx4 (no staging
-// registers, no ds_write), 64-wide K steps (a whole 128-byte line per row and
-// request), two LDS stages.  Each wave-instruction fills 1 KiB of LDS (8 rows
-// x 128 B), swizzled as below.  The 4 sixteen-wide k sub-steps of a stage are
-// software-pipelined over two fragment register sets: sub-step j+1 is read
-// while sub-step j's MFMAs run.  The barrier that publishes the next stage sits
-// behind the third sub-step's queued MFMAs; after it the stage just consumed
-// (all its fragments are in registers) is refilled with step kt+2, and the
-// next stage's first sub-step is read while the last MFMAs of step kt run.
-// Waits are explicit (s_waitcnt vmcnt + a bare s_barrier: a fence would drain
-// every outstanding load).
+// Same tile, waves and epilogue as ffn_mfma_kernel, for K % 64 == 0.
+//  * Tiles of A and B stream global -> LDS with global_load_lds_dwordx4 (no
+//    staging registers, no ds_write), in 64-wide K steps: each row request is
+//    a whole 128-byte line, and each wave-instruction fills 1 KiB of LDS
+//    (8 rows x 128 B), swizzled as below.
+//  * LDS is a ring of five 32 KiB half-stages (A or B of one K step, 256 rows
+//    x 64): A of step t in slot (2t) % 5, B of step t in slot (2t+1) % 5.  While
+//    step t computes, steps t+1 and half of t+2 are in flight (160 KiB total).
+//  * A wave blocks while the texture unit accepts a burst of loads, so the
+//    refills are spread one instruction per four MFMAs over the step: B of
+//    step t+2 during the last sub-step of t (after the barrier that frees its
+//    slot) and the first of t+1, A of step t+3 during the second and third
+//    sub-steps of t+1.
+//  * The four 16-wide k sub-steps of a step are software-pipelined over two
+//    fragment register sets (sub-step j+1 is read while j's MFMAs run).  One
+//    barrier per step, behind the third sub-step: every wave has read step
+//    t's stage and has its part of step t+1 landed.
+//  * The loads are issued from inline asm, so the compiler neither knows nor
+//    waits for them: the vmcnt waits are explicit, and the compiler's own LDS
+//    waits stay exact (a known LDS DMA makes it wait for every LDS read).
 constexpr int DL_BK = 64;
-constexpr int DL_STAGES = 2;
-constexpr int DL_STAGE_ELEMS = 2 * MF_BM * DL_BK;  // A then B
-constexpr size_t DL_LDS_MAIN = (size_t)DL_STAGES * DL_STAGE_ELEMS * sizeof(uint16_t);
+constexpr int DL_HALF = MF_BM * DL_BK;  // elements of one half-stage
+constexpr int DL_SLOTS = 5;
+constexpr size_t DL_LDS_MAIN = (size_t)DL_SLOTS * DL_HALF * sizeof(uint16_t);
 constexpr size_t DL_LDS_EPI = (size_t)MF_BM * (256 + 8) * sizeof(uint16_t);
 constexpr size_t DL_LDS_BYTES = DL_LDS_MAIN > DL_LDS_EPI ? DL_LDS_MAIN : DL_LDS_EPI;
 
 // 16-byte chunk c (0..7) of LDS row r sits in slot c ^ (((r >> 1) ^ (r << 2)) & 7):
 // conflict-free fragment reads whether the LDS serves 8 or 16 lanes per pass.
 __device__ __forceinline__ int dl_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row << 2)) & 7); }
+
+// 16 bytes per lane, global -> LDS: byte offset voff from the wave-uniform
+// base sbase; lane i lands at LDS byte address m0 + 16 i.
+__device__ __forceinline__ void dl_copy16(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 
 template <int MODE>
 __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t* __restrict__ x, int rows_x,
@@ -408,16 +423,17 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
   const int v0 = s.mt_v0[mt];
   const int vend = s.eoff[e + 1];
   const int K = MODE == 0 ? d : inter;
-  const uint16_t* amid = static_cast<const uint16_t*>(s.amid);
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
 
   // DMA rows of this lane: block (wave*8 + j) of 8 rows, row (lane >> 3) in it,
-  // slot (lane & 7) <- global chunk dl_slot(row, slot)
-  const uint16_t* abase = MODE == 0 ? x : amid;
+  // slot (lane & 7) <- global chunk dl_slot(row, slot); byte offsets
+  const uint16_t* abase = MODE == 0 ? x : static_cast<const uint16_t*>(s.amid);
   const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
   uint32_t aoff[8], boff[8];
 #pragma unroll
@@ -427,15 +443,15 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     int v = v0 + r;
     v = v < vend ? v : v0;
     if (MODE == 0) {
-      aoff[j] = (uint32_t)s.asrc[v] * (uint32_t)d + chunk * 8;
+      aoff[j] = ((uint32_t)s.asrc[v] * (uint32_t)d + chunk * 8) * 2u;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
-      boff[j] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8;
+      boff[j] = ((uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8) * 2u;
     } else {
-      aoff[j] = (uint32_t)v * (uint32_t)inter + chunk * 8;
+      aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;
       int c = nt * 256 + r;
       c = c < d ? c : 0;
-      boff[j] = (uint32_t)c * (uint32_t)inter + chunk * 8;
+      boff[j] = ((uint32_t)c * (uint32_t)inter + chunk * 8) * 2u;
     }
   }
 
@@ -453,18 +469,16 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
   const int KT = K / DL_BK;
-#define DL_ISSUE(KTI)                                                                                  \
+  const int nh = 2 * KT;  // half-stages: 2t = A of step t, 2t+1 = B of step t
+#define DL_COPY(J, JJ)                                                                                 \
   {                                                                                                    \
-    uint16_t* st_ = lds + ((KTI) & (DL_STAGES - 1)) * DL_STAGE_ELEMS;                                  \
-    const uint32_t k0_ = (uint32_t)(KTI) * DL_BK;                                                      \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                    \
-      const int blk = wave * 8 + j;                                                                    \
-      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + k0_), st_ + blk * 8 * DL_BK, 16, 0, 0);      \
-      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + k0_), st_ + MF_BM * DL_BK + blk * 8 * DL_BK,  \
-                                       16, 0, 0);                                                      \
-    }                                                                                                  \
+    const int j_ = (J);                                                                                \
+    const uint16_t* base_ = ((j_ & 1) ? bbase : abase) + (size_t)(j_ >> 1) * DL_BK;                    \
+    dl_copy16((j_ & 1) ? boff[JJ] : aoff[JJ], base_,                                                   \
+              lds_u32 + (uint32_t)(((j_ % DL_SLOTS) * DL_HALF + (wave_s * 8 + (JJ)) * 8 * DL_BK) * 2)); \
   }
-  // LDS element offsets of this lane's fragments, per 16-wide k sub-step
+  // LDS element offsets (inside a half-stage) of this lane's fragments, per
+  // 16-wide k sub-step
   const int fr = lane & 31;
   const int fh = lane >> 5;
   int aro[4][4], bro[4][4];
@@ -475,63 +489,75 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
       const int ra = wm * 128 + i * 32 + fr;
       const int rb = nb[i] + fr;
       aro[ks][i] = ra * DL_BK + dl_slot(ra, ks * 2 + fh) * 8;
-      bro[ks][i] = MF_BM * DL_BK + rb * DL_BK + dl_slot(rb, ks * 2 + fh) * 8;
+      bro[ks][i] = rb * DL_BK + dl_slot(rb, ks * 2 + fh) * 8;
     }
   bf16x8_t xa[4], xb[4], ya[4], yb[4];
-#define DL_READ(FA, FB, ST, KS)                                    \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                  \
-    FA[i] = *reinterpret_cast<const bf16x8_t*>((ST) + aro[KS][i]); \
-    FB[i] = *reinterpret_cast<const bf16x8_t*>((ST) + bro[KS][i]); \
+  // One k sub-step: per 32-row block mi, read the next set's fragments (from
+  // sub-step KS of half-stages SA/SB, if RD), run its 4 MFMAs on the current
+  // set, then issue DMA instruction J0+mi of half-stage J (if DO).
+#define DL_SUB(FA, FB, NA, NB, SA, SB, KS, RD, DO, J, J0)                                              \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                   \
+    if (RD) {                                                                                          \
+      NA[mi] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS][mi]);                                 \
+      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS][mi]);                                 \
+    }                                                                                                  \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);     \
+    if (DO) DL_COPY(J, (J0) + mi)                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
   }
-#define DL_MMA(FA, FB)                                         \
-  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)             \
-  _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)             \
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
-#define DL_INTERLEAVE()                                        \
-  _Pragma("unroll") for (int g = 0; g < 8; ++g) {              \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         \
-  }                                                            \
-  __builtin_amdgcn_sched_barrier(0);
 
-  DL_ISSUE(0)
-  if (KT > 1) DL_ISSUE(1)
-  // 16 DMA instructions per K step and wave: wait for step 0 only
-  if (KT > 1)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  DL_READ(xa, xb, lds, 0)
+  // the epilogue's scalar arguments are loaded before the loop: a scalar load
+  // still in flight would make every LDS wait in the loop a full drain
+  asm volatile("" ::"s"(y), "s"(s.rowmap), "s"(rows_x));
+  for (int j = 0; j < DL_SLOTS && j < nh; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) DL_COPY(j, jj)
+  {
+    // 8 instructions per half-stage and wave: wait for A_0 and B_0 only
+    const int after = min(DL_SLOTS, nh) - 2;
+    if (after >= 3)
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (after == 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + aro[0][i]);
+    xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0][i]);
+  }
   for (int kt = 0; kt < KT; ++kt) {
-    const uint16_t* st = lds + (kt & (DL_STAGES - 1)) * DL_STAGE_ELEMS;
-    DL_READ(ya, yb, st, 1)
-    DL_MMA(xa, xb)
-    DL_INTERLEAVE()
-    DL_READ(xa, xb, st, 2)
-    DL_MMA(ya, yb)
-    DL_INTERLEAVE()
-    DL_READ(ya, yb, st, 3)
-    DL_MMA(xa, xb)
-    DL_INTERLEAVE()
-    if (kt + 1 < KT) {
-      // only step kt+1 is outstanding here; lgkmcnt(0): this wave's reads of
-      // step kt's stage have landed before any wave refills it
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const uint16_t* sa = lds + ((2 * kt) % DL_SLOTS) * DL_HALF;
+    const uint16_t* sb = lds + ((2 * kt + 1) % DL_SLOTS) * DL_HALF;
+    const bool b1 = kt >= 1 && kt + 1 < KT;  // second half of B_kt+1
+    const bool a2 = kt >= 1 && kt + 2 < KT;  // A_kt+2
+    DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, b1, 2 * kt + 3, 4)
+    DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, a2, 2 * kt + 4, 0)
+    DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, a2, 2 * kt + 4, 4)
+    const bool more = kt + 1 < KT;
+    if (more) {
+      // A_kt+2 is the only half-stage issued after B_kt+1; lgkmcnt(0): this
+      // wave's reads of step kt have landed before any wave refills its slots
+      if (kt + 2 < KT)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // step kt's stage is fully in registers on every wave: refill it
-      if (kt + 2 < KT) DL_ISSUE(kt + 2)
-      DL_READ(xa, xb, lds + ((kt + 1) & (DL_STAGES - 1)) * DL_STAGE_ELEMS, 0)
     }
-    DL_MMA(ya, yb)
-    DL_INTERLEAVE()
+    // last sub-step: read step kt+1's first, refill A_kt's slot with the
+    // first half of B_kt+2
+    const uint16_t* na = lds + ((2 * kt + 2) % DL_SLOTS) * DL_HALF;
+    const uint16_t* nbs = lds + ((2 * kt + 3) % DL_SLOTS) * DL_HALF;
+    DL_SUB(ya, yb, xa, xb, na, nbs, 0, more, kt + 2 < KT, 2 * kt + 5, 0)
   }
-#undef DL_ISSUE
-#undef DL_READ
-#undef DL_MMA
-#undef DL_INTERLEAVE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef DL_COPY
+#undef DL_SUB
 
   constexpr int BN_OUT = MODE == 0 ? 128 : 256;
   constexpr int CS = BN_OUT + 8;
@@ -689,9 +715,10 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w13) | reinterpret_cast<uintptr_t>(w2) |
        reinterpret_cast<uintptr_t>(y)) & 15)
     return MOELB_EINVAL;
-  // 32-bit element offsets inside the GEMM kernels
-  if ((size_t)rows_x * d >= (1ull << 32) || (size_t)rows * inter >= (1ull << 32) ||
-      (size_t)2 * inter * d >= (1ull << 32))
+  // 32-bit byte offsets inside the GEMM kernels (per operand, from its base)
+  const size_t eb = moelb_elem_bytes(dtype);
+  if ((size_t)rows_x * d * eb >= (1ull << 32) || (size_t)rows * inter * eb >= (1ull << 32) ||
+      (size_t)2 * inter * d * eb >= (1ull << 32))
     return MOELB_EINVAL;
   const size_t need = sched_layout(rows, num_groups, E, inter, dtype, nullptr, nullptr);
   if (!ws || ws_bytes < need) return MOELB_EWORKSPACE;
