@@ -502,14 +502,21 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
       NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS][mi]);                                 \
     }                                                                                                  \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);     \
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ni], FA[mi], acc[mi][ni], 0, 0, 0);     \
     if (DO) DL_COPY(J, (J0) + mi)                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                 \
   }
 
+  // the output row of this thread's tile row (down GEMM: physical row of the
+  // virtual row), fetched now so its latency hides behind the K loop
+  int out_row = 0;
+  if (MODE == 1) {
+    const int v = v0 + tid;
+    out_row = v < vend ? min(max(s.rowmap[v], 0), rows_x - 1) : -1;
+  }
   // the epilogue's scalar arguments are loaded before the loop: a scalar load
   // still in flight would make every LDS wait in the loop a full drain
-  asm volatile("" ::"s"(y), "s"(s.rowmap), "s"(rows_x));
+  asm volatile("" ::"s"(y), "s"(rows_x));
   for (int j = 0; j < DL_SLOTS && j < nh; ++j)
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) DL_COPY(j, jj)
@@ -559,31 +566,50 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
 #undef DL_COPY
 #undef DL_SUB
 
+  // acc[mi][ni] holds its 32x32 block transposed (B fragment as the MFMA's
+  // first operand): lane -> row (lane % 32) of block mi, element j -> column
+  // (j / 4) * 8 + (lane / 32) * 4 + j % 4 of block ni, so a lane owns runs of 4
+  // adjacent output columns and stages them with 8-byte LDS writes.
   constexpr int BN_OUT = MODE == 0 ? 128 : 256;
   constexpr int CS = BN_OUT + 8;
   uint16_t* Cs = lds;
+  int* orow = reinterpret_cast<int*>(lds + MF_BM * CS);  // down GEMM: output row per tile row
   __syncthreads();
+  if (MODE == 1) orow[tid] = out_row;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
+    const int row = wm * 128 + mi * 32 + fr;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    for (int q = 0; q < 4; ++q) {
       if (MODE == 0) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float g = acc[mi][f][r], u = acc[mi][f + 2][r];
-          Cs[row * CS + wn * 64 + f * 32 + fr] = f32_to_bf16(silu_f32(g) * u);
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = acc[mi][f][q * 4 + i], u = acc[mi][f + 2][q * 4 + i];
+            h[i] = f32_to_bf16(silu_f32(g) * u);
+          }
+          *reinterpret_cast<uint2*>(Cs + row * CS + wn * 64 + f * 32 + q * 8 + fh * 4) =
+              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) Cs[row * CS + wn * 128 + ni * 32 + fr] = f32_to_bf16(acc[mi][ni][r]);
+        for (int ni = 0; ni < 4; ++ni) {
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16(acc[mi][ni][q * 4 + i]);
+          *reinterpret_cast<uint2*>(Cs + row * CS + wn * 128 + ni * 32 + q * 8 + fh * 4) =
+              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
       }
     }
   }
   __syncthreads();
-  constexpr int CPR = BN_OUT / 8;
+  constexpr int CPR = BN_OUT / 8;  // 16-byte chunks per row
   const int n0 = nt * BN_OUT;
   const int nout = MODE == 0 ? inter : d;
+#pragma unroll 4
   for (int c = tid; c < MF_BM * CPR; c += MF_THREADS) {
     const int row = c / CPR, ch = c % CPR;
     const int v = v0 + row;
@@ -593,8 +619,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     if (MODE == 0) {
       *reinterpret_cast<uint4*>(y + (size_t)v * inter + col) = val;
     } else {
-      const int prow = min(max(s.rowmap[v], 0), rows_x - 1);
-      *reinterpret_cast<uint4*>(y + (size_t)prow * d + col) = val;
+      *reinterpret_cast<uint4*>(y + (size_t)orow[row] * d + col) = val;
     }
   }
 }
