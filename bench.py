@@ -8,6 +8,13 @@ are seeded synthetic tensors of the workload's shapes, resident in HBM before
 the timed region.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Traffic counters: run under ``rocprofv3 --pmc FETCH_SIZE`` and then
+``--pmc WRITE_SIZE`` with ``--copy-bytes`` (a plain device copy of that many
+bytes follows the timed region and calibrates the counters), then
+``python bench.py --summarize-pmc FETCH_CSV WRITE_CSV`` writes
+profiles/ffn_gate_up_gemm_traffic.json, which later runs report as
+``roofline.traffic`` while the kernel source is unchanged.
 """
 from __future__ import annotations
 
@@ -24,6 +31,8 @@ METRIC = "MoE-layer tokens/s (route+plan+grouped FFN+combine), % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 DEFAULT_WORKLOAD = "c3_qwen3_235b_prefill"
+GATE_UP_KERNEL = "ffn_mfma_dma_kernel<0>"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "ffn_gate_up_gemm_traffic.json")
 
 
 def log(msg):
@@ -84,11 +93,18 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=20480)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed region, one plain device-to-device copy of this many bytes")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 counter_collection.csv files")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
                     help="gate/up GEMM reads h rows through the permutation, or a copied x_perm")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("this build measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
               "run with --gpus 1", file=sys.stderr)
@@ -171,9 +187,8 @@ def main():
         "combine": by["combine"] / (stage["combine"] * 1e-3) / 1e9,
     }
     traffic = None
-    prof = os.path.join(ROOT, "profiles", "ffn_gate_up_gemm_traffic.json")
-    if os.path.exists(prof):
-        with open(prof) as fh:
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
             tr = json.load(fh)
         if tr.get("workload") == cfg.name and tr.get("kernel_source_sha") == _kernel_sha():
             traffic = tr.get("bytes_per_launch")
@@ -196,7 +211,7 @@ def main():
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
                    "ffn_rows": args.rows},
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-        "roofline": {"bound": "mfma", "kernel": "ffn_mfma_kernel<0> (gate/up GEMM + SwiGLU)",
+        "roofline": {"bound": "mfma", "kernel": GATE_UP_KERNEL + " (gate/up GEMM + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flop_per_launch": f["ffn_gate_up_flop"], "avg_launch_ms": round(gu_ms, 4)},
@@ -206,12 +221,60 @@ def main():
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),
     }
+    if args.copy_bytes > 0:
+        # plain copy of known size: the counters' calibration in a PMC run
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_bytes"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg, li, w13, w2, shared, args.cpu_tokens)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def _read_pmc(path, counter):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    return rows
+
+
+def summarize_pmc(workload, fetch_csv, write_csv):
+    """Per-dispatch HBM-side bytes of the gate/up GEMM from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the same
+    counter on the largest plain copy dispatch to the bytes it must move."""
+    out = {"workload": workload, "kernel": GATE_UP_KERNEL, "kernel_source_sha": _kernel_sha()}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _read_pmc(path, counter)
+        gu = [float(r["Counter_Value"]) for r in rows if "ffn_mfma_dma_kernel<0>" in r["Kernel_Name"]]
+        cp = [r for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not gu or not cp:
+            raise SystemExit(f"{path}: no gate/up or copy dispatch with {counter}")
+        big = max(cp, key=lambda r: float(r["Counter_Value"]))
+        out[f"{key}_kib_per_dispatch"] = sum(gu) / len(gu)
+        out[f"{key}_dispatches"] = len(gu)
+        out[f"{key}_copy_kib"] = float(big["Counter_Value"])
+        out[f"{key}_copy_kernel"] = big["Kernel_Name"]
+    out["note"] = ("copy of copy_bytes moves copy_bytes read + copy_bytes written; factor = copy_bytes / "
+                   "(counter KiB x 1024) per counter")
+    cb = int(os.environ.get("COPY_BYTES", "0"))
+    if cb <= 0:
+        raise SystemExit("set COPY_BYTES to the --copy-bytes of the PMC runs")
+    out["copy_bytes"] = cb
+    f_fetch = cb / (out["fetch_copy_kib"] * 1024.0)
+    f_write = cb / (out["write_copy_kib"] * 1024.0)
+    out["fetch_factor"], out["write_factor"] = f_fetch, f_write
+    out["bytes_per_launch"] = (out["fetch_kib_per_dispatch"] * 1024.0 * f_fetch +
+                               out["write_kib_per_dispatch"] * 1024.0 * f_write)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def _kernel_sha():
