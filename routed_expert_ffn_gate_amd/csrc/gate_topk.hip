@@ -27,85 +27,85 @@ constexpr int GATE_BK = 64;        // K per pipeline step
 constexpr int GATE_THREADS = 512;  // 8 waves
 constexpr int A_STRIDE = GATE_BK + 8;  // bf16 elements per LDS row (16 B pad)
 
-__device__ __forceinline__ bool better(float v, int id, float v2, int id2) {
-  // bitwise, not short-circuit: keeps the unrolled merge branch-free
-  return (v > v2) | ((v == v2) & (id < id2));
+// Selection key of logit v of expert id: the float's bits mapped to an
+// order-preserving unsigned integer, the low 8 bits replaced by 255 - id.  A
+// larger key is a larger logit, equal logits rank the lower id first; logits
+// that agree in their top 24 bits (within 2^-15 relative of each other, far
+// inside the near-tie band of a k/k+1 gap below 1e-3) are ranked by id.  The
+// selected ids then read back their exact logits.
+__device__ __forceinline__ uint32_t topk_key(float v, int id) {
+  uint32_t b = __float_as_uint(v);
+  b ^= (b & 0x80000000u) ? 0xffffffffu : 0x80000000u;
+  return (b & 0xffffff00u) | (uint32_t)(255 - id);
 }
 
-// Sorted (descending, ties lower id) insertion into a register list of length KL.
+// Sorted (descending) insertion into a register list of KL keys: one max and
+// one min per list entry.
 template <int KL>
-__device__ __forceinline__ void list_insert(float (&lv)[KL], int (&li)[KL], float x, int xi) {
+__device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
-    const bool b = better(x, xi, lv[i], li[i]);
-    const float tv = b ? x : lv[i];
-    const int ti = b ? xi : li[i];
-    x = b ? lv[i] : x;
-    xi = b ? li[i] : xi;
-    lv[i] = tv;
-    li[i] = ti;
+    const uint32_t hi = max(x, l[i]);
+    x = min(x, l[i]);
+    l[i] = hi;
   }
 }
 
 // Epilogue over `ntok` tokens whose logits (bias included) sit in LDS rows of
 // `stride` floats: columns [0,E) current, [E,2E) lookahead (if has_next).
-// 512 threads: direction = tid / 256, token = (tid % 256) / 4, sub = tid % 4.
+// The 512 threads split into directions (two if has_next), then tokens of
+// `lpt` adjacent lanes (a power of two, 2..8): direction = tid / per_dir,
+// token = (tid % per_dir) / lpt, sub = tid % lpt.
 template <int KL>
-__device__ void topk_epilogue(const float* z, int stride, int ntok, int tok0, int T, int E, int k,
+__device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int tok0, int T, int E, int k,
                               bool has_next, int32_t* __restrict__ idx, float* __restrict__ wts,
                               float* __restrict__ gap, int32_t* __restrict__ idx_next) {
   const int tid = threadIdx.x;
-  const int dir = tid >> 8;
-  const int tl = (tid & 255) >> 2;
-  const int sub = tid & 3;
-  const bool active = tl < ntok && (dir == 0 || has_next);
+  const int per_dir = has_next ? GATE_THREADS / 2 : GATE_THREADS;
+  const int dir = tid / per_dir;
+  const int tl = (tid % per_dir) / lpt;
+  const int sub = tid & (lpt - 1);
+  const bool active = tl < ntok;
   const int t = tok0 + tl;
-  float lv[KL];
-  int li[KL];
+  uint32_t l[KL];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    lv[i] = -INFINITY;
-    li[i] = 0x7fffffff;
-  }
+  for (int i = 0; i < KL; ++i) l[i] = 0u;  // below every real key
   const float* row = z + tl * stride + dir * E;
   if (active) {
-    for (int e = sub; e < E; e += 4) list_insert<KL>(lv, li, row[e], e);
+    for (int e = sub; e < E; e += lpt) list_insert<KL>(l, topk_key(row[e], e));
   }
-  // merge the four partial lists (lanes sub ^ 1, then sub ^ 2)
+  // merge the partial lists of the token's lanes (sub ^ 1, sub ^ 2, ...)
+  for (int m = 1; m < lpt; m <<= 1) {
+    uint32_t p[KL];
 #pragma unroll
-  for (int m = 1; m <= 2; m <<= 1) {
-    float pv[KL];
-    int pi[KL];
+    for (int i = 0; i < KL; ++i) p[i] = __shfl_xor(l[i], m, MOELB_WAVE);
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      pv[i] = __shfl_xor(lv[i], m, MOELB_WAVE);
-      pi[i] = __shfl_xor(li[i], m, MOELB_WAVE);
-    }
-#pragma unroll
-    for (int i = 0; i < KL; ++i) list_insert<KL>(lv, li, pv[i], pi[i]);
+    for (int i = 0; i < KL; ++i) list_insert<KL>(l, p[i]);
   }
+  int li[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(l[i] & 0xffu), E - 1);  // unused entries stay in the row
   if (dir == 0) {
     // softmax denominator over all E logits of this token
-    const float mx = lv[0];
+    const float mx = active ? row[li[0]] : 0.f;
     float s = 0.f;
     if (active)
-      for (int e = sub; e < E; e += 4) s += __expf(row[e] - mx);
-    s += __shfl_xor(s, 1, MOELB_WAVE);
-    s += __shfl_xor(s, 2, MOELB_WAVE);
+      for (int e = sub; e < E; e += lpt) s += __expf(row[e] - mx);
+    for (int m = 1; m < lpt; m <<= 1) s += __shfl_xor(s, m, MOELB_WAVE);
     if (active && sub == 0 && t < T) {
       const float inv = 1.0f / s;
 #pragma unroll
       for (int j = 0; j < KL; ++j) {
         if (j < k) {
           idx[(size_t)t * k + j] = li[j];
-          wts[(size_t)t * k + j] = __expf(lv[j] - mx) * inv;
+          wts[(size_t)t * k + j] = __expf(row[li[j]] - mx) * inv;
         }
       }
       if (gap) {
         float g = INFINITY;
 #pragma unroll
         for (int j = 1; j < KL; ++j)
-          if (j == k && k < E) g = lv[j - 1] - lv[j];
+          if (j == k && k < E) g = fabsf(row[li[j - 1]] - row[li[j]]);
         gap[t] = g;
       }
     }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_bf16_kernel(
     __syncthreads();
     const int t0 = tok0 + half * 64;
     const int ntok = min(64, T - t0);
-    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, t0, T, E, k, has_next, idx, wts, gap, idx_next);
+    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, has_next ? 4 : 8, t0, T, E, k, has_next, idx, wts, gap, idx_next);
     __syncthreads();
   }
 }
@@ -248,11 +248,21 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_bf16_kernel(
 // N = 64 * NF columns and d % 64 == 0.  The h tile (128 x 64) and the router
 // rows (N x 64) of each 64-wide K step stream global -> LDS with
 // global_load_lds_dwordx4 into S swizzled stages (16-byte chunk c of row r in
-// slot c ^ (((r >> 1) ^ (r << 2)) & 7): conflict-free 16-row fragment reads),
-// so S-1 K steps are in flight while one computes; fragment reads are
-// software-pipelined against the MFMAs over two register sets; waits are
-// explicit vmcnt + a bare s_barrier.
+// slot c ^ (((r >> 1) ^ (r << 2)) & 7): conflict-free 16-row fragment reads).
+// A wave is held up while the texture unit accepts a burst of loads, so the
+// refill of a stage is spread over the MFMAs of the following sub-steps.
+// Fragment reads are software-pipelined against the MFMAs over two register
+// sets; one barrier per K step; waits are explicit vmcnt.
 __device__ __forceinline__ int gt_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row << 2)) & 7); }
+
+// 16 bytes per lane, global -> LDS: byte offset voff from the wave-uniform base
+// sbase, lane i lands at LDS byte address m0 + 16 i.  Issued from inline asm so
+// the compiler's LDS wait tracking stays exact; completion is tracked by the
+// caller's explicit vmcnt waits.
+__device__ __forceinline__ void gt_copy16(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 
 template <int NF, int KL, int S>
 __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
@@ -264,6 +274,8 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   constexpr int N = 64 * NF;
   constexpr int STAGE = (GATE_BM + N) * BK;  // elements: A rows, then B rows
   constexpr int VPS = 2 + NF;                // DMA instructions per wave and K step
+  // the logits of all 128 tokens fit in the stages' LDS
+  constexpr bool ONE_PASS = (size_t)GATE_BM * (N + 4) * 4 <= (size_t)S * STAGE * 2;
   extern __shared__ __align__(16) char smem[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   float* Z = reinterpret_cast<float*>(smem);
@@ -275,31 +287,38 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   const bool has_next = w_next != nullptr;
   const int KT = d / BK;
 
-  // DMA rows of this lane: 8-row blocks, row (lane >> 3), slot (lane & 7)
+  // DMA rows of this lane: 8-row blocks, row (lane >> 3), slot (lane & 7);
+  // byte offsets from a wave-uniform base (h, or the router matrix that holds
+  // the whole 8-row block: E is a multiple of 32 here)
   uint32_t aoff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = (wave * 2 + j) * 8 + (lane >> 3);
     const int t = min(tok0 + r, T - 1);  // rows past T are computed and dropped
-    aoff[j] = (uint32_t)t * (uint32_t)d + gt_slot(r, lane & 7) * 8;
+    aoff[j] = ((uint32_t)t * (uint32_t)d + gt_slot(r, lane & 7) * 8) * 2u;
   }
-  const uint16_t* bptr[NF];
+  uint32_t boff[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int r = (wave * NF + j) * 8 + (lane >> 3);
-    const uint16_t* base = r < E ? w_cur + (size_t)r * d : w_next + (size_t)(r - E) * d;
-    bptr[j] = base + gt_slot(r, lane & 7) * 8;
+    boff[j] = ((uint32_t)(r < E ? r : r - E) * (uint32_t)d + gt_slot(r, lane & 7) * 8) * 2u;
   }
-#define GT_ISSUE(KTI)                                                                              \
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  // DMA instruction U (0..VPS-1) of K step KTI: U < 2 are h rows, the rest router rows
+#define GT_COPY(KTI, U)                                                                            \
   {                                                                                                \
-    uint16_t* st_ = lds + ((KTI) % S) * STAGE;                                                     \
-    const uint32_t k0_ = (uint32_t)(KTI) * BK;                                                     \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
-      __builtin_amdgcn_global_load_lds((const void*)(h + (aoff[j] + k0_)),                          \
-                                       (void*)(st_ + (wave * 2 + j) * 8 * BK), 16, 0, 0);           \
-    _Pragma("unroll") for (int j = 0; j < NF; ++j)                                                 \
-      __builtin_amdgcn_global_load_lds((const void*)(bptr[j] + k0_),                                \
-                                       (void*)(st_ + (GATE_BM + (wave * NF + j) * 8) * BK), 16, 0, 0); \
+    const int kti_ = (KTI);                                                                        \
+    const uint32_t st_ = lds_u32 + (uint32_t)((kti_ % S) * STAGE) * 2u;                            \
+    if ((U) < 2) {                                                                                 \
+      gt_copy16(aoff[(U) & 1], h + (size_t)kti_ * BK,                                              \
+                st_ + (uint32_t)((wave_s * 2 + ((U) & 1)) * 8 * BK) * 2u);                         \
+    } else {                                                                                       \
+      const int jb_ = (U) >= 2 ? (U) - 2 : 0;                                                      \
+      const uint16_t* m_ = (wave_s * NF + jb_) * 8 < E ? w_cur : w_next;                           \
+      gt_copy16(boff[jb_], m_ + (size_t)kti_ * BK,                                                 \
+                st_ + (uint32_t)((GATE_BM + (wave_s * NF + jb_) * 8) * BK) * 2u);                  \
+    }                                                                                              \
   }
 
   // fragment rows are (multiple of 16) + (lane % 16): one lane term per 32-wide k sub-step
@@ -317,21 +336,50 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
 #pragma unroll
     for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bf16x8_t xa[4], xb[NF], ya[4], yb[NF];
-#define GT_READ(FA, FB, ST, KS)                                                                    \
-  {                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
-      FA[i] = *reinterpret_cast<const bf16x8_t*>((ST) + arow0 + i * 16 * BK + kofs[KS]);           \
-    _Pragma("unroll") for (int i = 0; i < NF; ++i)                                                 \
-      FB[i] = *reinterpret_cast<const bf16x8_t*>((ST) + brow0 + i * 16 * BK + kofs[KS]);           \
+  // refill of a freed stage: instructions [0, H1) right after the barrier that
+  // frees it, [H1, VPS) during the next step's first sub-step (two stages: all
+  // at once, it is needed one step later)
+  constexpr int H1 = S >= 3 ? (VPS + 1) / 2 : VPS;
+  constexpr int BPM = (NF + 3) / 4;  // router fragments read per 16-row block
+  // One 32-wide k sub-step: per 16-row block mi, read the next set's fragments
+  // (sub-step KS of stage RS, if RD), run the block's NF MFMAs on the current
+  // set, and issue a share of DMA instructions [P0, P1) of K step KI (if DO).
+#define GT_SUB(FA, FB, NA, NB, RS, KS, RD, DO, KI, P0, P1)                                         \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                               \
+    if (RD) {                                                                                      \
+      const uint16_t* rs_ = (RS);                                                                  \
+      NA[mi] = *reinterpret_cast<const bf16x8_t*>(rs_ + arow0 + mi * 16 * BK + kofs[KS]);          \
+      _Pragma("unroll") for (int q = 0; q < BPM; ++q) {                                            \
+        const int i_ = mi * BPM + q;                                                               \
+        if (i_ < NF) NB[i_] = *reinterpret_cast<const bf16x8_t*>(rs_ + brow0 + i_ * 16 * BK + kofs[KS]); \
+      }                                                                                            \
+    }                                                                                              \
+    _Pragma("unroll") for (int ni = 0; ni < NF; ++ni)                                              \
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0); \
+    if (DO) {                                                                                      \
+      constexpr int per_ = ((P1) - (P0) + 3) / 4;                                                  \
+      _Pragma("unroll") for (int q = 0; q < per_; ++q) {                                           \
+        const int u_ = (P0) + mi * per_ + q;                                                       \
+        if (u_ < (P1)) GT_COPY(KI, u_)                                                             \
+      }                                                                                            \
+    }                                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
   }
-#define GT_MMA(FA, FB)                                                                             \
-  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                                 \
-  _Pragma("unroll") for (int ni = 0; ni < NF; ++ni)                                                \
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
-#define GT_FENCE() __builtin_amdgcn_sched_barrier(0);
 
+  // this lane's logit biases, fetched now so the latency hides behind the K loop
+  float bias[NF];
+#pragma unroll
+  for (int ni = 0; ni < NF; ++ni) {
+    const int col = wn * NF * 16 + ni * 16 + (lane & 15);
+    bias[ni] = col < E ? b_cur[col] : b_next[col - E];
+  }
+  // scalar loads still in flight would turn every LDS wait of the loop into a full drain
+  asm volatile("" ::"s"(idx), "s"(wts), "s"(idx_next), "s"(gap));
   for (int t = 0; t < S; ++t)
-    if (t < KT) GT_ISSUE(t)
+    if (t < KT) {
+#pragma unroll
+      for (int u = 0; u < VPS; ++u) GT_COPY(t, u)
+    }
   {
     const int after = min(S, KT) - 1;  // steps issued after step 0
     if (after >= 2)
@@ -343,56 +391,69 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  GT_READ(xa, xb, lds, 0)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + arow0 + i * 16 * BK + kofs[0]);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + brow0 + i * 16 * BK + kofs[0]);
   for (int kt = 0; kt < KT; ++kt) {
-    const uint16_t* st = lds + (kt % S) * STAGE;
-    GT_READ(ya, yb, st, 1)
-    GT_MMA(xa, xb)
-    GT_FENCE()
-    if (kt + 1 < KT) {
-      // steps issued after kt+1 may stay in flight
-      const int after = min(kt + S - 1, KT - 1) - (kt + 1);
-      // lgkmcnt(0): this wave's reads of step kt's stage have landed before
-      // any wave refills it
-      if (after >= 1)
+    // first sub-step; second part of the refill of the stage freed one step ago
+    const bool p2 = S >= 3 && kt >= 1 && kt - 1 + S < KT;
+    GT_SUB(xa, xb, ya, yb, lds + (kt % S) * STAGE, 1, true, p2, kt - 1 + S, H1, VPS)
+    const bool more = kt + 1 < KT;
+    if (more) {
+      // step kt+1 landed: only step kt+2 (three stages) may still be in flight;
+      // lgkmcnt(0): this wave's reads of step kt are done before its stage is refilled
+      if (S >= 3 && kt + 2 < KT)
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VPS) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // step kt's stage is in registers on every wave: refill it with step kt+S
-      if (kt + S < KT) GT_ISSUE(kt + S)
-      GT_READ(xa, xb, lds + ((kt + 1) % S) * STAGE, 0)
     }
-    GT_MMA(ya, yb)
-    GT_FENCE()
+    // second sub-step; first part of the refill of step kt's stage with step kt+S
+    GT_SUB(ya, yb, xa, xb, lds + ((kt + 1) % S) * STAGE, 0, more, more && kt + S < KT, kt + S, 0, H1)
   }
-#undef GT_ISSUE
-#undef GT_READ
-#undef GT_MMA
-#undef GT_FENCE
+#undef GT_COPY
+#undef GT_SUB
   __syncthreads();  // LDS is reused for the logits
 
   const int colbase = wn * NF * 16;
+  if (ONE_PASS) {
+    // all 128 tokens' logits fit in LDS: one selection pass
+#pragma unroll
+    for (int ni = 0; ni < NF; ++ni) {
+      const int col = colbase + ni * 16 + (lane & 15);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+          Z[r * zstride + col] = acc[mi][ni][i] + bias[ni];
+        }
+    }
+    __syncthreads();
+    const int ntok = min(GATE_BM, T - tok0);
+    topk_epilogue<KL>(Z, zstride, ntok, has_next ? 2 : 4, tok0, T, E, k, has_next, idx, wts, gap, idx_next);
+    return;
+  }
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
       for (int ni = 0; ni < NF; ++ni) {
         const int col = colbase + ni * 16 + (lane & 15);
-        const float bias = col < E ? b_cur[col] : b_next[col - E];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = mi * 16 + (lane >> 4) * 4 + i;
-            Z[r * zstride + col] = acc[mi][ni][i] + bias;
+            Z[r * zstride + col] = acc[mi][ni][i] + bias[ni];
           }
       }
     }
     __syncthreads();
     const int t0 = tok0 + half * 64;
     const int ntok = min(64, T - t0);
-    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, t0, T, E, k, has_next, idx, wts, gap, idx_next);
+    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, has_next ? 4 : 8, t0, T, E, k, has_next, idx, wts, gap, idx_next);
     __syncthreads();
   }
 }
@@ -428,7 +489,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_f32_kernel(
     Z[tl * zstride + col] = s + (col < E ? b_cur[col] : b_next[col - E]);
   }
   __syncthreads();
-  topk_epilogue<KL>(Z, zstride, ntok, tok0, T, E, k, has_next, idx, wts, gap, idx_next);
+  topk_epilogue<KL>(Z, zstride, ntok, has_next ? 4 : 8, tok0, T, E, k, has_next, idx, wts, gap, idx_next);
 }
 
 int zstride_for(int N) { return ((N + 63) / 64) * 64 + 4; }
@@ -535,7 +596,7 @@ extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dt
   if (dtype == MOELB_BF16) {
     const int N = w_next ? 2 * E : E;
     const int NF = (N + 63) / 64;
-    if (N % 64 == 0 && NF <= (k <= 8 ? 7 : 6) && d % 64 == 0 && (size_t)T * d < (1ull << 32)) {
+    if (N % 64 == 0 && NF <= (k <= 8 ? 7 : 6) && d % 64 == 0 && (size_t)T * d * 2 < (1ull << 32)) {
       if (k <= 2) return launch_dma<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
       if (k <= 4) return launch_dma<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
       if (k <= 8) return launch_dma<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
