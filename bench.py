@@ -113,7 +113,7 @@ def main():
     import numpy as np
     import torch
     from synth import workloads as W
-    from routed_expert_ffn_gate_amd.layer import HipEvents, MoELayer, STAGES, to_device
+    from routed_expert_ffn_gate_amd.layer import EVENTS_PER_STEP, HipEvents, MoELayer, stage_times_ms, to_device
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -145,24 +145,21 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = HipEvents(12 * K + 2)
+    EPS = EVENTS_PER_STEP
+    ev = HipEvents(EPS * K + 2)
     torch.cuda.synchronize()
-    ev.record(12 * K, stream)
+    ev.record(EPS * K, stream)
     for i in range(K):
-        layer.step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2, events=ev, ev_base=12 * i)
-    ev.record(12 * K + 1, stream)
+        layer.step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2, events=ev, ev_base=EPS * i)
+    ev.record(EPS * K + 1, stream)
     torch.cuda.synchronize()
-    total_ms = ev.elapsed_ms(12 * K, 12 * K + 1)
+    total_ms = ev.elapsed_ms(EPS * K, EPS * K + 1)
     ms = total_ms / K
-    stage = {s: 0.0 for s in STAGES}
-    sub = {"ffn_schedule": 0.0, "ffn_gate_up_gemm": 0.0, "ffn_down_gemm": 0.0}
+    stage = {}
     for i in range(K):
-        b = 12 * i
-        for j, s in enumerate(STAGES):
-            stage[s] += ev.elapsed_ms(b + j, b + j + 1) / K
-        sub["ffn_schedule"] += ev.elapsed_ms(b + 8, b + 9) / K
-        sub["ffn_gate_up_gemm"] += ev.elapsed_ms(b + 9, b + 10) / K
-        sub["ffn_down_gemm"] += ev.elapsed_ms(b + 10, b + 11) / K
+        for name, v in stage_times_ms(ev, EPS * i).items():
+            stage[name] = stage.get(name, 0.0) + v / K
+    sub = {n: stage.pop(n) for n in ("ffn_schedule", "ffn_gate_up_gemm", "ffn_down_gemm")}
 
     # the row-materialising permutation, timed on its own (the step reads rows
     # of h straight through the permutation instead)

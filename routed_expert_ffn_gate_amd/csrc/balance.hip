@@ -6,15 +6,19 @@
 //   one LDS atomic (ballot), which takes the hot expert off the atomic path.
 // * Plan -- Libra README "Key Ideas", locality-aware expert replication
 //   planning (Phase 1 imports, Phase 2 balancing).  One workgroup; counts,
-//   host masks, slots and loads live in LDS.  Phase 1 runs one wave per rank
-//   (wave argmax per import).  Each Phase 2 step evaluates every expert's
-//   candidate move in parallel (one thread per expert) and keeps the best
-//   accepted one by (load on the most-loaded rank, then lower id) -- the same
-//   move the sequential walk takes first.
+//   host masks and slots live in LDS.  Phase 1 runs one wave per rank (wave
+//   argmax per import).  Phase 2 runs in one wave: lane r holds rank r's load,
+//   each lane owns four experts; every step evaluates all candidate moves in
+//   parallel and keeps the best accepted one by (load on the most-loaded rank,
+//   then lower id) -- the move the sequential walk takes first -- with wave
+//   reductions, and only the moved expert's contributions are updated.
 // * Split -- Relief ("A Per-Step Load-Balancing Engine for Expert-Parallel MoE
 //   Serving"), "The Relief Algorithm" and Algorithm 1: pairwise halving over
-//   replica edges in edge-coloured, rank-disjoint rounds, one barrier per
-//   round, no atomics in the relaxation.  Whole tokens in int32.
+//   replica edges in edge-coloured, rank-disjoint rounds, no atomics in the
+//   relaxation.  Whole tokens in int32.  Setup is parallel over experts (host
+//   masks by atomic OR, transfer offsets by a block scan); the colouring and
+//   the rounds run in one wave, whose own in-order LDS accesses order the
+//   rounds without barriers.
 #include "common.h"
 
 namespace {
@@ -81,8 +85,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* __res
   int* slots = reinterpret_cast<int*>(hostmask + E);          // [G][N]
   int* nslots = slots + G * N;                                // [G]
   int* load = nslots + G;                                     // [G]
-  __shared__ int s_a, s_any_free;
-  __shared__ unsigned long long s_best;
 
   const int tid = threadIdx.x;
   const int e = tid;
@@ -143,98 +145,143 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* __res
   }
   __syncthreads();
 
-  // Phase 2
-  for (int step = 0; step <= G * N; ++step) {
-    for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
-    if (tid == 0) s_best = 0ull;
-    __syncthreads();
-    int R = 0, m = 0;
-    uint64_t mask = 0;
-    if (e < E) {
-      mask = hostmask[e];
-      m = __popcll(mask);
-      for (int s = 0; s < G; ++s)
-        if (!((mask >> s) & 1ull)) R += c[s * E + e];
-      int pos = 0;
-      for (int s = 0; s < G; ++s)
-        if ((mask >> s) & 1ull) {
-          atomicAdd(&load[s], c[s * E + e] + even_share(R, m, pos));
-          ++pos;
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int a = 0, any = 0;
-      for (int r = 0; r < G; ++r) {
-        if (load[r] > load[a]) a = r;
-        any |= nslots[r] < N;
+  // Phase 2 starts from the modeled loads of the Phase 1 placement
+  for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
+  int* Rarr = reinterpret_cast<int*>(hostmask + E) + G * N + 2 * G;  // [E] remote pool per expert
+  __syncthreads();
+  if (e < E) {
+    const uint64_t mask = hostmask[e];
+    const int m = __popcll(mask);
+    int R = 0;
+    for (int s = 0; s < G; ++s)
+      if (!((mask >> s) & 1ull)) R += c[s * E + e];
+    Rarr[e] = R;
+    int pos = 0;
+    for (int s = 0; s < G; ++s)
+      if ((mask >> s) & 1ull) {
+        atomicAdd(&load[s], c[s * E + e] + even_share(R, m, pos));
+        ++pos;
       }
-      s_a = a;
-      s_any_free = any;
-    }
-    __syncthreads();
-    if (!s_any_free) break;
-    const int a = s_a;
-    int best_b = -1;
-    if (e < E && ((mask >> a) & 1ull) && R > 0) {
-      int b = -1;
-      for (int r = 0; r < G; ++r)
-        if (!((mask >> r) & 1ull) && nslots[r] < N && (b < 0 || load[r] < load[b])) b = r;
-      if (b >= 0) {
-        const int share_a = even_share(R, m, host_pos(mask, a));
-        const uint64_t mask2 = mask | (1ull << b);
-        const int R2 = R - c[b * E + e];
-        const int new_a = load[a] - share_a + even_share(R2, m + 1, host_pos(mask2, a));
-        const int new_b = load[b] + c[b * E + e] + even_share(R2, m + 1, host_pos(mask2, b));
-        if (max(new_a, new_b) < load[a]) {
-          const int contrib = c[a * E + e] + share_a;
-          const unsigned long long key =
-              (static_cast<unsigned long long>(static_cast<unsigned>(contrib)) << 16) | (0xffffu - e);
-          atomicMax(&s_best, key);
-          best_b = b;
-        }
-      }
-    }
-    __syncthreads();
-    const unsigned long long best = s_best;
-    if (best == 0ull) break;
-    const int be = 0xffff - static_cast<int>(best & 0xffffull);
-    if (e == be) {
-      hostmask[e] = mask | (1ull << best_b);
-      slots[best_b * N + nslots[best_b]] = e;
-      nslots[best_b] += 1;
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  if (tid >= 64) return;
 
-  for (int i = tid; i < G * N; i += blockDim.x) replica[i] = slots[i];
-  if (plan_load) {
-    // final modeled loads
-    for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
-    __syncthreads();
-    if (e < E) {
-      const uint64_t mask = hostmask[e];
-      const int m = __popcll(mask);
-      int R = 0;
-      for (int s = 0; s < G; ++s)
-        if (!((mask >> s) & 1ull)) R += c[s * E + e];
-      int pos = 0;
-      for (int s = 0; s < G; ++s)
-        if ((mask >> s) & 1ull) {
-          atomicAdd(&load[s], c[s * E + e] + even_share(R, m, pos));
-          ++pos;
+  // Phase 2 runs in one wave, everything in registers or LDS that only this
+  // wave touches: lane r holds rank r's load and slot count; lane l owns
+  // experts l, l+64, l+128, l+192 (mask and remote pool).  A move changes only
+  // the contributions of the replicated expert, so loads update incrementally.
+  const int lane = tid;
+  int my_load = lane < G ? load[lane] : 0;
+  int my_nslots = lane < G ? nslots[lane] : N;
+  uint64_t emask[4];
+  int eR[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int x = lane + 64 * q;
+    emask[q] = x < E ? hostmask[x] : 0ull;
+    eR[q] = x < E ? Rarr[x] : 0;
+  }
+  for (int step = 0; step <= G * N; ++step) {
+    // most-loaded rank (ties: lowest) and whether any slot is free
+    int a_load = lane < G ? my_load : INT_MIN, a = lane < G ? lane : 0x7fffffff;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int ol = __shfl_xor(a_load, o, 64), oa = __shfl_xor(a, o, 64);
+      if (ol > a_load || (ol == a_load && oa < a)) {
+        a_load = ol;
+        a = oa;
+      }
+    }
+    if (__ballot(lane < G && my_nslots < N) == 0ull) break;
+    // candidate move of each owned expert hosted on a: least-loaded eligible b
+    int bb[4] = {-1, -1, -1, -1}, bl[4] = {0, 0, 0, 0};
+    for (int r = 0; r < G; ++r) {
+      const int lr = __shfl(my_load, r, 64), nr = __shfl(my_nslots, r, 64);
+      if (nr >= N) continue;  // uniform
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!((emask[q] >> r) & 1ull) && (bb[q] < 0 || lr < bl[q])) {
+          bb[q] = r;
+          bl[q] = lr;
+        }
+      }
+    }
+    unsigned long long key = 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int x = lane + 64 * q;
+      const uint64_t mask = emask[q];
+      if (x < E && ((mask >> a) & 1ull) && eR[q] > 0 && bb[q] >= 0) {
+        const int b = bb[q];
+        const int m = __popcll(mask);
+        const int share_a = even_share(eR[q], m, host_pos(mask, a));
+        const uint64_t mask2 = mask | (1ull << b);
+        const int R2 = eR[q] - c[b * E + x];
+        const int new_a = a_load - share_a + even_share(R2, m + 1, host_pos(mask2, a));
+        const int new_b = bl[q] + c[b * E + x] + even_share(R2, m + 1, host_pos(mask2, b));
+        if (max(new_a, new_b) < a_load) {
+          const int contrib = c[a * E + x] + share_a;
+          const unsigned long long k2 = (static_cast<unsigned long long>(static_cast<unsigned>(contrib)) << 16) |
+                                        (static_cast<unsigned long long>(255 - x) << 8) | static_cast<unsigned>(b);
+          key = k2 > key ? k2 : key;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long ok = __shfl_xor(key, o, 64);
+      key = ok > key ? ok : key;
+    }
+    if (key == 0ull) break;
+    const int be = 255 - static_cast<int>((key >> 8) & 0xffull);
+    const int b = static_cast<int>(key & 0xffull);
+    // owner's state of be before the move, broadcast
+    const int owner = be & 63, qq = be >> 6;
+    uint64_t om = 0ull;
+    int oR = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q == qq) {
+        om = emask[q];
+        oR = eR[q];
+      }
+    const uint64_t mask_old = __shfl(om, owner, 64);
+    const int R_old = __shfl(oR, owner, 64);
+    const uint64_t mask_new = mask_old | (1ull << b);
+    const int R_new = R_old - c[b * E + be];
+    // every rank updates its own load with be's contribution change
+    if (lane < G) {
+      const int m0 = __popcll(mask_old), m1 = m0 + 1;
+      const int cr = c[lane * E + be];
+      const int before = ((mask_old >> lane) & 1ull) ? cr + even_share(R_old, m0, host_pos(mask_old, lane)) : 0;
+      const int after = ((mask_new >> lane) & 1ull) ? cr + even_share(R_new, m1, host_pos(mask_new, lane)) : 0;
+      my_load += after - before;
+      if (lane == b) {
+        slots[b * N + my_nslots] = be;
+        my_nslots += 1;
+      }
+    }
+    if (lane == owner) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == qq) {
+          emask[q] = mask_new;
+          eR[q] = R_new;
         }
     }
-    __syncthreads();
-    for (int r = tid; r < G; r += blockDim.x) plan_load[r] = load[r];
   }
+  // every slot written in Phase 2 was written by this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  for (int i = lane; i < G * N; i += 64) replica[i] = slots[i];
+  if (plan_load && lane < G) plan_load[lane] = my_load;
 }
 
 // ---------------------------------------------------------------- split
 
-constexpr int SPLIT_THREADS = 256;
+constexpr int SPLIT_THREADS = 256;                        // >= MOELB_MAX_E: one thread per expert
 constexpr int MAX_TRANSFERS = MOELB_MAX_G * MOELB_MAX_N;  // one per replica slot
 constexpr int COLOUR_WORDS = 32;                          // up to 1024 colours
+constexpr int TR_PER_LANE = MAX_TRANSFERS / 64;
 
 __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __restrict__ counts,
                                                                const int32_t* __restrict__ home,
@@ -242,41 +289,44 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
                                                                int N, int passes, int eps,
                                                                int32_t* __restrict__ host_count,
                                                                int32_t* __restrict__ load_out) {
-  __shared__ uint64_t hostmask[MOELB_MAX_E];
+  __shared__ unsigned long long hostmask[MOELB_MAX_E];
   __shared__ int xhome[MOELB_MAX_E];        // pool mass on the home rank (replicated experts)
   __shared__ int toff[MOELB_MAX_E + 1];     // first transfer of each expert
-  __shared__ int t_u[MAX_TRANSFERS], t_v[MAX_TRANSFERS], t_e[MAX_TRANSFERS], t_x[MAX_TRANSFERS];
-  __shared__ int t_col[MAX_TRANSFERS];
-  __shared__ int order[MAX_TRANSFERS];      // transfers sorted by colour
-  __shared__ int round_off[MAX_TRANSFERS + 1];
+  __shared__ int t_u[MAX_TRANSFERS], t_v[MAX_TRANSFERS], t_x[MAX_TRANSFERS];
+  __shared__ int t_e[MAX_TRANSFERS];
   __shared__ unsigned used[MOELB_MAX_G][COLOUR_WORDS];
   __shared__ int load[MOELB_MAX_G];
-  __shared__ int s_rounds, s_ntr;
+  __shared__ int wave_sum[SPLIT_THREADS / 64];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int e = tid;
   for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
   for (int i = tid; i < G * COLOUR_WORDS; i += blockDim.x) used[i / COLOUR_WORDS][i % COLOUR_WORDS] = 0u;
+  // replica slots (at most 2 per thread) are fetched with the home ranks
+  const int rs0 = tid < G * N ? replica[tid] : -1;
+  const int rs1 = tid + SPLIT_THREADS < G * N ? replica[tid + SPLIT_THREADS] : -1;
   int my_home = 0;
-  uint64_t mask = 0;
   if (e < E) {
     my_home = clamp_rank(home[e], G);
-    mask = 1ull << my_home;
-    for (int r = 0; r < G; ++r)
-      for (int j = 0; j < N; ++j)
-        if (replica[r * N + j] == e) mask |= 1ull << r;
-    hostmask[e] = mask;
+    hostmask[e] = 1ull << my_home;
   }
+  __syncthreads();
+  // replica slots set their host bits
+  if (rs0 >= 0 && rs0 < E) atomicOr(&hostmask[rs0], 1ull << (tid / N));
+  if (rs1 >= 0 && rs1 < E) atomicOr(&hostmask[rs1], 1ull << ((tid + SPLIT_THREADS) / N));
   __syncthreads();
 
   // fixed loads, initial even split, unreplicated pools
+  uint64_t mask = 0;
   int R = 0, m = 0;
   if (e < E) {
+    mask = hostmask[e];
     m = __popcll(mask);
-    for (int s = 0; s < G; ++s) {
-      const int cs = counts[(size_t)s * E + e];
-      if ((mask >> s) & 1ull)
-        atomicAdd(&load[s], cs);
+    for (int s2 = 0; s2 < G; ++s2) {
+      const int cs = counts[(size_t)s2 * E + e];
+      if ((mask >> s2) & 1ull)
+        atomicAdd(&load[s2], cs);
       else
         R += cs;
     }
@@ -286,15 +336,21 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
       host_count[(size_t)e * G + my_home] = R;
     }
   }
-  // transfer list: (home(e), v, e) for e ascending, v ascending
-  if (tid == 0) {
-    int n = 0;
-    for (int x = 0; x < E; ++x) {
-      toff[x] = n;
-      n += __popcll(hostmask[x]) - 1;
+  // transfer list: (home(e), v, e) for e ascending, v ascending; offsets by a block scan
+  {
+    const int cnt = (e < E) ? m - 1 : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
     }
-    toff[E] = n;
-    s_ntr = n;
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wave_sum[w];
+    if (e < E) toff[e] = base + incl - cnt;
+    if (tid == SPLIT_THREADS - 1) toff[E] = base + incl;  // E <= SPLIT_THREADS
   }
   __syncthreads();
   if (e < E && m > 1) {
@@ -314,75 +370,141 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
       }
     }
   }
+  const int n = toff[E];
   __syncthreads();
+  if (tid >= 64) return;
 
-  // greedy edge colouring in list order, then transfers grouped by colour
-  if (tid == 0) {
-    const int n = s_ntr;
-    int ncol = 0;
+  // One wave from here.  Greedy edge colouring in list order.  Fast path: lane
+  // r holds rank r's used colours below 64 in a register; if some transfer
+  // finds none free, the colouring is redone with LDS words (1024 colours).
+  int my_col[TR_PER_LANE];
+  int ncol = 0;
+  bool wide = false;
+  {
+    uint32_t used_lo = 0u, used_hi = 0u;  // rank `lane`'s used colours 0..63
+    const int my_u = lane < n ? t_u[lane] : 0, my_v = lane < n ? t_v[lane] : 0;
     for (int t = 0; t < n; ++t) {
-      const int u = t_u[t], v = t_v[t];
-      int col = 0;
-      for (int w = 0; w < COLOUR_WORDS; ++w) {
-        const unsigned fr = ~(used[u][w] | used[v][w]);
-        if (fr) {
-          col = w * 32 + __builtin_ctz(fr);
-          break;
-        }
+      const int src = t & 63;
+      int u, v;
+      if (t < 64) {  // endpoints from registers, broadcast with readlane
+        u = __builtin_amdgcn_readlane(my_u, src);
+        v = __builtin_amdgcn_readlane(my_v, src);
+      } else {
+        u = t_u[t];
+        v = t_v[t];
+        u = __builtin_amdgcn_readfirstlane(u);
+        v = __builtin_amdgcn_readfirstlane(v);
       }
-      used[u][col >> 5] |= 1u << (col & 31);
-      used[v][col >> 5] |= 1u << (col & 31);
-      t_col[t] = col;
+      const uint32_t blo = __builtin_amdgcn_readlane(used_lo, u) | __builtin_amdgcn_readlane(used_lo, v);
+      const uint32_t bhi = __builtin_amdgcn_readlane(used_hi, u) | __builtin_amdgcn_readlane(used_hi, v);
+      if ((blo & bhi) == ~0u) {
+        wide = true;
+        break;
+      }
+      const int col = blo != ~0u ? __builtin_ctz(~blo) : 32 + __builtin_ctz(~bhi);
+      if (lane == u || lane == v) {
+        if (col < 32)
+          used_lo |= 1u << col;
+        else
+          used_hi |= 1u << (col - 32);
+      }
+#pragma unroll
+      for (int q = 0; q < TR_PER_LANE; ++q)
+        if (t == lane + 64 * q) my_col[q] = col;
       ncol = max(ncol, col + 1);
     }
-    // counting sort by colour
-    for (int r = 0; r <= ncol; ++r) round_off[r] = 0;
-    for (int t = 0; t < n; ++t) round_off[t_col[t] + 1] += 1;
-    for (int r = 0; r < ncol; ++r) round_off[r + 1] += round_off[r];
-    for (int r = 0; r < ncol; ++r) {
-      int q = round_off[r];
-      for (int t = 0; t < n; ++t)
-        if (t_col[t] == r) order[q++] = t;
-    }
-    s_rounds = ncol;
   }
-  __syncthreads();
-
-  // relaxation: passes x rounds, transfers of a round in parallel
-  const int nrounds = s_rounds;
-  for (int p = 0; p < passes; ++p) {
-    for (int rd = 0; rd < nrounds; ++rd) {
-      const int q = round_off[rd] + tid;
-      if (q < round_off[rd + 1]) {
-        const int t = order[q];
-        const int u = t_u[t], v = t_v[t], x = t_e[t];
-        const int gap = load[u] - load[v];
-        int delta = (gap < 0 ? -gap : gap) >> 1;
-        const int limit = gap > 0 ? xhome[x] : t_x[t];
-        delta = min(delta, limit);
-        if (delta > eps) {
-          if (gap > 0) {
-            load[u] -= delta;
-            load[v] += delta;
-            xhome[x] -= delta;
-            t_x[t] += delta;
-          } else {
-            load[v] -= delta;
-            load[u] += delta;
-            t_x[t] -= delta;
-            xhome[x] += delta;
+  if (wide) {
+    ncol = 0;
+    for (int t = 0; t < n; ++t) {
+      const int u = t_u[t], v = t_v[t];
+      const unsigned fr = lane < COLOUR_WORDS ? ~(used[u][lane] | used[v][lane]) : 0u;
+      const uint64_t nz = __ballot(fr != 0u);
+      const int w = nz ? __ffsll(static_cast<long long>(nz)) - 1 : 0;
+      const int col = w * 32 + __builtin_ctz(__shfl(fr, w, 64) | (nz ? 0u : 1u));
+      if (lane == w) {
+        used[u][w] |= 1u << (col & 31);
+        used[v][w] |= 1u << (col & 31);
+      }
+#pragma unroll
+      for (int q = 0; q < TR_PER_LANE; ++q)
+        if (t == lane + 64 * q) my_col[q] = col;
+      ncol = max(ncol, col + 1);
+    }
+  }
+  // relaxation: passes x rounds; the transfers of a round touch disjoint
+  // ranks (and experts), and one wave applies them in order with its own LDS
+  // accesses.  A pass that moves nothing leaves every later pass unchanged,
+  // so the loop stops there.
+  if (n <= 64) {
+    // one transfer per lane, its endpoints and mass in registers
+    const bool has = lane < n;
+    const int u = has ? t_u[lane] : 0, v = has ? t_v[lane] : 0, x = has ? t_e[lane] : 0;
+    const int col = has ? my_col[0] : -1;
+    int tx = has ? t_x[lane] : 0;
+    for (int p = 0; p < passes; ++p) {
+      bool moved = false;
+      for (int rd = 0; rd < ncol; ++rd) {
+        if (col == rd) {
+          const int lu = load[u], lv = load[v], xh = xhome[x];
+          const int gap = lu - lv;
+          int delta = (gap < 0 ? -gap : gap) >> 1;
+          delta = min(delta, gap > 0 ? xh : tx);
+          if (delta > eps) {
+            const int sd = gap > 0 ? delta : -delta;  // mass moved from u to v
+            load[u] = lu - sd;
+            load[v] = lv + sd;
+            xhome[x] = xh - sd;
+            tx += sd;
+            moved = true;
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       }
-      __syncthreads();
+      if (__ballot(moved) == 0ull) break;
+    }
+    if (has) t_x[lane] = tx;
+  } else {
+    for (int p = 0; p < passes; ++p) {
+      bool moved = false;
+      for (int rd = 0; rd < ncol; ++rd) {
+#pragma unroll
+        for (int q = 0; q < TR_PER_LANE; ++q) {
+          const int t = lane + 64 * q;
+          if (t < n && my_col[q] == rd) {
+            const int u = t_u[t], v = t_v[t], x = t_e[t];
+            const int gap = load[u] - load[v];
+            int delta = (gap < 0 ? -gap : gap) >> 1;
+            const int limit = gap > 0 ? xhome[x] : t_x[t];
+            delta = min(delta, limit);
+            if (delta > eps) {
+              if (gap > 0) {
+                load[u] -= delta;
+                load[v] += delta;
+                xhome[x] -= delta;
+                t_x[t] += delta;
+              } else {
+                load[v] -= delta;
+                load[u] += delta;
+                t_x[t] -= delta;
+                xhome[x] += delta;
+              }
+              moved = true;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      }
+      if (__ballot(moved) == 0ull) break;
     }
   }
-
-  if (e < E && m > 1) {
-    host_count[(size_t)e * G + my_home] = xhome[e];
-    for (int t = toff[e]; t < toff[e + 1]; ++t) host_count[(size_t)e * G + t_v[t]] = t_x[t];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int t = lane; t < n; t += 64) {
+    const int x = t_e[t];
+    host_count[(size_t)x * G + t_v[t]] = t_x[t];
+    if (t == toff[x]) host_count[(size_t)x * G + t_u[t]] = xhome[x];  // t_u is x's home
   }
-  for (int r = tid; r < G; r += blockDim.x) load_out[r] = load[r];
+  for (int r = lane; r < G; r += 64) load_out[r] = load[r];
 }
 
 }  // namespace
@@ -407,7 +529,8 @@ extern "C" int moelb_plan(const int32_t* counts, const int32_t* home, int G, int
     return MOELB_EINVAL;
   if (!counts || !home || (N > 0 && !replica)) return MOELB_EINVAL;
   if (N == 0 && !plan_load) return MOELB_OK;
-  const size_t lds = (size_t)((G * E + 1) & ~1) * 4 + (size_t)E * 8 + (size_t)G * N * 4 + (size_t)G * 8;
+  const size_t lds =
+      (size_t)((G * E + 1) & ~1) * 4 + (size_t)E * 8 + (size_t)G * N * 4 + (size_t)G * 8 + (size_t)E * 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!moelb_allow_lds(plan_kernel, lds)) return MOELB_ELAUNCH;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), lds, s, counts, home, G, E, N, L, replica,

@@ -3,9 +3,11 @@
 PyTorch only allocates device memory and supplies the stream; every stage
 runs in the HIP library:
 
-  gate_topk (current + lookahead) -> histogram x2 -> plan (next layer)
-  -> split (this step, with the plan made one step earlier) -> permute
-  -> grouped SwiGLU FFN (+ shared expert) -> combine
+  gate_topk (current + lookahead) -> histogram -> split (this step, with the
+  plan made one step earlier) -> permute -> grouped SwiGLU FFN (+ shared
+  expert) -> combine,
+  and, on a side stream after the gate, the lookahead histogram and the plan
+  for the next layer, joined before the step ends
 
 The hidden-state rows are read by the gate/up GEMM straight from ``h``
 through the permutation (``gather_rows=True``, the default; the permutation
@@ -23,7 +25,10 @@ import torch
 
 from . import moelb as M
 
-STAGES = ["gate_topk", "histogram", "plan", "split", "permute", "grouped_ffn", "combine"]
+# Stages on the step's stream, in order; the lookahead histogram and the next
+# layer's plan run on a side stream (they feed the next step, not this one).
+STAGES = ["gate_topk", "histogram", "split", "permute", "grouped_ffn", "combine", "join"]
+EVENTS_PER_STEP = 14
 
 
 def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -134,6 +139,9 @@ class MoELayer:
                                    device=self.dev)
         self.ws_ffn = torch.empty((max(1, M.moelb_grouped_ffn_workspace_bytes(P, 2 * G * E, E, d, inter, code)),),
                                   dtype=torch.uint8, device=self.dev)
+        self.side = torch.cuda.Stream(device=self.dev)  # default priority
+        self.ev_gate = torch.cuda.Event()
+        self.ev_side = torch.cuda.Event()
         self.ws_shared = None
         if shared_inter > 0:
             self.ws_shared = torch.empty((M.moelb_grouped_ffn_workspace_bytes(T, 1, 1, d, shared_inter, code),),
@@ -151,41 +159,50 @@ class MoELayer:
     def step(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None, shared_w2=None,
              stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
         """One layer step.  With ``events``, marks ev_base+0..7 bracket the
-        seven stages and ev_base+8..11 are recorded inside the grouped FFN
-        (before its schedule, gate/up GEMM and down GEMM kernels, and after)."""
+        stages of STAGES on the step's stream, ev_base+8..11 are recorded
+        inside the grouped FFN (before its schedule, gate/up GEMM and down GEMM
+        kernels, and after), ev_base+12..13 bracket the side stream's work."""
         ev = events
+        s0 = stream if stream is not None else torch.cuda.current_stream()
 
-        def mark(i):
+        def mark(i, st=None):
             if ev is not None:
-                ev.record(ev_base + i, stream)
+                ev.record(ev_base + i, st if st is not None else s0)
 
         mark(0)
-        M.moelb_gate_topk(h, w_cur, b_cur, w_next, b_next, self.idx, self.wts, self.gap, self.idx_next, stream=stream)
+        M.moelb_gate_topk(h, w_cur, b_cur, w_next, b_next, self.idx, self.wts, self.gap, self.idx_next, stream=s0)
+        self.ev_gate.record(s0)
+        # side stream: lookahead histogram and the next layer's plan
+        self.side.wait_event(self.ev_gate)
+        mark(12, self.side)
+        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=self.side)
+        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+        mark(13, self.side)
+        self.ev_side.record(self.side)
         mark(1)
-        M.moelb_histogram(self.idx, self.G, self.counts, stream=stream)
-        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
+        M.moelb_histogram(self.idx, self.G, self.counts, stream=s0)
         mark(2)
-        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=stream)
+        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes, stream=s0)
         mark(3)
-        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes, stream=stream)
-        mark(4)
         copy_rows = not self.gather_rows  # the gather GEMM reads h through perm instead
         M.moelb_permute(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
                         self.ws_perm, self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None,
-                        d=self.d, dtype=M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32, stream=stream)
-        mark(5)
+                        d=self.d, dtype=M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32, stream=s0)
+        mark(4)
         ffn_ev = ev.handles(ev_base + 8, 4) if ev is not None else None
         if self.gather_rows:
             M.moelb_grouped_ffn(h, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                gather=self.perm, gather_k=self.k, stream=stream, events=ffn_ev)
+                                gather=self.perm, gather_k=self.k, stream=s0, events=ffn_ev)
         else:
             M.moelb_grouped_ffn(self.x_perm, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                stream=stream, events=ffn_ev)
+                                stream=s0, events=ffn_ev)
         if self.shared is not None:
             M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
-                                stream=stream)
+                                stream=s0)
+        mark(5)
+        M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=s0)
         mark(6)
-        M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=stream)
+        s0.wait_event(self.ev_side)
         mark(7)
         return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
                        self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
@@ -198,4 +215,5 @@ def stage_times_ms(ev: HipEvents, base: int = 0) -> Dict[str, float]:
     t["ffn_schedule"] = ev.elapsed_ms(base + 8, base + 9)
     t["ffn_gate_up_gemm"] = ev.elapsed_ms(base + 9, base + 10)
     t["ffn_down_gemm"] = ev.elapsed_ms(base + 10, base + 11)
+    t["side_histogram_plan"] = ev.elapsed_ms(base + 12, base + 13)
     return t
