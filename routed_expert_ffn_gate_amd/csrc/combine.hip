@@ -26,11 +26,8 @@ template <> struct Vec<uint16_t> {
     }
   }
   static __device__ __forceinline__ uint4 pack(const float* f) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(bf16x2_pack(f[0], f[1]), bf16x2_pack(f[2], f[3]), bf16x2_pack(f[4], f[5]),
+                      bf16x2_pack(f[6], f[7]));
   }
 };
 template <> struct Vec<float> {

@@ -27,6 +27,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 
+// Two floats to packed bf16 (lo in bits 0..15), rounded to nearest even by the
+// hardware conversion (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_pack(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Element access for the two storage types.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -38,7 +47,9 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-__device__ __forceinline__ float silu_f32(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware exponential and reciprocal (each
+// within about one ulp); the IEEE division sequence would cost ten instructions.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- wave helpers
 

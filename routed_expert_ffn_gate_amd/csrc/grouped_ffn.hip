@@ -584,23 +584,18 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
       if (MODE == 0) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          uint32_t h[4];
+          float o[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = acc[mi][f][q * 4 + i], u = acc[mi][f + 2][q * 4 + i];
-            h[i] = f32_to_bf16(silu_f32(g) * u);
-          }
+          for (int i = 0; i < 4; ++i) o[i] = silu_f32(acc[mi][f][q * 4 + i]) * acc[mi][f + 2][q * 4 + i];
           *reinterpret_cast<uint2*>(Cs + row * CS + wn * 64 + f * 32 + q * 8 + fh * 4) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+              make_uint2(bf16x2_pack(o[0], o[1]), bf16x2_pack(o[2], o[3]));
         }
       } else {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          uint32_t h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16(acc[mi][ni][q * 4 + i]);
+          const f32x16_t& a4 = acc[mi][ni];
           *reinterpret_cast<uint2*>(Cs + row * CS + wn * 128 + ni * 32 + q * 8 + fh * 4) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+              make_uint2(bf16x2_pack(a4[q * 4], a4[q * 4 + 1]), bf16x2_pack(a4[q * 4 + 2], a4[q * 4 + 3]));
         }
       }
     }
