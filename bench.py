@@ -93,7 +93,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-tokens", type=int, default=20480)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, one plain device-to-device copy of this many bytes")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
