@@ -58,6 +58,23 @@ def algorithmic_work(cfg):
     return f, by
 
 
+def routing_stats(cfg, layer, idx_pred, home):
+    """Reported alongside the throughput, from the step's device outputs:
+    lookahead hit rate (fraction of the step's top-k assignments that the
+    lookahead routing predicted) and spatial balance sum(L)/(G max L) of the
+    per-rank loads without balancing (every pair at its expert's home) and
+    after the split."""
+    import torch
+    idx = layer.idx.long()
+    hit = (idx_pred.long()[:, :, None] == idx[:, None, :]).any(-1).sum().item() / idx.numel()
+    per_expert = layer.counts.long().sum(0)
+    static = torch.zeros(cfg.G, dtype=torch.long, device=idx.device).index_add_(0, home.long(), per_expert)
+    split = layer.load.long()
+    sp = lambda l: (l.sum() / (cfg.G * l.max().clamp(min=1))).item()  # noqa: E731
+    return {"lookahead_hit": round(hit, 4), "spatial_static": round(sp(static), 4),
+            "spatial_split": round(sp(split), 4)}
+
+
 def cpu_baseline(cfg, li, w13, w2, shared, ntok):
     """The oracle as it stands, on the first ``ntok`` tokens of the workload."""
     import numpy as np
@@ -136,6 +153,7 @@ def main():
                      shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True)
     replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
     layer.predict_plan(h_prev, wc, bc, home, replica_cur)
+    idx_pred = layer.idx_next.clone()  # the lookahead routing this step's plan was made from
     torch.cuda.synchronize()
     log(f"uploaded; workspace {layer.ws_ffn.numel() / 2**30:.2f} GiB")
 
@@ -173,6 +191,7 @@ def main():
     pe.record(1, stream)
     permute_rows_ms = pe.elapsed_ms(0, 1) / reps
 
+    balance = routing_stats(cfg, layer, idx_pred, home)
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
@@ -214,6 +233,7 @@ def main():
                      "flop_per_launch": f["ffn_gate_up_flop"], "avg_launch_ms": round(gu_ms, 4)},
         "stages_ms": {k_: round(v, 4) for k_, v in {**stage, **sub, "permute_rows": permute_rows_ms}.items()},
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
+        "routing": balance,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),

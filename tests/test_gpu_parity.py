@@ -182,6 +182,36 @@ def test_plan_and_split_random_instances(moelb):
         assert np.array_equal(ld.cpu().numpy(), ld_o)
 
 
+def test_split_heavily_replicated_home(moelb):
+    """Every rank replicates the four experts of rank 0: rank 0 ends up in one
+    transfer per replica, which takes the split past 64 edge colours (and, at
+    G=16, just below)."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(5)
+    for G in (16, 32, 64):
+        E, N = 4 * G, 8
+        home = (np.arange(E) // 4).astype(np.int32)
+        rep = np.empty((G, N), np.int32)
+        for r in range(G):
+            if r == 0:
+                rep[r] = [4 + j for j in range(4)] + [8 + j for j in range(4)]
+            else:
+                nxt = (r + 1) % G or 1  # a rank other than r and 0
+                rep[r] = [0, 1, 2, 3] + [4 * nxt + j for j in range(4)]
+        pop = np.ones(E)
+        pop[:4] = 40.0
+        c = np.stack([rng.multinomial(4000, pop / pop.sum()) for _ in range(G)]).astype(np.int32)
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split(torch.from_numpy(c).to(dev), torch.from_numpy(home).to(dev), torch.from_numpy(rep).to(dev),
+                      hc, ld, passes=12)
+        hc_o, ld_o = O.split(c, home, rep, G, E, passes=12)
+        assert np.array_equal(hc.cpu().numpy(), hc_o), G
+        assert np.array_equal(ld.cpu().numpy(), ld_o), G
+
+
 def test_empty_batch(moelb):
     from routed_expert_ffn_gate_amd import moelb as M
     dev = torch.device("cuda")
