@@ -619,6 +619,279 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
   }
 }
 
+// ---------------------------------------------------------------- persistent down GEMM
+//
+// The down GEMM (K = inter, output rows scattered through the row map) runs as
+// a persistent kernel: one workgroup per CU walks its tiles, and the K steps of
+// consecutive tiles form one stream through the same 5-slot LDS ring, so the
+// next tile's first steps load while the current tile finishes and stores.
+// The DMA offsets switch to the next tile two steps before a tile's end (from
+// then on every refill belongs to it).  The epilogue stages the output through
+// the ring slot of the tile's last B half-stage (free once its last sub-step
+// has read it; the A slot beside it already takes the next refill), in four
+// rounds of 64 rows with XOR-swizzled 16-byte chunks.  Requires inter / 64 >= 3.
+// (The gate/up GEMM keeps one workgroup per tile: its SiLU epilogue inside the
+// tile loop needs more registers than the pipeline leaves.)
+
+struct DlTile {
+  int nt, e, v0, vend;
+};
+
+// Tile j of this workgroup: XCD x = blockIdx % 8 owns the contiguous range
+// [x*per, (x+1)*per) of the grouped tile order and its workgroups take it in
+// turn, so the tiles running at once on an XCD stay neighbours in that order.
+__device__ __forceinline__ int dl_tile_id(int j, int total) {
+  const int per = (total + 7) / 8;
+  const int lo = (blockIdx.x >> 3) + j * (gridDim.x >> 3);
+  const int t = (blockIdx.x & 7) * per + lo;
+  return (lo < per && t < total) ? t : -1;
+}
+
+__device__ __forceinline__ DlTile dl_tile(int t, int n_mtiles, int ntn, const FfnSched& s) {
+  DlTile c;
+  int mt, nt;
+  grouped_tile(t, n_mtiles, ntn, mt, nt);
+  c.nt = nt;
+  c.e = s.mt_e[mt];
+  c.v0 = s.mt_v0[mt];
+  c.vend = s.eoff[c.e + 1];
+  return c;
+}
+
+// Output row held by lane l of wave w.  In store round rd, iteration i, lane l
+// of wave w stores staging row rl = 2w + (l>>5) + 8i, which is tile row
+// (rl>>5)*128 + 32*rd + (rl&31); lane l holds the row of round l>>4, half
+// (l>>3)&1, iteration l&7 (rows past the expert's end give row 0, unused).
+__device__ __forceinline__ int dl_out_row(const DlTile& c, const FfnSched& s, int rows_y, int wave, int lane) {
+  const int rl = 2 * wave + ((lane >> 3) & 1) + 8 * (lane & 7);
+  const int row = (rl >> 5) * 128 + 32 * (lane >> 4) + (rl & 31);
+  const int v = c.v0 + row;
+  return v < c.vend ? min(max(s.rowmap[v], 0), rows_y - 1) : 0;
+}
+
+__global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const uint16_t* __restrict__ w, FfnSched s,
+                                                                        int rows_y, int d, int inter, int ntn,
+                                                                        uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) char smem[];
+  const int n_mtiles = *s.n_mtiles;
+  const int total = n_mtiles * ntn;
+  int ntiles = 0;
+  while (dl_tile_id(ntiles, total) >= 0) ++ntiles;
+  if (ntiles == 0) return;
+  const int KT = inter / DL_BK;
+  const int nsteps = ntiles * KT;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint16_t* abase = static_cast<const uint16_t*>(s.amid);
+
+  // tile being stored (cur), the next one, and the DMA byte offsets of the
+  // tile being loaded: block (wave*8 + j) of 8 rows, row (lane >> 3) in it,
+  // slot (lane & 7) <- global chunk dl_slot(row, slot)
+  DlTile cur = dl_tile(dl_tile_id(0, total), n_mtiles, ntn, s);
+  DlTile nxt = ntiles > 1 ? dl_tile(dl_tile_id(1, total), n_mtiles, ntn, s) : cur;
+  const uint16_t* bbase;
+  uint32_t aoff[8], boff[8];
+#define DL_OFFSETS(C)                                                                                  \
+  {                                                                                                    \
+    bbase = w + (size_t)(C).e * d * inter;                                                             \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                    \
+      const int r = (wave * 8 + j) * 8 + (lane >> 3);                                                  \
+      const int chunk = dl_slot(r, lane & 7);                                                          \
+      int v = (C).v0 + r;                                                                              \
+      v = v < (C).vend ? v : (C).v0;                                                                   \
+      aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;                                      \
+      int col = (C).nt * 256 + r;                                                                      \
+      col = col < d ? col : 0;                                                                         \
+      boff[j] = ((uint32_t)col * (uint32_t)inter + chunk * 8) * 2u;                                    \
+    }                                                                                                  \
+  }
+  DL_OFFSETS(cur)
+  int out_row = dl_out_row(cur, s, rows_y, wave, lane);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  // DMA instruction JJ into ring slot SLOT of the A (ISB false) or B operand
+  // of a K step that is KK steps into its tile
+#define DL_COPY(SLOT, KK, ISB, JJ)                                                                     \
+  {                                                                                                    \
+    const uint16_t* base_ = ((ISB) ? bbase : abase) + (size_t)(KK) * DL_BK;                            \
+    dl_copy16((ISB) ? boff[JJ] : aoff[JJ], base_,                                                      \
+              lds_u32 + (uint32_t)(((SLOT) * DL_HALF + (wave_s * 8 + (JJ)) * 8 * DL_BK) * 2));         \
+  }
+  // LDS element offsets (inside a half-stage) of this lane's fragments: block
+  // i adds i * 32 rows (the swizzle of a row depends on row % 32 only)
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  const int fsw = ((fr >> 1) ^ (fr << 2)) & 7;
+  int aro[4], bro[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    aro[ks] = (wm * 128 + fr) * DL_BK + (((ks * 2 + fh) ^ fsw) * 8);
+    bro[ks] = (wn * 128 + fr) * DL_BK + (((ks * 2 + fh) ^ fsw) * 8);
+  }
+  bf16x8_t xa[4], xb[4], ya[4], yb[4];
+  // One k sub-step: per 32-row block mi, read the next set's fragments (from
+  // sub-step KS of half-stages SA/SB, if RD), run its 4 MFMAs on the current
+  // set (B fragment first: the accumulator holds the block transposed), then
+  // issue DMA instruction J0+mi of half-stage SLOT (if DO).
+#define DL_SUB(FA, FB, NA, NB, SA, SB, KS, RD, DO, SLOT, KK, ISB, J0)                                  \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                   \
+    if (RD) {                                                                                          \
+      NA[mi] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS] + mi * 32 * DL_BK);                   \
+      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + mi * 32 * DL_BK);                   \
+    }                                                                                                  \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ni], FA[mi], acc[mi][ni], 0, 0, 0);     \
+    if (DO) DL_COPY(SLOT, KK, ISB, (J0) + mi)                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+  }
+
+  // values loaded by the compiler's own loads are waited for here, before any
+  // DMA is in flight; scalar loads still pending would make every LDS wait in
+  // the loop a full drain
+  asm volatile("" ::"s"(y), "s"(rows_y), "s"(nxt.e), "s"(nxt.v0), "s"(nxt.vend), "s"(nxt.nt), "s"(cur.v0),
+               "s"(cur.vend), "s"(cur.nt));
+  asm volatile("" ::"v"(out_row));
+  const int nh = 2 * nsteps;
+  for (int j = 0; j < DL_SLOTS && j < nh; ++j)  // steps 0..2 of the first tile (K/64 >= 3)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) DL_COPY(j, j >> 1, j & 1, jj)
+  {
+    // 8 instructions per half-stage and wave: wait for A_0 and B_0 only
+    const int after = min(DL_SLOTS, nh) - 2;
+    if (after >= 3)
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (after == 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + aro[0] + i * 32 * DL_BK);
+    xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0] + i * 32 * DL_BK);
+  }
+  int g = 0;  // step of the whole stream; half-stages 2g (A) and 2g+1 (B)
+  for (int jcur = 0; jcur < ntiles; ++jcur) {
+    for (int kt = 0; kt < KT; ++kt, ++g) {
+      // ring slots of half-stages 2g .. 2g+4, places of steps g+1, g+2 in their tiles
+      const int s0 = (2 * g) % DL_SLOTS;
+      const int s1 = s0 + 1 < DL_SLOTS ? s0 + 1 : s0 + 1 - DL_SLOTS;
+      const int s2 = s1 + 1 < DL_SLOTS ? s1 + 1 : s1 + 1 - DL_SLOTS;
+      const int s3 = s2 + 1 < DL_SLOTS ? s2 + 1 : s2 + 1 - DL_SLOTS;
+      const int s4 = s3 + 1 < DL_SLOTS ? s3 + 1 : s3 + 1 - DL_SLOTS;
+      const int k1 = kt + 1 < KT ? kt + 1 : kt + 1 - KT;
+      const int k2 = kt + 2 < KT ? kt + 2 : kt + 2 - KT;
+      // slot offsets opaque to the compiler: it would otherwise precompute the
+      // fragment addresses of every slot and hold them all in registers
+      int o0 = s0 * DL_HALF, o1 = s1 * DL_HALF, o2 = s2 * DL_HALF, o3 = s3 * DL_HALF;
+      asm volatile("" : "+s"(o0), "+s"(o1), "+s"(o2), "+s"(o3));
+      const uint16_t* sa = lds + o0;
+      const uint16_t* sb = lds + o1;
+      const bool b1 = g >= 1 && g + 1 < nsteps;  // second half of B_g+1
+      const bool a2 = g >= 1 && g + 2 < nsteps;  // A_g+2
+      DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, b1, s3, k1, true, 4)
+      if (kt == KT - 2 && jcur + 1 < ntiles) {
+        // from here on, refills load the next tile
+        DL_OFFSETS(nxt)
+      }
+      DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, a2, s4, k2, false, 0)
+      DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, a2, s4, k2, false, 4)
+      const bool more = g + 1 < nsteps;
+      if (more) {
+        // A_g+2 is the only half-stage issued after B_g+1; lgkmcnt(0): this
+        // wave's reads of step g have landed before any wave refills its slots
+        if (g + 2 < nsteps)
+          asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      const bool tile_end = kt == KT - 1;
+      // last sub-step: read step g+1's first fragments (not at a tile's end:
+      // they are read after the epilogue) and refill A_g's slot s0 with the
+      // first half of B_g+2
+      const uint16_t* na = lds + o2;
+      const uint16_t* nbs = lds + o3;
+      DL_SUB(ya, yb, xa, xb, na, nbs, 0, more && !tile_end, g + 2 < nsteps, s0, k2, true, 0)
+    }
+    // ---- epilogue of tile jcur, staged through the slot of its last B
+    // half-stage, 32 KiB per round
+    const int gl = g - 1;
+    uint16_t* Cs = lds + ((2 * gl + 1) % DL_SLOTS) * DL_HALF;
+    __syncthreads();
+    const bool has_nn = jcur + 2 < ntiles;
+    const DlTile nn = has_nn ? dl_tile(dl_tile_id(jcur + 2, total), n_mtiles, ntn, s) : nxt;
+    const int next_out_row = jcur + 1 < ntiles ? dl_out_row(nxt, s, rows_y, wave, lane) : 0;
+    asm volatile("" ::"s"(nn.e), "s"(nn.v0), "s"(nn.vend), "s"(nn.nt));
+    const int n0 = cur.nt * 256;
+    // four rounds; in round rd every wave stages its block mi = rd: staging
+    // row wm*32 + fr (512 B, chunk c at c ^ (row & 15))
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd) {
+      const int r = wm * 32 + fr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const f32x16_t& a4 = acc[rd][ni];
+          const int chunk = wn * 16 + ni * 4 + q;
+          *reinterpret_cast<uint2*>(Cs + r * 256 + ((chunk ^ (r & 15)) * 8) + fh * 4) =
+              make_uint2(bf16x2_pack(a4[q * 4], a4[q * 4 + 1]), bf16x2_pack(a4[q * 4 + 2], a4[q * 4 + 3]));
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = tid + MF_THREADS * i;
+        const int rl = c >> 5, ch = c & 31;  // rl = 2*wave + (lane >> 5) + 8*i
+        const int v = cur.v0 + (rl >> 5) * 128 + rd * 32 + (rl & 31);
+        const int col = n0 + ch * 8;
+        const int orow = __shfl(out_row, rd * 16 + (lane >> 5) * 8 + i, 64);
+        const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 256 + ((ch ^ (rl & 15)) * 8));
+        if (v < cur.vend && col < d) *reinterpret_cast<uint4*>(y + (size_t)orow * d + col) = val;
+      }
+      __syncthreads();
+    }
+    cur = nxt;
+    nxt = nn;
+    out_row = next_out_row;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    // first fragments of the next tile (its first step landed before the epilogue)
+    if (gl + 1 < nsteps) {
+      const uint16_t* na = lds + ((2 * gl + 2) % DL_SLOTS) * DL_HALF;
+      const uint16_t* nbs = lds + ((2 * gl + 3) % DL_SLOTS) * DL_HALF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = *reinterpret_cast<const bf16x8_t*>(na + aro[0] + i * 32 * DL_BK);
+        xb[i] = *reinterpret_cast<const bf16x8_t*>(nbs + bro[0] + i * 32 * DL_BK);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef DL_COPY
+#undef DL_SUB
+#undef DL_OFFSETS
+}
+
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
 template <int MODE>
@@ -717,6 +990,15 @@ __global__ __launch_bounds__(256) void ffn_simt_kernel(const float* __restrict__
 
 }  // namespace
 
+// One workgroup per compute unit (a multiple of the 8 XCDs).
+static int persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  return cus & ~7;
+}
+
 extern "C" size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, int E, int d, int inter, int dtype) {
   (void)d;
   if (rows < 0 || num_groups < 1 || E < 1 || inter < 1 || !moelb_dtype_ok(dtype)) return 0;
@@ -765,8 +1047,10 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
     const int ntn1 = (d + 255) / 256;
     // direct-to-LDS pipeline when K is a multiple of its 64-wide step
     const bool dma0 = d % DL_BK == 0, dma1 = inter % DL_BK == 0;  // else the register-staged kernel
+    const bool pers1 = dma1 && inter / DL_BK >= 3;                  // persistent down GEMM
     if ((dma0 && !moelb_allow_lds(ffn_mfma_dma_kernel<0>, DL_LDS_BYTES)) ||
-        (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)))
+        (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)) ||
+        (pers1 && !moelb_allow_lds(ffn_down_persistent_kernel, DL_LDS_BYTES)))
       return MOELB_ELAUNCH;
     rec(1);
     if (dma0)
@@ -779,7 +1063,10 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
                          sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
     MOELB_CHECK_LAUNCH();
     rec(2);
-    if (dma1)
+    if (pers1)
+      hipLaunchKernelGGL(ffn_down_persistent_kernel, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1, static_cast<uint16_t*>(y));
+    else if (dma1)
       hipLaunchKernelGGL(ffn_mfma_dma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
                          static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
                          d, inter, ntn1, static_cast<uint16_t*>(y));
