@@ -8,6 +8,7 @@ Compiles every ``csrc/*.hip`` with hipcc for gfx950 and links them into
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -50,6 +51,37 @@ def _check_kernel_stubs(lib_path: str) -> None:
         raise RuntimeError(f"{lib_path}: kernels without a host stub: {missing[:4]}")
 
 
+_M0_WRITE = re.compile(r"^\s*s_mov_b32\s+m0,\s*s\d+\s*$")
+
+
+def m0_violations(asm_lines) -> list:
+    """Lines of device assembly that use M0 other than as the LDS DMA helpers
+    do (s_mov_b32 m0, sN; s_nop 0; global_load_lds_dwordx4)."""
+    lines = [l.split(";")[0].strip() for l in asm_lines]
+    lines = [l for l in lines if l]
+    bad = []
+    for i, l in enumerate(lines):
+        if not re.search(r"\bm0\b", l):
+            continue
+        ok = (_M0_WRITE.match(l) and i + 2 < len(lines) and lines[i + 1] == "s_nop 0"
+              and lines[i + 2].startswith("global_load_lds_dwordx4"))
+        if not ok:
+            bad.append(l)
+    return bad
+
+
+def _check_m0(src: str) -> None:
+    """The LDS DMA helpers set M0 in inline asm and list it as clobbered; the
+    compiler does not preserve a reserved register across such asm, so the
+    build requires that no compiler code relies on M0."""
+    asm = os.path.join(BUILD, os.path.basename(src)[:-4] + ".device.s")
+    _run([HIPCC, *FLAGS, "--cuda-device-only", "-S", src, "-o", asm])
+    with open(asm) as fh:
+        bad = m0_violations(fh)
+    if bad:
+        raise RuntimeError(f"{src}: M0 used outside the LDS DMA helpers: {bad[:4]}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -63,6 +95,8 @@ def build(verbose: bool = False) -> str:
         for out in ex.map(one, zip(srcs, objs)):
             if verbose and out.strip():
                 print(out)
+    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+        list(ex.map(_check_m0, [src for src in srcs if "m0" in open(src).read()]))
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     _check_kernel_stubs(tmp)

@@ -259,10 +259,15 @@ __device__ __forceinline__ int gt_slot(int row, int chunk) { return chunk ^ (((r
 // sbase, lane i lands at LDS byte address m0 + 16 i.  Issued from inline asm so
 // the compiler's LDS wait tracking stays exact; completion is tracked by the
 // caller's explicit vmcnt waits.
+// M0 is a reserved register, so the compiler warns that it does not preserve
+// it across this asm; the build checks that no compiler code uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void gt_copy16(uint32_t voff, const void* sbase, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int NF, int KL, int S>
 __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(

@@ -402,10 +402,15 @@ __device__ __forceinline__ int dl_slot(int row, int chunk) { return chunk ^ (((r
 
 // 16 bytes per lane, global -> LDS: byte offset voff from the wave-uniform
 // base sbase; lane i lands at LDS byte address m0 + 16 i.
+// M0 is a reserved register, so the compiler warns that it does not preserve
+// it across this asm; the build checks that no compiler code uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dl_copy16(uint32_t voff, const void* sbase, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int MODE>
 __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t* __restrict__ x, int rows_x,

@@ -77,3 +77,13 @@ def test_workspace_sizes_monotone(lib):
     b = lib.moelb_grouped_ffn_workspace_bytes(2048, 64, 8, 256, 512, 1)
     assert 0 < a < b
     assert lib.moelb_grouped_ffn_workspace_bytes(2048, 64, 8, 256, 512, 0) > b   # fp32 activations
+
+
+def test_m0_check_accepts_only_the_dma_pattern():
+    from routed_expert_ffn_gate_amd.build import m0_violations
+    good = ["\ts_mov_b32 m0, s12", "\ts_nop 0", "\tglobal_load_lds_dwordx4 v46, s[2:3]", "\tv_add_u32 v1, v2, v3"]
+    assert m0_violations(good) == []
+    # the compiler indexing registers through M0, or writing it for its own use
+    assert m0_violations(["\ts_mov_b32 m0, s4", "\tv_movrels_b32_e32 v1, v2"]) != []
+    assert m0_violations(["\ts_add_i32 m0, s4, 16", "\ts_nop 0", "\tglobal_load_lds_dwordx4 v1, s[2:3]"]) != []
+    assert m0_violations(["\ts_mov_b32 m0, s12 ; comment", "\ts_nop 0", "\tglobal_load_lds_dwordx4 v4, s[6:7]"]) == []
