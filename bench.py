@@ -104,6 +104,33 @@ def cpu_baseline(cfg, li, w13, w2, shared, ntok):
             "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, whole layer step (fp64), {dt:.1f} s"}
 
 
+def time_two_stage(layer, args, K, stream, T):
+    """The same step with MoE_local beside the split and the remote
+    permutation: step time, its stages, and how much of the split stream's
+    work stayed hidden under the local FFN."""
+    import torch
+    from routed_expert_ffn_gate_amd.layer import EVENTS_PER_STEP, TWO_STAGE_MARKS, HipEvents
+    for _ in range(2):
+        layer.step_two_stage(*args)
+    torch.cuda.synchronize()
+    EPS = EVENTS_PER_STEP
+    ev = HipEvents(EPS * K + 2)
+    ev.record(EPS * K, stream)
+    for i in range(K):
+        layer.step_two_stage(*args, events=ev, ev_base=EPS * i)
+    ev.record(EPS * K + 1, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(EPS * K, EPS * K + 1) / K
+    st = {n: sum(ev.elapsed_ms(EPS * i + a, EPS * i + b) for i in range(K)) / K
+          for n, (a, b) in TWO_STAGE_MARKS.items()}
+    ev.close()
+    side = st["split"] + st["permute_remote"]
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "stages_ms": {n: round(v, 4) for n, v in st.items()},
+            "side_work_ms": round(side, 4), "exposed_ms": round(st["wait_remote"], 4),
+            "hidden_ms": round(max(0.0, side - st["wait_remote"]), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +219,7 @@ def main():
     permute_rows_ms = pe.elapsed_ms(0, 1) / reps
 
     balance = routing_stats(cfg, layer, idx_pred, home)
+    two_stage = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K, stream, cfg.T)
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
@@ -234,6 +262,7 @@ def main():
         "stages_ms": {k_: round(v, 4) for k_, v in {**stage, **sub, "permute_rows": permute_rows_ms}.items()},
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
         "routing": balance,
+        "two_stage": two_stage,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),

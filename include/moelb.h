@@ -184,6 +184,33 @@ int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E,
                   void* stream);
 
 /*
+ * The same permutation in two phases (Libra README "Key Ideas": MoE_local
+ * starts right after gating; the token sharding of the remote pairs runs
+ * beside it).  Calling moelb_permute_local and then moelb_permute_remote with
+ * the same arguments and the same workspace (untouched in between) gives
+ * exactly moelb_permute's outputs.
+ *  moelb_permute_local needs no host_count: it writes group_off[0..G*E]
+ *  (the local groups; group_off[G*E] = number of local pairs), the perm
+ *  entries below group_off[G*E], pos of every local pair, pos = -1 for remote
+ *  pairs, and the local rows of x_perm (if given).  The local groups can be
+ *  computed from this point on (moelb_grouped_ffn over the first G*E groups).
+ *  moelb_permute_remote takes host_count (from moelb_split) and writes
+ *  group_off[G*E+1..2*G*E], the remaining perm entries, pos of the remote
+ *  pairs and their x_perm rows.  Its workspace must hold the local phase's
+ *  state for the same idx, home and replica.
+ * Same requirements and errors as moelb_permute.
+ */
+int moelb_permute_local(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                        int dtype, const int32_t* home, const int32_t* replica, void* ws,
+                        size_t ws_bytes, int32_t* group_off, int32_t* perm, int32_t* pos,
+                        void* x_perm, void* stream);
+int moelb_permute_remote(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                         int dtype, const int32_t* home, const int32_t* replica,
+                         const int32_t* host_count, void* ws, size_t ws_bytes,
+                         int32_t* group_off, int32_t* perm, int32_t* pos, void* x_perm,
+                         void* stream);
+
+/*
  * Masked grouped SwiGLU expert FFN (Libra README "Repository Layout": FusedMoE
  * over masked tokens; FreeBalance section 2.1: expert_i(h)).
  *  Group g covers rows [group_off[g], group_off[g+1]) and uses expert g mod E

@@ -17,6 +17,14 @@
 //      equal experts inside a step from popcount below the lane) and writes
 //      pos/perm; then all waves copy each token's row once into its k
 //      destinations (read once, written k times).
+//
+// Two-phase form (the two stages run apart, so MoE_local can start before
+// the split exists): the local phase does all of the above except what
+// depends on host_count -- it places the local pairs and keeps each remote
+// pair's place rho in its expert's remote pool; the remote phase turns
+// host_count into host ranges and remote group offsets (after the local
+// total) and places the remote pairs.  Both phases together give exactly the
+// one-call result.
 #include "common.h"
 
 namespace {
@@ -31,6 +39,8 @@ struct PermuteWs {
   int32_t* host_lo;       // [E][G]  first remote rank (rho) served by that host
   int32_t* host_hi;       // [E][G]  one past the last
   int32_t* gsize;         // [2GE]
+  int32_t* remote_total;  // [E]    size of each expert's remote pool
+  int32_t* rho;           // [T*k]  two-phase form: remote pair's place in its pool, -1 otherwise
 };
 
 inline size_t ws_layout(int T, int k, int E, int G, PermuteWs* w, char* base) {
@@ -50,7 +60,8 @@ inline size_t ws_layout(int T, int k, int E, int G, PermuteWs* w, char* base) {
   take(&t->host_lo, (size_t)E * G);
   take(&t->host_hi, (size_t)E * G);
   take(&t->gsize, (size_t)2 * G * E);
-  (void)k;
+  take(&t->remote_total, (size_t)E);
+  take(&t->rho, (size_t)T * k);
   return off;
 }
 
@@ -81,6 +92,33 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(size_t)c * E + e] = bins[e];
+}
+
+// Expert e's remote pool (R pairs, in pair-id order) over its hosts in
+// ascending rank: host i serves places [host_lo, host_hi) -- host_count[e,h]
+// pairs each (negative read as 0), the highest host also the rest; the sizes
+// of the remote groups follow.
+__device__ void remote_ranges(int e, uint64_t mask, int R, const int32_t* __restrict__ host_count, int E, int G,
+                              PermuteWs ws) {
+  const int m = __popcll(mask);
+  int cum = 0, i = 0;
+  for (int h = 0; h < G; ++h) {
+    int size = 0;
+    if ((mask >> h) & 1ull) {
+      const int hc = max(host_count[(size_t)e * G + h], 0);
+      const int lo = min(cum, R);
+      cum = (cum > R - hc) ? R + 1 : cum + hc;  // saturating: stays > R once past it
+      int hi = min(cum, R);
+      if (i == m - 1) hi = R;                    // the highest host takes the rest
+      size = hi - lo;
+      ws.host_rank[(size_t)e * G + i] = h;
+      ws.host_lo[(size_t)e * G + i] = lo;
+      ws.host_hi[(size_t)e * G + i] = hi;
+      ++i;
+    }
+    ws.gsize[(size_t)(1 * G + h) * E + e] = size;
+  }
+  for (; i < G; ++i) ws.host_rank[(size_t)e * G + i] = -1;
 }
 
 // One workgroup per expert: a block scan over the chunks (token order) of the
@@ -155,32 +193,27 @@ __global__ __launch_bounds__(ESCAN_THREADS) void expert_scan_kernel(const int32_
     ws.gsize[(size_t)(0 * G + s) * E + e] = size;
   }
   if (tid == 0) {
-    // remote pool over the hosts in ascending rank
-    const int m = __popcll(mask);
-    int cum = 0, i = 0;
-    for (int h = 0; h < G; ++h) {
-      int size = 0;
-      if ((mask >> h) & 1ull) {
-        const int hc = max(host_count[(size_t)e * G + h], 0);
-        const int lo = min(cum, R);
-        cum = (cum > R - hc) ? R + 1 : cum + hc;  // saturating: stays > R once past it
-        int hi = min(cum, R);
-        if (i == m - 1) hi = R;                    // the highest host takes the rest
-        size = hi - lo;
-        ws.host_rank[(size_t)e * G + i] = h;
-        ws.host_lo[(size_t)e * G + i] = lo;
-        ws.host_hi[(size_t)e * G + i] = hi;
-        ++i;
-      }
-      ws.gsize[(size_t)(1 * G + h) * E + e] = size;
-    }
-    for (; i < G; ++i) ws.host_rank[(size_t)e * G + i] = -1;
+    ws.remote_total[e] = R;
+    if (host_count) remote_ranges(e, mask, R, host_count, E, G, ws);
   }
 }
 
+// Remote phase: host ranges of every expert (thread e).
+__global__ __launch_bounds__(256) void remote_ranges_kernel(const int32_t* __restrict__ home,
+                                                            const int32_t* __restrict__ replica,
+                                                            const int32_t* __restrict__ host_count, int E, int G,
+                                                            int N, PermuteWs ws) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  remote_ranges(e, host_mask(home, replica, G, N, e), ws.remote_total[e], host_count, E, G, ws);
+}
+
 // Exclusive scan of the 2GE group sizes into group_off (one workgroup).
+// With `base`, offsets start at *base (the remote groups after the local
+// total, which is group_off[G*E] itself: every thread reads the same value
+// that the first write stores back).
 __global__ __launch_bounds__(SCAN_THREADS) void group_scan_kernel(const int32_t* __restrict__ gsize, int ngroups,
-                                                                  int32_t* __restrict__ group_off) {
+                                                                  const int32_t* base, int32_t* group_off) {
   __shared__ int part[SCAN_THREADS];
   const int tid = threadIdx.x;
   const int seg = (ngroups + SCAN_THREADS - 1) / SCAN_THREADS;
@@ -195,15 +228,19 @@ __global__ __launch_bounds__(SCAN_THREADS) void group_scan_kernel(const int32_t*
     part[tid] += v;
     __syncthreads();
   }
-  int run = part[tid] - sum;
+  const int b = base ? *base : 0;
+  int run = b + part[tid] - sum;
   for (int g = b0; g < b1; ++g) {
     group_off[g] = run;
     run += gsize[g];
   }
-  if (tid == SCAN_THREADS - 1) group_off[ngroups] = part[tid];
+  if (tid == SCAN_THREADS - 1) group_off[ngroups] = b + part[tid];
 }
 
-template <typename T>
+// LOCAL_ONLY (local phase of the two-phase form): remote pairs get pos -1 and
+// their place rho in ws.rho (every other pair -1 there); no perm entry or row
+// copy for them yet.
+template <typename T, bool LOCAL_ONLY>
 __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__ h, const int32_t* __restrict__ idx,
                                                            int Ttok, int d, int k, int E, int G, int N, int nchr,
                                                            const int32_t* __restrict__ home,
@@ -247,12 +284,15 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
         remaining &= ~m;
       }
       int q = -1;
+      int rho = -1;
       if (valid) {
         rank += ws.chunk_base[(size_t)c * E + e];
         const uint64_t mask = hmask[e];
-        int key;
+        int key = -1;
         if ((mask >> s) & 1ull) {
           key = (0 * G + s) * E + e;
+        } else if (LOCAL_ONLY) {
+          rho = rank;
         } else {
           // rank is rho, this pair's place in e's remote pool
           int i = 0;
@@ -261,12 +301,15 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
           rank -= ws.host_lo[(size_t)e * G + i];
           key = (1 * G + hst) * E + e;
         }
-        q = group_off[key] + rank;
-        perm[q] = static_cast<int32_t>(pid);
+        if (key >= 0) {
+          q = group_off[key] + rank;
+          perm[q] = static_cast<int32_t>(pid);
+        }
       }
       if (inr) {
         pos[pid] = q;
         qpos[pl] = q;
+        if (LOCAL_ONLY) ws.rho[pid] = rho;
       }
     }
   }
@@ -286,6 +329,48 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
   }
 }
 
+// Remote phase: one thread per pair places the remote pairs (rho >= 0) with
+// the host ranges; then the workgroup copies their rows (16-byte chunks).
+constexpr int RS_THREADS = 256;
+
+template <typename T>
+__global__ __launch_bounds__(RS_THREADS) void remote_scatter_kernel(const T* __restrict__ h,
+                                                                    const int32_t* __restrict__ idx, int P, int d,
+                                                                    int k, int E, int G, PermuteWs ws,
+                                                                    const int32_t* __restrict__ group_off,
+                                                                    int32_t* __restrict__ perm,
+                                                                    int32_t* __restrict__ pos, T* __restrict__ x_perm) {
+  __shared__ int qs[RS_THREADS];
+  __shared__ int any;
+  const int pid = blockIdx.x * RS_THREADS + threadIdx.x;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  int q = -1;
+  const int rho = pid < P ? ws.rho[pid] : -1;
+  if (rho >= 0) {
+    const int e = idx[pid];  // valid: the local phase kept rho only for valid pairs
+    int i = 0;
+    while (i + 1 < G && ws.host_rank[(size_t)e * G + i + 1] >= 0 && rho >= ws.host_hi[(size_t)e * G + i]) ++i;
+    const int hst = ws.host_rank[(size_t)e * G + i];
+    q = group_off[(1 * G + hst) * E + e] + rho - ws.host_lo[(size_t)e * G + i];
+    perm[q] = pid;
+    pos[pid] = q;
+    any = 1;
+  }
+  qs[threadIdx.x] = q;
+  __syncthreads();
+  if (x_perm == nullptr || !any) return;
+  const int nvec = d * (int)sizeof(T) / 16;
+  for (int i = 0; i < RS_THREADS; ++i) {
+    const int qi = qs[i];
+    if (qi < 0) continue;
+    const int p = blockIdx.x * RS_THREADS + i;
+    const uint4* src = reinterpret_cast<const uint4*>(h + (size_t)(p / k) * d);
+    uint4* dst = reinterpret_cast<uint4*>(x_perm + (size_t)qi * d);
+    for (int v = threadIdx.x; v < nvec; v += RS_THREADS) dst[v] = src[v];
+  }
+}
+
 }  // namespace
 
 extern "C" size_t moelb_permute_workspace_bytes(int T, int k, int E, int G) {
@@ -293,42 +378,103 @@ extern "C" size_t moelb_permute_workspace_bytes(int T, int k, int E, int G) {
   return ws_layout(T, k, E, G, nullptr, nullptr);
 }
 
-extern "C" int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
-                             const int32_t* home, const int32_t* replica, const int32_t* host_count, void* ws,
-                             size_t ws_bytes, int32_t* group_off, int32_t* perm, int32_t* pos, void* x_perm,
-                             void* stream) {
+static int permute_check(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
+                         const int32_t* home, const int32_t* replica, void* ws, size_t ws_bytes,
+                         const int32_t* group_off, const int32_t* perm, const int32_t* pos, const void* x_perm) {
   if (T < 0 || d <= 0 || d % 8 != 0 || k < 1 || k > MOELB_MAX_K || E < 1 || E > MOELB_MAX_E || G < 1 ||
       G > MOELB_MAX_G || N < 0 || N > MOELB_MAX_N || T % G != 0 || !moelb_dtype_ok(dtype))
     return MOELB_EINVAL;
-  if (!home || (N > 0 && !replica) || !host_count || !group_off || (T > 0 && (!idx || !perm || !pos)))
-    return MOELB_EINVAL;
+  if (!home || (N > 0 && !replica) || !group_off || (T > 0 && (!idx || !perm || !pos))) return MOELB_EINVAL;
   if (x_perm && !h) return MOELB_EINVAL;
   if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(x_perm)) & 15) return MOELB_EINVAL;
   if ((size_t)T * k > 0x7fffffffull) return MOELB_EINVAL;
   const size_t need = ws_layout(T, k, E, G, nullptr, nullptr);
   if (!ws || ws_bytes < need) return MOELB_EWORKSPACE;
+  return MOELB_OK;
+}
+
+// count, expert scan, group scan (all groups, or the local ones), rank+scatter
+static int permute_launch(bool local_only, const void* h, const int32_t* idx, int T, int d, int k, int E, int G,
+                          int N, int dtype, const int32_t* home, const int32_t* replica,
+                          const int32_t* host_count, void* ws, int32_t* group_off, int32_t* perm, int32_t* pos,
+                          void* x_perm, hipStream_t s) {
   PermuteWs w;
   ws_layout(T, k, E, G, &w, static_cast<char*>(ws));
   const int per = T / G;
   const int nchr = per > 0 ? (per + CHUNK - 1) / CHUNK : 1;
   const int nchunks = G * nchr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t* rep = N > 0 ? replica : home;
   hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(256), 0, s, idx, T, k, E, G, nchr, w.chunk_counts);
   MOELB_CHECK_LAUNCH();
-  hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(ESCAN_THREADS), 0, s, home, rep, host_count, E, G, N, nchr,
-                     w);
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(ESCAN_THREADS), 0, s, home, rep,
+                     local_only ? nullptr : host_count, E, G, N, nchr, w);
   MOELB_CHECK_LAUNCH();
-  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, w.gsize, 2 * G * E, group_off);
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, w.gsize, (local_only ? 1 : 2) * G * E,
+                     nullptr, group_off);
   MOELB_CHECK_LAUNCH();
+#define PERMUTE_SCATTER(TY, LO)                                                                                  \
+  hipLaunchKernelGGL((rank_scatter_kernel<TY, LO>), dim3(nchunks), dim3(256), 0, s, static_cast<const TY*>(h), \
+                     idx, T, d, k, E, G, N, nchr, home, rep, w, group_off, perm, pos, static_cast<TY*>(x_perm))
   if (dtype == MOELB_BF16) {
-    hipLaunchKernelGGL(rank_scatter_kernel<uint16_t>, dim3(nchunks), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(h), idx, T, d, k, E, G, N, nchr, home, rep, w, group_off, perm,
-                       pos, static_cast<uint16_t*>(x_perm));
+    if (local_only) PERMUTE_SCATTER(uint16_t, true); else PERMUTE_SCATTER(uint16_t, false);
   } else {
-    hipLaunchKernelGGL(rank_scatter_kernel<float>, dim3(nchunks), dim3(256), 0, s, static_cast<const float*>(h), idx,
-                       T, d, k, E, G, N, nchr, home, rep, w, group_off, perm, pos, static_cast<float*>(x_perm));
+    if (local_only) PERMUTE_SCATTER(float, true); else PERMUTE_SCATTER(float, false);
   }
+#undef PERMUTE_SCATTER
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+extern "C" int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
+                             const int32_t* home, const int32_t* replica, const int32_t* host_count, void* ws,
+                             size_t ws_bytes, int32_t* group_off, int32_t* perm, int32_t* pos, void* x_perm,
+                             void* stream) {
+  const int st = permute_check(h, idx, T, d, k, E, G, N, dtype, home, replica, ws, ws_bytes, group_off, perm, pos,
+                               x_perm);
+  if (st != MOELB_OK) return st;
+  if (!host_count) return MOELB_EINVAL;
+  return permute_launch(false, h, idx, T, d, k, E, G, N, dtype, home, replica, host_count, ws, group_off, perm, pos,
+                        x_perm, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int moelb_permute_local(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                                   int dtype, const int32_t* home, const int32_t* replica, void* ws,
+                                   size_t ws_bytes, int32_t* group_off, int32_t* perm, int32_t* pos, void* x_perm,
+                                   void* stream) {
+  const int st = permute_check(h, idx, T, d, k, E, G, N, dtype, home, replica, ws, ws_bytes, group_off, perm, pos,
+                               x_perm);
+  if (st != MOELB_OK) return st;
+  return permute_launch(true, h, idx, T, d, k, E, G, N, dtype, home, replica, nullptr, ws, group_off, perm, pos,
+                        x_perm, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int moelb_permute_remote(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                                    int dtype, const int32_t* home, const int32_t* replica,
+                                    const int32_t* host_count, void* ws, size_t ws_bytes, int32_t* group_off,
+                                    int32_t* perm, int32_t* pos, void* x_perm, void* stream) {
+  const int st = permute_check(h, idx, T, d, k, E, G, N, dtype, home, replica, ws, ws_bytes, group_off, perm, pos,
+                               x_perm);
+  if (st != MOELB_OK) return st;
+  if (!host_count) return MOELB_EINVAL;
+  PermuteWs w;
+  ws_layout(T, k, E, G, &w, static_cast<char*>(ws));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* rep = N > 0 ? replica : home;
+  hipLaunchKernelGGL(remote_ranges_kernel, dim3((E + 255) / 256), dim3(256), 0, s, home, rep, host_count, E, G, N, w);
+  MOELB_CHECK_LAUNCH();
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, w.gsize + (size_t)G * E, G * E,
+                     group_off + (size_t)G * E, group_off + (size_t)G * E);
+  MOELB_CHECK_LAUNCH();
+  const int P = T * k;
+  if (P == 0) return MOELB_OK;
+  const int nb = (P + RS_THREADS - 1) / RS_THREADS;
+  if (dtype == MOELB_BF16)
+    hipLaunchKernelGGL(remote_scatter_kernel<uint16_t>, dim3(nb), dim3(RS_THREADS), 0, s,
+                       static_cast<const uint16_t*>(h), idx, P, d, k, E, G, w, group_off, perm, pos,
+                       static_cast<uint16_t*>(x_perm));
+  else
+    hipLaunchKernelGGL(remote_scatter_kernel<float>, dim3(nb), dim3(RS_THREADS), 0, s, static_cast<const float*>(h),
+                       idx, P, d, k, E, G, w, group_off, perm, pos, static_cast<float*>(x_perm));
   MOELB_CHECK_LAUNCH();
   return MOELB_OK;
 }

@@ -7,7 +7,9 @@ runs in the HIP library:
   plan made one step earlier) -> permute -> grouped SwiGLU FFN (+ shared
   expert) -> combine,
   and, on a side stream after the gate, the lookahead histogram and the plan
-  for the next layer, joined before the step ends
+  for the next layer, joined before the step ends.  ``step_two_stage`` runs
+  the same step with MoE_local (local permutation and FFN over the local
+  groups) beside the split and the remote permutation.
 
 The hidden-state rows are read by the gate/up GEMM straight from ``h``
 through the permutation (``gather_rows=True``, the default; the permutation
@@ -142,6 +144,11 @@ class MoELayer:
         self.side = torch.cuda.Stream(device=self.dev)  # default priority
         self.ev_gate = torch.cuda.Event()
         self.ev_side = torch.cuda.Event()
+        # two-stage schedule: split and remote permutation beside MoE_local
+        self.side2 = torch.cuda.Stream(device=self.dev)  # default priority
+        self.ev_hist = torch.cuda.Event()
+        self.ev_local = torch.cuda.Event()
+        self.ev_remote = torch.cuda.Event()
         self.ws_shared = None
         if shared_inter > 0:
             self.ws_shared = torch.empty((M.moelb_grouped_ffn_workspace_bytes(T, 1, 1, d, shared_inter, code),),
@@ -207,6 +214,90 @@ class MoELayer:
         return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
                        self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
                        self.x_perm, self.y, self.shared, self.out)
+
+
+    def step_two_stage(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None,
+                       shared_w2=None, stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
+        """The same layer step in two stages (Libra README "Key Ideas":
+        MoE_local starts right after gating, the token sharding runs beside
+        it).  After the histogram, the step's stream places the local pairs
+        and runs the grouped FFN over the local groups while a second stream
+        runs the split and places the remote pairs; the remote groups follow.
+        Outputs are identical to ``step``'s.  Event marks (TWO_STAGE_MARKS):
+        ev_base+0..8 on the step's stream, +9..11 on the split stream, +12..13
+        on the lookahead stream."""
+        ev = events
+        s0 = stream if stream is not None else torch.cuda.current_stream()
+        GE = self.G * self.E
+        code = M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32
+        copy_rows = not self.gather_rows
+
+        def mark(i, st=None):
+            if ev is not None:
+                ev.record(ev_base + i, st if st is not None else s0)
+
+        def ffn(off):
+            if self.gather_rows:
+                M.moelb_grouped_ffn(h, self.P, off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
+                                    gather=self.perm, gather_k=self.k, stream=s0)
+            else:
+                M.moelb_grouped_ffn(self.x_perm, self.P, off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
+                                    stream=s0)
+
+        mark(0)
+        M.moelb_gate_topk(h, w_cur, b_cur, w_next, b_next, self.idx, self.wts, self.gap, self.idx_next, stream=s0)
+        self.ev_gate.record(s0)
+        self.side.wait_event(self.ev_gate)
+        mark(12, self.side)
+        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=self.side)
+        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+        mark(13, self.side)
+        self.ev_side.record(self.side)
+        mark(1)
+        M.moelb_histogram(self.idx, self.G, self.counts, stream=s0)
+        self.ev_hist.record(s0)
+        mark(2)
+        # split stream: the split needs only the counts
+        self.side2.wait_event(self.ev_hist)
+        mark(9, self.side2)
+        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes,
+                      stream=self.side2)
+        mark(10, self.side2)
+        M.moelb_permute_local(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.ws_perm,
+                              self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None, d=self.d,
+                              dtype=code, stream=s0)
+        self.ev_local.record(s0)
+        mark(3)
+        self.side2.wait_event(self.ev_local)
+        M.moelb_permute_remote(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
+                               self.ws_perm, self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None,
+                               d=self.d, dtype=code, stream=self.side2)
+        mark(11, self.side2)
+        self.ev_remote.record(self.side2)
+        ffn(self.group_off[:GE + 1])  # MoE_local
+        mark(4)
+        s0.wait_event(self.ev_remote)
+        mark(5)
+        ffn(self.group_off[GE:])  # MoE_remote
+        if self.shared is not None:
+            M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
+                                stream=s0)
+        mark(6)
+        M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=s0)
+        mark(7)
+        s0.wait_event(self.ev_side)
+        mark(8)
+        return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
+                       self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
+                       self.x_perm, self.y, self.shared, self.out)
+
+
+# Event marks of step_two_stage: (name, first, last) -> elapsed between them.
+TWO_STAGE_MARKS = {
+    "gate_topk": (0, 1), "histogram": (1, 2), "permute_local": (2, 3), "ffn_local": (3, 4),
+    "wait_remote": (4, 5), "ffn_remote": (5, 6), "combine": (6, 7), "join": (7, 8),
+    "split": (9, 10), "permute_remote": (10, 11), "side_histogram_plan": (12, 13),
+}
 
 
 def stage_times_ms(ev: HipEvents, base: int = 0) -> Dict[str, float]:

@@ -31,6 +31,8 @@ SIGNATURES = {
     "moelb_split": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_permute_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moelb_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
+    "moelb_permute_local": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
+    "moelb_permute_remote": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moelb_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moelb_grouped_ffn": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]),
     "moelb_combine": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
@@ -134,6 +136,30 @@ def moelb_permute(h, idx, G, home, replica, host_count, ws, group_off, perm, pos
     _check(lib().moelb_permute(_p(h), _p(idx), T, d, k, E, G, N, dtype, _p(home), _p(replica), _p(host_count),
                                _p(ws), ws.numel() * ws.element_size(), _p(group_off), _p(perm), _p(pos), _p(x_perm),
                                _stream(stream)), "moelb_permute")
+
+
+def moelb_permute_local(h, idx, G, home, replica, ws, group_off, perm, pos, x_perm=None, d=None, dtype=None,
+                        stream=None):
+    T, k = idx.shape
+    E = home.shape[0]
+    N = replica.shape[1]
+    if h is not None:
+        d, dtype = h.shape[1], dtype_code(h)
+    _check(lib().moelb_permute_local(_p(h), _p(idx), T, d, k, E, G, N, dtype, _p(home), _p(replica), _p(ws),
+                                     ws.numel() * ws.element_size(), _p(group_off), _p(perm), _p(pos), _p(x_perm),
+                                     _stream(stream)), "moelb_permute_local")
+
+
+def moelb_permute_remote(h, idx, G, home, replica, host_count, ws, group_off, perm, pos, x_perm=None, d=None,
+                         dtype=None, stream=None):
+    T, k = idx.shape
+    E = home.shape[0]
+    N = replica.shape[1]
+    if h is not None:
+        d, dtype = h.shape[1], dtype_code(h)
+    _check(lib().moelb_permute_remote(_p(h), _p(idx), T, d, k, E, G, N, dtype, _p(home), _p(replica),
+                                      _p(host_count), _p(ws), ws.numel() * ws.element_size(), _p(group_off),
+                                      _p(perm), _p(pos), _p(x_perm), _stream(stream)), "moelb_permute_remote")
 
 
 def moelb_grouped_ffn_workspace_bytes(rows, num_groups, E, d, inter, dtype) -> int:

@@ -41,7 +41,7 @@ class LayerRun:
 
 
 def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool = True,
-              materialize_x: bool = True, hs=None, weights=None) -> LayerRun:
+              materialize_x: bool = True, hs=None, weights=None, two_stage: bool = False) -> LayerRun:
     from routed_expert_ffn_gate_amd.layer import MoELayer, to_device, to_host
     dev = torch.device("cuda")
     li = W.layer_inputs(cfg, layer, step, hs=hs)
@@ -61,7 +61,8 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
     replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
     L.predict_plan(h_prev, wc, bc, home, replica_cur)
     idx_pred = L.idx_next.clone()
-    o = L.step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2)
+    run_step = L.step_two_stage if two_stage else L.step
+    o = run_step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2)
     torch.cuda.synchronize()
     x_ok = None
     if o.x_perm is not None and materialize_x:

@@ -95,6 +95,77 @@ def test_down_gemm_short_k_several_tiles_per_workgroup(moelb, d, inter):
     _full_check(cfg, tokens=sample_tokens(cfg.T, 64))
 
 
+@pytest.mark.parametrize("name,changes", [
+    ("c2_qwen3_30b_decode", dict(steps=1, **RAGGED)),
+    ("c2_qwen3_30b_decode", dict(steps=1)),
+    ("c4_glm45_prefill", dict(T=2048)),
+])
+def test_two_stage_step_identical_to_one_stage(moelb, name, changes):
+    # MoE_local beside the split and remote permutation: the same step, bit
+    # for bit, and the oracle's where checked
+    cfg = W.scaled(W.config(name), **changes)
+    a = run_layer(cfg)
+    b = _full_check(cfg, tokens=sample_tokens(cfg.T, 32), two_stage=True)
+    valid = a.out["pos"] >= 0
+    for key in ["idx", "counts", "host_count", "load", "group_off", "perm", "pos", "replica_next", "out"]:
+        assert np.array_equal(a.out[key], b.out[key]), key
+    rows = a.out["pos"][valid]
+    assert np.array_equal(a.out["y"][rows], b.out["y"][rows])
+
+
+def test_permute_two_phases_equal_one_call(moelb):
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(21)
+    for trial in range(12):
+        G = int(rng.choice([1, 2, 4, 8]))
+        E = G * int(rng.choice([1, 3, 8, 16]))
+        k = int(rng.integers(1, 9))
+        T = G * int(rng.choice([0, 1, 37, 200]))
+        N = int(rng.integers(0, 4))
+        d = 64
+        pop = 1.0 / (1 + rng.permutation(E)) ** 1.2
+        idx = rng.choice(E, size=(T, k), p=pop / pop.sum()).astype(np.int32)
+        if T:
+            idx[rng.random((T, k)) < 0.02] = -1  # pairs left out
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = np.where(rng.random((G, max(N, 1))) < 0.8, rng.integers(0, E, (G, max(N, 1))), -1).astype(np.int32)
+        t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+        idx_t, home_t, rep_t = t(idx), t(home), t(rep)
+        h = torch.randn((T, d), device=dev).to(torch.bfloat16)
+        counts = torch.empty((G, E), dtype=torch.int32, device=dev)
+        M.moelb_histogram(idx_t, G, counts)
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split(counts, home_t, rep_t if N else torch.full((G, 1), -1, dtype=torch.int32, device=dev), hc, ld,
+                      passes=12)
+        repn = rep_t[:, :N] if N else torch.empty((G, 0), dtype=torch.int32, device=dev)
+        ws = torch.empty(M.moelb_permute_workspace_bytes(T, k, E, G), dtype=torch.uint8, device=dev)
+        outs = []
+        for two in (False, True):
+            off = torch.full((2 * G * E + 1,), -9, dtype=torch.int32, device=dev)
+            perm = torch.full((T * k,), -9, dtype=torch.int32, device=dev)
+            pos = torch.full((T * k,), -9, dtype=torch.int32, device=dev)
+            xp = torch.zeros((T * k, d), dtype=torch.bfloat16, device=dev)
+            if two:
+                M.moelb_permute_local(h, idx_t, G, home_t, repn, ws, off, perm, pos, xp)
+                torch.cuda.synchronize()
+                nl = int(off[G * E])
+                ref = outs[0]
+                assert torch.equal(off[:G * E + 1], ref[0][:G * E + 1]), trial
+                assert torch.equal(perm[:nl], ref[1][:nl]), trial
+                local = ref[2] < nl
+                assert torch.equal(pos[local], ref[2][local]), trial
+                assert bool((pos[~local] == -1).all()), trial
+                M.moelb_permute_remote(h, idx_t, G, home_t, repn, hc, ws, off, perm, pos, xp)
+            else:
+                M.moelb_permute(h, idx_t, G, home_t, repn, hc, ws, off, perm, pos, xp)
+            torch.cuda.synchronize()
+            outs.append((off, perm, pos, xp.view(torch.int16)))
+        for a, b in zip(*outs):
+            assert torch.equal(a, b), trial
+
+
 def test_zero_router_single_hot_set(moelb):
     # W = 0: every token picks the same k experts (by bias), so a few groups
     # hold every pair -- the most skewed case the method has.
