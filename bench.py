@@ -131,6 +131,34 @@ def time_two_stage(layer, args, K, stream, T):
             "hidden_ms": round(max(0.0, side - st["wait_remote"]), 4)}
 
 
+def time_split_variants(layer, home, replica_cur, stream, reps=20):
+    """Each split variant on this step's counts and placement: kernel time
+    (HIP events around `reps` calls) and the spatial balance mean/max of the
+    rank loads it leaves ("hash" = the even split, Relief with 0 passes)."""
+    import torch
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import HipEvents
+    hc = torch.empty_like(layer.host_count)
+    ld = torch.empty_like(layer.load)
+    out = {}
+    for name, code, passes in (("relief", M.MOELB_SPLIT_RELIEF, layer.passes),
+                               ("no_reverse", M.MOELB_SPLIT_NO_REVERSE, layer.passes),
+                               ("jacobi", M.MOELB_SPLIT_JACOBI, layer.passes),
+                               ("libra_greedy", M.MOELB_SPLIT_LIBRA_GREEDY, layer.passes),
+                               ("hash", M.MOELB_SPLIT_RELIEF, 0)):
+        ev = HipEvents(2)
+        ev.record(0, stream)
+        for _ in range(reps):
+            M.moelb_split_variant(layer.counts, home, replica_cur, hc, ld, code, passes=passes, stream=stream)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        lf = ld.double()
+        out[name] = {"us": round(1e3 * ev.elapsed_ms(0, 1) / reps, 2),
+                     "spatial": round(float(lf.mean() / lf.max()), 4)}
+        ev.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +248,7 @@ def main():
 
     balance = routing_stats(cfg, layer, idx_pred, home)
     two_stage = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K, stream, cfg.T)
+    split_variants = time_split_variants(layer, home, replica_cur, stream)
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
@@ -263,6 +292,7 @@ def main():
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
         "routing": balance,
         "two_stage": two_stage,
+        "split_variants": split_variants,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),

@@ -156,6 +156,37 @@ int moelb_split(const int32_t* counts, const int32_t* home, const int32_t* repli
                 int32_t* host_count, int32_t* load, void* stream);
 
 /*
+ * Split variants on the same transfers (Relief, "Ablation Results (Table
+ * III)"; Libra README "Key Ideas", adaptive token sharding), for comparing
+ * balance and latency.  moelb_split is variant MOELB_SPLIT_RELIEF; passes = 0
+ * of any pairwise variant is the even ("hash") split.
+ *  MOELB_SPLIT_NO_REVERSE   Relief's move only when the home is the heavier
+ *                           side (mass only flows from home to replica).
+ *  MOELB_SPLIT_JACOBI       every transfer of a pass reads the loads of the
+ *                           pass start and moves |gap| >> 2 (damped),
+ *                           capped by the giver's current mass.
+ *  MOELB_SPLIT_LIBRA_GREEDY pools start on their homes; repeatedly the
+ *                           most-loaded rank a (ties: lower rank) hands
+ *                           min(mass, (load[a]-load[b]) >> 1) tokens of its
+ *                           replicated expert with the most mass on a (ties:
+ *                           lower id) to that expert's least-loaded other
+ *                           host b (ties: lower rank), if load[a]-load[b] >= 2;
+ *                           at most passes x (number of replica transfers)
+ *                           moves.
+ * Same arguments, outputs and requirements as moelb_split; counts must be
+ * non-negative.  An unknown variant returns MOELB_EINVAL.
+ */
+enum moelb_split_variant {
+  MOELB_SPLIT_RELIEF = 0,
+  MOELB_SPLIT_NO_REVERSE = 1,
+  MOELB_SPLIT_JACOBI = 2,
+  MOELB_SPLIT_LIBRA_GREEDY = 3
+};
+int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica,
+                        int G, int E, int N, int passes, int eps, int variant,
+                        int32_t* host_count, int32_t* load, void* stream);
+
+/*
  * Local/remote permutation (Libra README "Key Ideas": two-stage locality-aware
  * execution, MoE_local on the token's own GPU, MoE_remote on the others).
  *  Pair p = t*k + j, expert e = idx[t,j], owner s = t div (T/G).  Local

@@ -283,10 +283,22 @@ constexpr int MAX_TRANSFERS = MOELB_MAX_G * MOELB_MAX_N;  // one per replica slo
 constexpr int COLOUR_WORDS = 32;                          // up to 1024 colours
 constexpr int TR_PER_LANE = MAX_TRANSFERS / 64;
 
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// variant: MOELB_SPLIT_* (include/moelb.h).  Relief, and the two ablations
+// that change one ingredient of its pairwise move, share the round schedule;
+// Libra's greedy sharding starts from the pools on their homes and needs no
+// schedule.
 __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __restrict__ counts,
                                                                const int32_t* __restrict__ home,
                                                                const int32_t* __restrict__ replica, int G, int E,
-                                                               int N, int passes, int eps,
+                                                               int N, int passes, int eps, int variant,
                                                                int32_t* __restrict__ host_count,
                                                                int32_t* __restrict__ load_out) {
   __shared__ unsigned long long hostmask[MOELB_MAX_E];
@@ -296,7 +308,11 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   __shared__ int t_e[MAX_TRANSFERS];
   __shared__ unsigned used[MOELB_MAX_G][COLOUR_WORDS];
   __shared__ int load[MOELB_MAX_G];
+  __shared__ int snap[MOELB_MAX_G];         // Jacobi: loads at the start of the pass
   __shared__ int wave_sum[SPLIT_THREADS / 64];
+  const bool greedy = variant == MOELB_SPLIT_LIBRA_GREEDY;
+  const bool no_reverse = variant == MOELB_SPLIT_NO_REVERSE;
+  const bool jacobi = variant == MOELB_SPLIT_JACOBI;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -357,7 +373,9 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
     int t = toff[e], pos = 0;
     for (int r = 0; r < G; ++r) {
       if (!((mask >> r) & 1ull)) continue;
-      const int share = even_share(R, m, pos++);
+      // even split, or (greedy) the whole pool on the home
+      const int share = greedy ? (r == my_home ? R : 0) : even_share(R, m, pos);
+      ++pos;
       atomicAdd(&load[r], share);
       if (r == my_home) {
         xhome[e] = share;
@@ -373,6 +391,80 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   const int n = toff[E];
   __syncthreads();
   if (tid >= 64) return;
+
+  if (greedy) {
+    // Libra's sharding, one wave: the most-loaded rank a hands
+    // min(mass, gap >> 1) tokens of its replicated expert with the most mass
+    // on it (ties: lower id) to that expert's least-loaded other host b
+    // (ties: lower rank), if load[a] - load[b] >= 2; lane l owns experts
+    // l + 64 q.  At most passes x n moves.
+    const int max_moves = passes * max(1, n);
+    for (int it = 0; it < max_moves; ++it) {
+      unsigned long long key = 0ull;
+      if (lane < G) key = ((unsigned long long)((uint32_t)load[lane] ^ 0x80000000u) << 6) | (unsigned)(63 - lane);
+      const int a = 63 - (int)(wave_max_u64(key) & 63);
+      const int load_a = load[a];
+      unsigned long long best = 0ull;
+      int best_b = 0, best_d = 0;
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        if (e >= E) break;
+        const int t0 = toff[e], t1 = toff[e + 1];
+        if (t1 == t0) continue;  // unreplicated
+        const int hh = t_u[t0];  // the home
+        int mass_a = 0, b = -1, lb = 0;
+        if (hh == a) {
+          mass_a = xhome[e];
+        } else {
+          b = hh;
+          lb = load[hh];
+        }
+        for (int t = t0; t < t1; ++t) {
+          const int v = t_v[t];
+          if (v == a) {
+            mass_a = t_x[t];
+          } else {
+            const int l = load[v];
+            if (b < 0 || l < lb || (l == lb && v < b)) {
+              b = v;
+              lb = l;
+            }
+          }
+        }
+        if (mass_a > 0 && (long long)load_a - lb >= 2) {
+          const unsigned long long k = ((unsigned long long)(uint32_t)mass_a << 8) | (unsigned)(255 - e);
+          if (k > best) {
+            best = k;
+            best_b = b;
+            best_d = min(mass_a, (int)(((long long)load_a - lb) >> 1));
+          }
+        }
+      }
+      const unsigned long long wbest = wave_max_u64(best);
+      if (wbest == 0ull) break;
+      const int e = 255 - (int)(wbest & 255);
+      if (lane == (e & 63)) {
+        const int b = best_b, d = best_d;
+        load[a] -= d;
+        load[b] += d;
+        const int t0 = toff[e], t1 = toff[e + 1];
+        if (t_u[t0] == a) xhome[e] -= d;
+        if (t_u[t0] == b) xhome[e] += d;
+        for (int t = t0; t < t1; ++t) {
+          if (t_v[t] == a) t_x[t] -= d;
+          if (t_v[t] == b) t_x[t] += d;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    for (int t = lane; t < n; t += 64) {
+      const int x = t_e[t];
+      host_count[(size_t)x * G + t_v[t]] = t_x[t];
+      if (t == toff[x]) host_count[(size_t)x * G + t_u[t]] = xhome[x];
+    }
+    for (int r = lane; r < G; r += 64) load_out[r] = load[r];
+    return;
+  }
 
   // One wave from here.  Greedy edge colouring in list order.  Fast path: lane
   // r holds rank r's used colours below 64 in a register; if some transfer
@@ -444,12 +536,17 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
     int tx = has ? t_x[lane] : 0;
     for (int p = 0; p < passes; ++p) {
       bool moved = false;
+      if (jacobi) {
+        for (int r = lane; r < G; r += 64) snap[r] = load[r];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      }
       for (int rd = 0; rd < ncol; ++rd) {
         if (col == rd) {
           const int lu = load[u], lv = load[v], xh = xhome[x];
-          const int gap = lu - lv;
-          int delta = (gap < 0 ? -gap : gap) >> 1;
+          const int gap = jacobi ? snap[u] - snap[v] : lu - lv;
+          int delta = (gap < 0 ? -gap : gap) >> (jacobi ? 2 : 1);
           delta = min(delta, gap > 0 ? xh : tx);
+          if (no_reverse && gap <= 0) delta = 0;
           if (delta > eps) {
             const int sd = gap > 0 ? delta : -delta;  // mass moved from u to v
             load[u] = lu - sd;
@@ -467,16 +564,21 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   } else {
     for (int p = 0; p < passes; ++p) {
       bool moved = false;
+      if (jacobi) {
+        for (int r = lane; r < G; r += 64) snap[r] = load[r];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      }
       for (int rd = 0; rd < ncol; ++rd) {
 #pragma unroll
         for (int q = 0; q < TR_PER_LANE; ++q) {
           const int t = lane + 64 * q;
           if (t < n && my_col[q] == rd) {
             const int u = t_u[t], v = t_v[t], x = t_e[t];
-            const int gap = load[u] - load[v];
-            int delta = (gap < 0 ? -gap : gap) >> 1;
+            const int gap = jacobi ? snap[u] - snap[v] : load[u] - load[v];
+            int delta = (gap < 0 ? -gap : gap) >> (jacobi ? 2 : 1);
             const int limit = gap > 0 ? xhome[x] : t_x[t];
             delta = min(delta, limit);
+            if (no_reverse && gap <= 0) delta = 0;
             if (delta > eps) {
               if (gap > 0) {
                 load[u] -= delta;
@@ -539,14 +641,22 @@ extern "C" int moelb_plan(const int32_t* counts, const int32_t* home, int G, int
   return MOELB_OK;
 }
 
-extern "C" int moelb_split(const int32_t* counts, const int32_t* home, const int32_t* replica, int G, int E,
-                           int N, int passes, int eps, int32_t* host_count, int32_t* load, void* stream) {
+extern "C" int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica, int G,
+                                   int E, int N, int passes, int eps, int variant, int32_t* host_count,
+                                   int32_t* load, void* stream) {
   if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
   if (passes < 0 || passes > 1024 || eps < 0) return MOELB_EINVAL;
+  if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_LIBRA_GREEDY) return MOELB_EINVAL;
   if (!counts || !home || (N > 0 && !replica) || !host_count || !load) return MOELB_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(split_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home, N > 0 ? replica : home, G, E,
-                     N, passes, eps, host_count, load);
+                     N, passes, eps, variant, host_count, load);
   MOELB_CHECK_LAUNCH();
   return MOELB_OK;
+}
+
+extern "C" int moelb_split(const int32_t* counts, const int32_t* home, const int32_t* replica, int G, int E,
+                           int N, int passes, int eps, int32_t* host_count, int32_t* load, void* stream) {
+  return moelb_split_variant(counts, home, replica, G, E, N, passes, eps, MOELB_SPLIT_RELIEF, host_count, load,
+                             stream);
 }

@@ -29,6 +29,7 @@ SIGNATURES = {
     "moelb_histogram": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_plan": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moelb_split_variant": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_permute_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moelb_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moelb_permute_local": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
@@ -120,6 +121,16 @@ def moelb_split(counts, home, replica, host_count, load, passes=12, eps=0, strea
     N = replica.shape[1]
     _check(lib().moelb_split(_p(counts), _p(home), _p(replica), G, E, N, passes, eps, _p(host_count), _p(load),
                              _stream(stream)), "moelb_split")
+
+
+MOELB_SPLIT_RELIEF, MOELB_SPLIT_NO_REVERSE, MOELB_SPLIT_JACOBI, MOELB_SPLIT_LIBRA_GREEDY = 0, 1, 2, 3
+
+
+def moelb_split_variant(counts, home, replica, host_count, load, variant, passes=12, eps=0, stream=None):
+    G, E = counts.shape
+    N = replica.shape[1]
+    _check(lib().moelb_split_variant(_p(counts), _p(home), _p(replica), G, E, N, passes, eps, variant,
+                                     _p(host_count), _p(load), _stream(stream)), "moelb_split_variant")
 
 
 def moelb_permute_workspace_bytes(T, k, E, G) -> int:

@@ -60,6 +60,12 @@ def test_invalid_arguments_rejected_before_launch(lib):
     # negative passes / eps
     assert lib.moelb_split(P, P, P, 4, 8, 1, -1, 0, P, P, N) == 1
     assert lib.moelb_split(P, P, P, 4, 8, 1, 12, -1, P, P, N) == 1
+    # unknown split variant; negative passes for a variant
+    assert lib.moelb_split_variant(P, P, P, 4, 8, 1, 12, 0, 4, P, P, N) == 1
+    assert lib.moelb_split_variant(P, P, P, 4, 8, 1, -1, 0, 3, P, P, N) == 1
+    # two-phase permute: workspace too small; remote phase without host_count
+    assert lib.moelb_permute_local(N, P, 64, 8, 2, 8, 4, 1, 1, P, P, P, 1, P, P, P, N, N) == 3
+    assert lib.moelb_permute_remote(N, P, 64, 8, 2, 8, 4, 1, 1, P, P, N, P, 1 << 20, P, P, P, N, N) == 1
     # permute: workspace too small
     need = lib.moelb_permute_workspace_bytes(64, 2, 8, 4)
     assert need > 0

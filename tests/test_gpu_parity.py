@@ -261,6 +261,38 @@ def test_plan_and_split_random_instances(moelb):
         assert np.array_equal(ld.cpu().numpy(), ld_o)
 
 
+def test_split_variants_random_instances(moelb):
+    """Each GPU split variant against its oracle, bit for bit, on random
+    placements from the plan (register path up to 64 transfers, LDS path
+    beyond)."""
+    from oracle import moe_oracle as O
+    from oracle import split_variants as V
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(17)
+    codes = {"relief": M.MOELB_SPLIT_RELIEF, "no_reverse": M.MOELB_SPLIT_NO_REVERSE,
+             "jacobi": M.MOELB_SPLIT_JACOBI, "libra_greedy": M.MOELB_SPLIT_LIBRA_GREEDY}
+    for trial in range(48):
+        G = int(rng.choice([2, 4, 8, 16, 64]))
+        E = G * int(rng.choice([1, 2, 4])) if G < 64 else int(rng.choice([64, 128, 256]))
+        N = int(rng.integers(1, 9 if G >= 16 else 4))
+        L = int(rng.integers(0, N + 1))
+        pop = 1.0 / (1 + rng.permutation(E)) ** rng.uniform(0.5, 1.6)
+        c = np.stack([rng.multinomial(int(rng.integers(0, 3000)), pop / pop.sum()) for _ in range(G)]).astype(np.int32)
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = O.plan(c[:, rng.permutation(E)] if trial % 2 else c, home, G, E, N, L)
+        passes = int(rng.choice([0, 1, 3, 12]))
+        ct, ht, rt = (torch.from_numpy(a).to(dev) for a in (c, home, rep))
+        for name, code in codes.items():
+            eps = 0 if name == "libra_greedy" else int(rng.choice([0, 0, 2]))
+            hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+            ld = torch.empty(G, dtype=torch.int32, device=dev)
+            M.moelb_split_variant(ct, ht, rt, hc, ld, code, passes=passes, eps=eps)
+            hc_o, ld_o = V.split_variant(c, home, rep, G, E, name, passes=passes, eps=eps)
+            assert np.array_equal(hc.cpu().numpy(), hc_o), (trial, name, G, E, N, passes)
+            assert np.array_equal(ld.cpu().numpy(), ld_o), (trial, name)
+
+
 def test_split_heavily_replicated_home(moelb):
     """Every rank replicates the four experts of rank 0: rank 0 ends up in one
     transfer per replica, which takes the split past 64 edge colours (and, at
