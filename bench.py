@@ -159,6 +159,52 @@ def time_split_variants(layer, home, replica_cur, stream, reps=20):
     return out
 
 
+def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20):
+    """The same step with FreeBalance's expert swaps in place of replication
+    (budget: the N replica slots as swaps per rank; gamma = 1 / mean rank
+    load): step time, the balance its placement leaves, the swap count and
+    the planner kernel's time."""
+    import torch
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import HipEvents, MoELayer
+    h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2 = tensors
+    dev = h.device
+    fl = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
+                  shared_inter=cfg.shared_inter, gather_rows=gather_rows, materialize_x=not gather_rows,
+                  balancer="freebalance", fb_budget=cfg.N)
+    home_cur = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    no_rep = torch.empty((cfg.G, 0), dtype=torch.int32, device=dev)
+    fl.predict_placement(h_prev, wc, bc, home, home_cur)
+    swaps = int(fl.n_swaps_next.item())  # the swaps that made this step's placement
+    for _ in range(W):
+        fl.step(h, wc, bc, wn, bn, home_cur, no_rep, W13, W2, S13, S2)
+    ev = HipEvents(4)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(K):
+        fl.step(h, wc, bc, wn, bn, home_cur, no_rep, W13, W2, S13, S2)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / K
+    ld = fl.load.double()
+    ho = torch.empty_like(home_cur)
+    pl = torch.empty_like(fl.plan_load_next)
+    ev.record(2, stream)
+    for _ in range(reps):
+        M.moelb_plan_swaps(fl.counts_next, home, ho, pl, tau=fl.fb_tau, gamma=fl.fb_gamma,
+                           max_swaps_per_rank=fl.fb_budget, stream=stream)
+    ev.record(3, stream)
+    torch.cuda.synchronize()
+    out = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "spatial": round(float(ld.mean() / ld.max()), 4), "swaps": swaps,
+           "plan_us": round(1e3 * ev.elapsed_ms(2, 3) / reps, 2),
+           "gamma": list(fl.fb_gamma), "swaps_per_rank_budget": fl.fb_budget}
+    ev.close()
+    del fl
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +295,8 @@ def main():
     balance = routing_stats(cfg, layer, idx_pred, home)
     two_stage = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K, stream, cfg.T)
     split_variants = time_split_variants(layer, home, replica_cur, stream)
+    freebalance = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K, args.warmup, stream,
+                                   gather_rows=args.rows == "gather")
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
@@ -293,6 +341,7 @@ def main():
         "routing": balance,
         "two_stage": two_stage,
         "split_variants": split_variants,
+        "freebalance": freebalance,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),

@@ -156,6 +156,35 @@ int moelb_split(const int32_t* counts, const int32_t* home, const int32_t* repli
                 int32_t* host_count, int32_t* load, void* stream);
 
 /*
+ * Budgeted expert-swap planner (FreeBalance section 3.3, eq. 6-8 and
+ * Algorithm 1): the alternative to replication -- experts trade places, so
+ * every rank keeps its number of experts and no split is needed (run the rest
+ * of the path with home_out and no replicas).
+ *   n_e = sum_s counts[s,e] (predicted pairs); L_r = sum of n_e over the
+ *   experts on r.  While L_a - L_b > tau for a = most-loaded and b =
+ *   least-loaded rank (ties: lower rank) and both have budget left: among the
+ *   experts on a and on b that have not moved yet, swap the pair with the
+ *   largest positive drop of Phi(L) = max_r L_r + gamma * sum_r (L_r -
+ *   mean)^2, gamma = gamma_num / gamma_den (ties: lower e_a, then lower e_b);
+ *   stop if no pair lowers Phi.  Each swap spends one of both ranks'
+ *   max_swaps_per_rank (every swap moves two equal-sized experts, so the
+ *   page's per-rank transfer budget is a swap count).
+ *  counts   [G,E] int32  predicted counts (the lookahead histogram), >= 0,
+ *                        totalling below 2^24 pairs (exact 64-bit scores)
+ *  home     [E]   int32  current placement (entries outside [0,G) read as 0)
+ *  home_out [E]   int32 out: placement after the swaps (may be `home` itself)
+ *  swaps    [E/2][2] int32 out or NULL: (e_a, e_b) in acceptance order
+ *  n_swaps  [1]   int32 out or NULL: number of swaps
+ *  load     [G]   int32 out: rank loads after the swaps
+ * Requires G <= 64, E <= 256, tau >= 0, 0 <= gamma_num <= 2^12,
+ * 1 <= gamma_den <= 2^20, max_swaps_per_rank >= 0.
+ */
+int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int G, int E, int tau,
+                     int gamma_num, int gamma_den, int max_swaps_per_rank,
+                     int32_t* home_out, int32_t* swaps, int32_t* n_swaps, int32_t* load,
+                     void* stream);
+
+/*
  * Split variants on the same transfers (Relief, "Ablation Results (Table
  * III)"; Libra README "Key Ideas", adaptive token sharding), for comparing
  * balance and latency.  moelb_split is variant MOELB_SPLIT_RELIEF; passes = 0

@@ -19,6 +19,8 @@
 //   masks by atomic OR, transfer offsets by a block scan); the colouring and
 //   the rounds run in one wave, whose own in-order LDS accesses order the
 //   rounds without barriers.
+#include <climits>
+
 #include "common.h"
 
 namespace {
@@ -274,6 +276,154 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* __res
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   for (int i = lane; i < G * N; i += 64) replica[i] = slots[i];
   if (plan_load && lane < G) plan_load[lane] = my_load;
+}
+
+// ---------------------------------------------------------------- swap planner
+//
+// FreeBalance ("FreeBalance: Pre-Routing Online MoE Load Balancing via
+// Residual Workload Prediction"), section 3.3 and Algorithm 1: pairwise
+// expert swaps between the most- and the least-loaded rank, each the one
+// with the largest drop of Phi(L) = max L + gamma * sum (L - mean)^2 (eq. 8;
+// a swap moves d = n_a - n_b pairs from a to b, so the variance term drops
+// by 2 d (L_a - L_b - d), eq. 6-7), ties to the lower e_a then e_b; an
+// expert moves at most once, each rank takes part in at most `budget` swaps,
+// and planning stops when L_a - L_b <= tau or no swap lowers Phi.  Exact
+// integer arithmetic: the benefit is kept times gamma's denominator.  One
+// workgroup: wave 0 finds the rank pair, every thread scores candidate
+// pairs, block reductions pick the swap, thread 0 applies it.
+
+constexpr int SWAP_THREADS = 256;  // >= MOELB_MAX_E
+
+__device__ __forceinline__ long long wave_max_i64(long long v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const long long w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(SWAP_THREADS) void swap_plan_kernel(const int32_t* __restrict__ counts,
+                                                                  const int32_t* __restrict__ home_in, int G, int E,
+                                                                  int tau, int gamma_num, int gamma_den, int budget,
+                                                                  int32_t* __restrict__ home_out,
+                                                                  int32_t* __restrict__ swaps,
+                                                                  int32_t* __restrict__ n_swaps,
+                                                                  int32_t* __restrict__ load_out) {
+  __shared__ int n[MOELB_MAX_E], where[MOELB_MAX_E], moved[MOELB_MAX_E];
+  __shared__ int list_a[MOELB_MAX_E], list_b[MOELB_MAX_E];
+  __shared__ int load[MOELB_MAX_G], left[MOELB_MAX_G];
+  __shared__ long long red_b[SWAP_THREADS / 64];
+  __shared__ int red_t[SWAP_THREADS / 64];
+  __shared__ int s_a, s_b, s_other, s_na, s_nb, s_stop, s_nsw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int r = tid; r < G; r += SWAP_THREADS) {
+    load[r] = 0;
+    left[r] = budget;
+  }
+  if (tid == 0) s_nsw = 0;
+  __syncthreads();
+  if (tid < E) {
+    int sum = 0;
+    for (int s2 = 0; s2 < G; ++s2) sum += counts[(size_t)s2 * E + tid];
+    const int h = home_in[tid];
+    n[tid] = sum;
+    where[tid] = (h >= 0 && h < G) ? h : 0;
+    moved[tid] = 0;
+    atomicAdd(&load[where[tid]], sum);
+  }
+  __syncthreads();
+  for (;;) {
+    if (wave == 0) {
+      // a: most loaded (ties lower rank), b: least loaded (ties lower rank)
+      const int l = lane < G ? load[lane] : 0;
+      const long long ka = lane < G ? (long long)l * 64 + (63 - lane) : LLONG_MIN;
+      const int a = 63 - (int)(wave_max_i64(ka) & 63);
+      const long long kb = lane < G ? -(long long)l * 64 + (63 - lane) : LLONG_MIN;
+      const int b = 63 - (int)(wave_max_i64(kb) & 63);
+      // largest load outside {a, b}
+      const long long ko = (lane < G && lane != a && lane != b) ? (long long)l : LLONG_MIN;
+      const long long other = wave_max_i64(ko);
+      if (lane == 0) {
+        s_a = a;
+        s_b = b;
+        s_other = other == LLONG_MIN ? INT_MIN : (int)other;
+        s_stop = (load[a] - load[b] <= tau || left[a] == 0 || left[b] == 0) ? 1 : 0;
+        s_na = 0;
+        s_nb = 0;
+      }
+    }
+    __syncthreads();
+    if (s_stop) break;
+    const int a = s_a, b = s_b;
+    if (tid < E && !moved[tid]) {
+      if (where[tid] == a) list_a[atomicAdd(&s_na, 1)] = tid;
+      if (where[tid] == b) list_b[atomicAdd(&s_nb, 1)] = tid;
+    }
+    __syncthreads();
+    const int na = s_na, nb = s_nb;
+    const long long la = load[a], lb = load[b], gap = la - lb;
+    const long long other = s_other;
+    long long best = 0;  // benefit x gamma_den; only positive ones count
+    int best_t = INT_MAX;
+    for (int i = tid; i < na * nb; i += SWAP_THREADS) {
+      const int ea = list_a[i / nb], eb = list_b[i % nb];
+      const long long d = (long long)n[ea] - n[eb];
+      const long long na2 = la - d, nb2 = lb + d;
+      long long m = na2 > nb2 ? na2 : nb2;
+      m = other > m ? other : m;
+      const long long ben = (long long)gamma_den * (la - m) + (long long)gamma_num * 2 * d * (gap - d);
+      const int t = (ea << 8) | eb;
+      if (ben > 0 && (ben > best || (ben == best && t < best_t))) {
+        best = ben;
+        best_t = t;
+      }
+    }
+    // block arg-max of the benefit, then the smallest (e_a, e_b) among its holders
+    const long long wb = wave_max_i64(best);
+    const int wt = wave_min_i32(best == wb ? best_t : INT_MAX);
+    if (lane == 0) {
+      red_b[wave] = wb;
+      red_t[wave] = wt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      long long bb = 0;
+      int bt = INT_MAX;
+      for (int w = 0; w < SWAP_THREADS / 64; ++w)
+        if (red_b[w] > bb || (red_b[w] == bb && red_t[w] < bt)) {
+          bb = red_b[w];
+          bt = red_t[w];
+        }
+      if (bb <= 0) {
+        s_stop = 1;
+      } else {
+        const int ea = bt >> 8, eb = bt & 255;
+        const int d = n[ea] - n[eb];
+        load[a] -= d;
+        load[b] += d;
+        where[ea] = b;
+        where[eb] = a;
+        moved[ea] = moved[eb] = 1;
+        --left[a];
+        --left[b];
+        if (swaps) {
+          swaps[2 * s_nsw] = ea;
+          swaps[2 * s_nsw + 1] = eb;
+        }
+        ++s_nsw;
+      }
+    }
+    __syncthreads();
+    if (s_stop) break;
+  }
+  if (tid < E) home_out[tid] = where[tid];
+  if (tid < G) load_out[tid] = load[tid];
+  if (tid == 0 && n_swaps) *n_swaps = s_nsw;
 }
 
 // ---------------------------------------------------------------- split
@@ -659,4 +809,19 @@ extern "C" int moelb_split(const int32_t* counts, const int32_t* home, const int
                            int N, int passes, int eps, int32_t* host_count, int32_t* load, void* stream) {
   return moelb_split_variant(counts, home, replica, G, E, N, passes, eps, MOELB_SPLIT_RELIEF, host_count, load,
                              stream);
+}
+
+extern "C" int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int G, int E, int tau, int gamma_num,
+                                int gamma_den, int max_swaps_per_rank, int32_t* home_out, int32_t* swaps,
+                                int32_t* n_swaps, int32_t* load, void* stream) {
+  if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E) return MOELB_EINVAL;
+  if (tau < 0 || gamma_num < 0 || gamma_num > (1 << 12) || gamma_den < 1 || gamma_den > (1 << 20) ||
+      max_swaps_per_rank < 0)
+    return MOELB_EINVAL;
+  if (!counts || !home || !home_out || !load) return MOELB_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(swap_plan_kernel, dim3(1), dim3(SWAP_THREADS), 0, s, counts, home, G, E, tau, gamma_num,
+                     gamma_den, max_swaps_per_rank, home_out, swaps, n_swaps, load);
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
 }

@@ -97,6 +97,7 @@ class StepOut:
     y: torch.Tensor
     shared: Optional[torch.Tensor]
     out: torch.Tensor
+    home_next: Optional[torch.Tensor] = None  # FreeBalance: the next layer's placement
 
 
 class MoELayer:
@@ -106,9 +107,20 @@ class MoELayer:
     replica slots, L locality imports; ``dtype`` "bf16" or "f32"."""
 
     def __init__(self, T, d, E, k, inter, G, N, L, dtype, device="cuda", shared_inter=0, passes=12,
-                 gather_rows=True, materialize_x=False):
+                 gather_rows=True, materialize_x=False, balancer="libra", fb_tau=0, fb_gamma=None,
+                 fb_budget=None):
+        """balancer "libra": replication plan (N slots, L locality imports)
+        and the per-step split; "freebalance": expert swaps instead (no
+        replicas; at most fb_budget swaps per rank, default N; threshold
+        fb_tau; gamma = fb_gamma (num, den), default 1 / the mean rank load)."""
         self.T, self.d, self.E, self.k, self.inter = T, d, E, k, inter
         self.G, self.N, self.L, self.passes = G, N, L, passes
+        if balancer not in ("libra", "freebalance"):
+            raise ValueError(balancer)
+        self.balancer = balancer
+        self.fb_tau = fb_tau
+        self.fb_gamma = fb_gamma if fb_gamma is not None else (1, min(1 << 20, max(1, (T * k) // G)))
+        self.fb_budget = fb_budget if fb_budget is not None else N
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.dev = torch.device(device)
@@ -149,6 +161,11 @@ class MoELayer:
         self.ev_hist = torch.cuda.Event()
         self.ev_local = torch.cuda.Event()
         self.ev_remote = torch.cuda.Event()
+        if balancer == "freebalance":
+            self.home_next = torch.empty((E,), **i32)
+            self.swaps_next = torch.empty((E // 2 + 1, 2), **i32)
+            self.n_swaps_next = torch.empty((1,), **i32)
+            self.home_base = None
         self.ws_shared = None
         if shared_inter > 0:
             self.ws_shared = torch.empty((M.moelb_grouped_ffn_workspace_bytes(T, 1, 1, d, shared_inter, code),),
@@ -162,6 +179,34 @@ class MoELayer:
         M.moelb_gate_topk(h_prev, w_cur, b_cur, None, None, self.idx_next, self.wts, None, None, stream=stream)
         M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
         M.moelb_plan(self.counts_next, home, self.L, replica_out, None, stream=stream)
+
+    def predict_placement(self, h_prev, w_cur, b_cur, home_base, home_out, stream=None):
+        """FreeBalance prologue: the early router (this layer's gate on the
+        previous hidden states), its histogram, and the swaps from the base
+        placement ``home_base`` (kept as the next layer's starting placement)
+        into ``home_out``."""
+        M.moelb_gate_topk(h_prev, w_cur, b_cur, None, None, self.idx_next, self.wts, None, None, stream=stream)
+        M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
+        self.home_base = home_base
+        self._plan_swaps(home_out, stream)
+
+    def _plan_swaps(self, home_out, stream):
+        M.moelb_plan_swaps(self.counts_next, self.home_base, home_out, self.plan_load_next, tau=self.fb_tau,
+                           gamma=self.fb_gamma, max_swaps_per_rank=self.fb_budget, swaps=self.swaps_next,
+                           n_swaps=self.n_swaps_next, stream=stream)
+
+    def _plan_next(self, home):
+        """The next layer's balancing, on the side stream."""
+        if self.balancer == "freebalance":
+            self._plan_swaps(self.home_next, self.side)
+        else:
+            M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+
+    def _out(self):
+        return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
+                       self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
+                       self.x_perm, self.y, self.shared, self.out,
+                       self.home_next if self.balancer == "freebalance" else None)
 
     def step(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None, shared_w2=None,
              stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
@@ -183,7 +228,7 @@ class MoELayer:
         self.side.wait_event(self.ev_gate)
         mark(12, self.side)
         M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=self.side)
-        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+        self._plan_next(home)
         mark(13, self.side)
         self.ev_side.record(self.side)
         mark(1)
@@ -211,9 +256,7 @@ class MoELayer:
         mark(6)
         s0.wait_event(self.ev_side)
         mark(7)
-        return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
-                       self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
-                       self.x_perm, self.y, self.shared, self.out)
+        return self._out()
 
 
     def step_two_stage(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None,
@@ -250,7 +293,7 @@ class MoELayer:
         self.side.wait_event(self.ev_gate)
         mark(12, self.side)
         M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=self.side)
-        M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+        self._plan_next(home)
         mark(13, self.side)
         self.ev_side.record(self.side)
         mark(1)
@@ -287,9 +330,7 @@ class MoELayer:
         mark(7)
         s0.wait_event(self.ev_side)
         mark(8)
-        return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
-                       self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
-                       self.x_perm, self.y, self.shared, self.out)
+        return self._out()
 
 
 # Event marks of step_two_stage: (name, first, last) -> elapsed between them.

@@ -30,6 +30,7 @@ SIGNATURES = {
     "moelb_plan": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split_variant": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moelb_plan_swaps": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moelb_permute_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moelb_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moelb_permute_local": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
@@ -131,6 +132,14 @@ def moelb_split_variant(counts, home, replica, host_count, load, variant, passes
     N = replica.shape[1]
     _check(lib().moelb_split_variant(_p(counts), _p(home), _p(replica), G, E, N, passes, eps, variant,
                                      _p(host_count), _p(load), _stream(stream)), "moelb_split_variant")
+
+
+def moelb_plan_swaps(counts, home, home_out, load, tau=0, gamma=(0, 1), max_swaps_per_rank=1 << 30, swaps=None,
+                     n_swaps=None, stream=None):
+    G, E = counts.shape
+    _check(lib().moelb_plan_swaps(_p(counts), _p(home), G, E, tau, gamma[0], gamma[1], max_swaps_per_rank,
+                                  _p(home_out), _p(swaps), _p(n_swaps), _p(load), _stream(stream)),
+           "moelb_plan_swaps")
 
 
 def moelb_permute_workspace_bytes(T, k, E, G) -> int:

@@ -38,10 +38,14 @@ class LayerRun:
     replica_cur: np.ndarray
     out: Dict[str, np.ndarray]
     x_perm_ok: Optional[bool]
+    balancer: str = "libra"
+    home_cur: Optional[np.ndarray] = None     # FreeBalance: placement of this step
+    fb: Optional[tuple] = None                # FreeBalance: (tau, gamma num, gamma den, budget)
 
 
 def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool = True,
-              materialize_x: bool = True, hs=None, weights=None, two_stage: bool = False) -> LayerRun:
+              materialize_x: bool = True, hs=None, weights=None, two_stage: bool = False,
+              balancer: str = "libra") -> LayerRun:
     from routed_expert_ffn_gate_amd.layer import MoELayer, to_device, to_host
     dev = torch.device("cuda")
     li = W.layer_inputs(cfg, layer, step, hs=hs)
@@ -57,18 +61,26 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
     if sh is not None:
         S13, S2 = d(sh[0]), d(sh[1])
     L = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype, shared_inter=cfg.shared_inter,
-                 gather_rows=gather_rows, materialize_x=materialize_x)
-    replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
-    L.predict_plan(h_prev, wc, bc, home, replica_cur)
+                 gather_rows=gather_rows, materialize_x=materialize_x, balancer=balancer)
+    home_cur = None
+    if balancer == "freebalance":
+        replica_cur = torch.empty((cfg.G, 0), dtype=torch.int32, device=dev)
+        home_cur = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+        L.predict_placement(h_prev, wc, bc, home, home_cur)
+        home_step = home_cur
+    else:
+        replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
+        L.predict_plan(h_prev, wc, bc, home, replica_cur)
+        home_step = home
     idx_pred = L.idx_next.clone()
     run_step = L.step_two_stage if two_stage else L.step
-    o = run_step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2)
+    o = run_step(h, wc, bc, wn, bn, home_step, replica_cur, W13, W2, S13, S2)
     torch.cuda.synchronize()
     x_ok = None
     if o.x_perm is not None and materialize_x:
         from routed_expert_ffn_gate_amd import moelb as M
         # the row-copying permutation, on the same inputs, checked bit for bit
-        M.moelb_permute(h, o.idx, cfg.G, home, replica_cur, o.host_count, L.ws_perm, o.group_off, o.perm,
+        M.moelb_permute(h, o.idx, cfg.G, home_step, replica_cur, o.host_count, L.ws_perm, o.group_off, o.perm,
                         o.pos, o.x_perm)
         torch.cuda.synchronize()
         src = h[(o.perm.long() // cfg.k)]
@@ -80,7 +92,12 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
             "host_count", "load", "group_off", "perm", "pos", "y", "out"]}
     if o.shared is not None:
         out["shared"] = to_host(o.shared)
-    run = LayerRun(cfg, li, w13, w2, sh, to_host(idx_pred), to_host(replica_cur), out, x_ok)
+    fb = None
+    if balancer == "freebalance":
+        out["home_next"] = to_host(o.home_next)
+        fb = (L.fb_tau, L.fb_gamma[0], L.fb_gamma[1], L.fb_budget)
+    run = LayerRun(cfg, li, w13, w2, sh, to_host(idx_pred), to_host(replica_cur), out, x_ok, balancer,
+                   to_host(home_cur) if home_cur is not None else None, fb)
     del L, W13, W2, h, h_prev
     torch.cuda.empty_cache()
     return run
@@ -136,7 +153,20 @@ def check_integer_stages(run: LayerRun) -> dict:
     assert np.array_equal(g["counts_next"], cn), "histogram (lookahead)"
     cp = O.histogram(run.idx_pred, G, E)
     N = cfg.N
-    if N > 0:
+    home = li.home
+    if run.balancer == "freebalance":
+        from fractions import Fraction
+        from oracle import swap_planner as SP
+        tau, num, den, budget = run.fb
+        home_cur, _, _ = SP.plan_swaps(cp, li.home, G, E, tau=tau, gamma=Fraction(num, den), max_swaps_per_rank=budget)
+        assert np.array_equal(run.home_cur, home_cur), "swap plan (prologue)"
+        home_next, _, pl = SP.plan_swaps(cn, li.home, G, E, tau=tau, gamma=Fraction(num, den),
+                                         max_swaps_per_rank=budget)
+        assert np.array_equal(g["home_next"], home_next), "swap plan (next layer)"
+        assert np.array_equal(g["plan_load_next"], pl), "swap plan loads"
+        home, N = home_cur, 0
+        rep_cur = None
+    elif N > 0:
         rep_cur = O.plan(cp, li.home, G, E, N, cfg.L)
         assert np.array_equal(run.replica_cur[:, :N], rep_cur), ("plan (prologue)", run.replica_cur, rep_cur)
         rep_next, pl = O.plan(cn, li.home, G, E, N, cfg.L, return_loads=True)
@@ -144,10 +174,10 @@ def check_integer_stages(run: LayerRun) -> dict:
         assert np.array_equal(g["plan_load_next"], np.array(pl)), "plan loads"
     else:
         rep_cur = np.full((G, 1), -1, dtype=np.int32)
-    hc, load = O.split(c, li.home, rep_cur if N > 0 else None, G, E, passes=12)
+    hc, load = O.split(c, home, rep_cur if N > 0 else None, G, E, passes=12)
     assert np.array_equal(g["host_count"], hc), "split host_count"
     assert np.array_equal(g["load"], load), "split load"
-    off, perm, pos = O.permute(g["idx"], li.home, rep_cur if N > 0 else None, hc, G, E)
+    off, perm, pos = O.permute(g["idx"], home, rep_cur if N > 0 else None, hc, G, E)
     assert np.array_equal(g["group_off"], off), "permute group_off"
     assert np.array_equal(g["perm"][:len(perm)], perm), "permute perm"
     assert np.array_equal(g["pos"], pos), "permute pos"

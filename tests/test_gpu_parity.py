@@ -113,6 +113,21 @@ def test_two_stage_step_identical_to_one_stage(moelb, name, changes):
     assert np.array_equal(a.out["y"][rows], b.out["y"][rows])
 
 
+@pytest.mark.parametrize("name,changes", [
+    ("c2_qwen3_30b_decode", dict(steps=1, **RAGGED)),
+    ("c4_glm45_prefill", dict(T=2048)),
+    ("c3_qwen3_235b_prefill", dict()),
+])
+def test_freebalance_layer_step(moelb, name, changes):
+    # the same path with FreeBalance's swaps in place of replication: the
+    # prologue and next-layer placements, the identity split, permutation,
+    # FFN and combine against the oracle
+    cfg = W.scaled(W.config(name), **changes)
+    run = _full_check(cfg, tokens=sample_tokens(cfg.T, 24), balancer="freebalance")
+    assert run.home_cur is not None
+    assert np.array_equal(np.bincount(run.home_cur, minlength=cfg.G), np.bincount(run.li.home, minlength=cfg.G))
+
+
 def test_permute_two_phases_equal_one_call(moelb):
     from routed_expert_ffn_gate_amd import moelb as M
     dev = torch.device("cuda")
@@ -291,6 +306,39 @@ def test_split_variants_random_instances(moelb):
             hc_o, ld_o = V.split_variant(c, home, rep, G, E, name, passes=passes, eps=eps)
             assert np.array_equal(hc.cpu().numpy(), hc_o), (trial, name, G, E, N, passes)
             assert np.array_equal(ld.cpu().numpy(), ld_o), (trial, name)
+
+
+def test_swap_planner_random_instances(moelb):
+    """FreeBalance's swap planner against its oracle, bit for bit: placement,
+    swap sequence and loads."""
+    from fractions import Fraction
+    from oracle import swap_planner as SP
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(29)
+    for trial in range(40):
+        G = int(rng.choice([1, 2, 3, 8, 16, 64]))
+        E = min(256, G * int(rng.choice([1, 2, 4, 8])))
+        pop = 1.0 / (1 + rng.permutation(E)) ** rng.uniform(0.3, 1.6)
+        c = np.stack([rng.multinomial(int(rng.integers(0, 20000)), pop / pop.sum()) for _ in range(G)]).astype(np.int32)
+        home = rng.permutation(np.arange(E) // (E // G)).astype(np.int32)
+        if trial % 5 == 0:
+            home[rng.integers(0, E)] = -3  # read as rank 0
+        num, den = int(rng.integers(0, 5)), int(rng.choice([1, 7, 1000, 1 << 20]))
+        tau, budget = int(rng.choice([0, 0, 50])), int(rng.choice([0, 1, 2, 1 << 20]))
+        ct, ht = torch.from_numpy(c).to(dev), torch.from_numpy(home).to(dev)
+        ho = torch.empty(E, dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        sw = torch.full((E // 2 + 1, 2), -1, dtype=torch.int32, device=dev)
+        ns = torch.empty(1, dtype=torch.int32, device=dev)
+        M.moelb_plan_swaps(ct, ht, ho, ld, tau=tau, gamma=(num, den), max_swaps_per_rank=budget, swaps=sw, n_swaps=ns)
+        where, swaps, load = SP.plan_swaps(c, home, G, E, tau=tau, gamma=Fraction(num, den),
+                                           max_swaps_per_rank=budget)
+        assert np.array_equal(ho.cpu().numpy(), where), trial
+        assert np.array_equal(ld.cpu().numpy(), load), trial
+        k = int(ns.item())
+        assert k == len(swaps), trial
+        assert [tuple(r) for r in sw.cpu().numpy()[:k].tolist()] == swaps, trial
 
 
 def test_split_heavily_replicated_home(moelb):
