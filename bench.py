@@ -224,7 +224,7 @@ def main():
         summarize_pmc(args.workload, *args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("this build measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
+        print("bench.py measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
