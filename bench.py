@@ -217,6 +217,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter_collection.csv files")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--studies", action="store_true",
+                    help="also measure the two-stage step, the split variants and FreeBalance's swaps "
+                         "(reported beside the headline; their kernels then share the profile)")
     ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
                     help="gate/up GEMM reads h rows through the permutation, or a copied x_perm")
     args = ap.parse_args()
@@ -293,10 +296,13 @@ def main():
     permute_rows_ms = pe.elapsed_ms(0, 1) / reps
 
     balance = routing_stats(cfg, layer, idx_pred, home)
-    two_stage = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K, stream, cfg.T)
-    split_variants = time_split_variants(layer, home, replica_cur, stream)
-    freebalance = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K, args.warmup, stream,
-                                   gather_rows=args.rows == "gather")
+    studies = {}
+    if args.studies:
+        studies["two_stage"] = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K,
+                                              stream, cfg.T)
+        studies["split_variants"] = time_split_variants(layer, home, replica_cur, stream)
+        studies["freebalance"] = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K,
+                                                  args.warmup, stream, gather_rows=args.rows == "gather")
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
@@ -339,9 +345,7 @@ def main():
         "stages_ms": {k_: round(v, 4) for k_, v in {**stage, **sub, "permute_rows": permute_rows_ms}.items()},
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
         "routing": balance,
-        "two_stage": two_stage,
-        "split_variants": split_variants,
-        "freebalance": freebalance,
+        **studies,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
                                ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                                4),
