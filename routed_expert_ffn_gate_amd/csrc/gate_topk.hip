@@ -86,10 +86,11 @@ __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int
 #pragma unroll
   for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(l[i] & 0xffu), E - 1);  // unused entries stay in the row
   if (dir == 0) {
-    // softmax denominator over all E logits of this token
+    // softmax denominator over all E logits of this token (no weights wanted:
+    // a lookahead-only block of the split launch)
     const float mx = active ? row[li[0]] : 0.f;
     float s = 0.f;
-    if (active)
+    if (active && wts)
       for (int e = sub; e < E; e += lpt) s += __expf(row[e] - mx);
     for (int m = 1; m < lpt; m <<= 1) s += __shfl_xor(s, m, MOELB_WAVE);
     if (active && sub == 0 && t < T) {
@@ -98,7 +99,7 @@ __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int
       for (int j = 0; j < KL; ++j) {
         if (j < k) {
           idx[(size_t)t * k + j] = li[j];
-          wts[(size_t)t * k + j] = __expf(row[li[j]] - mx) * inv;
+          if (wts) wts[(size_t)t * k + j] = __expf(row[li[j]] - mx) * inv;
         }
       }
       if (gap) {
@@ -269,12 +270,27 @@ __device__ __forceinline__ void gt_copy16(uint32_t voff, const void* sbase, uint
 }
 #pragma clang diagnostic pop
 
+// Split launch (gridDim.y == 2, for few token blocks): the blocks with y = 0
+// run the current router alone and the blocks with y = 1 the lookahead router
+// alone (its top-k indices only), so twice as many workgroups each read half
+// the router rows; N = 64 * NF then covers E columns (padding columns read row
+// 0 and are never selected).
 template <int NF, int KL, int S>
 __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
-    const uint16_t* __restrict__ h, int T, int d, int E, int k, const uint16_t* __restrict__ w_cur,
-    const float* __restrict__ b_cur, const uint16_t* __restrict__ w_next, const float* __restrict__ b_next,
-    int32_t* __restrict__ idx, float* __restrict__ wts, float* __restrict__ gap, int32_t* __restrict__ idx_next,
-    int zstride) {
+    const uint16_t* __restrict__ h, int T, int d, int E, int k, const uint16_t* __restrict__ w_cur_in,
+    const float* __restrict__ b_cur_in, const uint16_t* __restrict__ w_next_in, const float* __restrict__ b_next_in,
+    int32_t* __restrict__ idx_in, float* __restrict__ wts_in, float* __restrict__ gap_in,
+    int32_t* __restrict__ idx_next_in, int zstride) {
+  const bool split = gridDim.y == 2;
+  const bool look = split && blockIdx.y == 1;
+  const uint16_t* w_cur = look ? w_next_in : w_cur_in;
+  const float* b_cur = look ? b_next_in : b_cur_in;
+  const uint16_t* w_next = split ? nullptr : w_next_in;
+  const float* b_next = split ? nullptr : b_next_in;
+  int32_t* idx = look ? idx_next_in : idx_in;
+  float* wts = look ? nullptr : wts_in;
+  float* gap = look ? nullptr : gap_in;
+  int32_t* idx_next = split ? nullptr : idx_next_in;
   constexpr int BK = 64;
   constexpr int N = 64 * NF;
   constexpr int STAGE = (GATE_BM + N) * BK;  // elements: A rows, then B rows
@@ -306,7 +322,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int r = (wave * NF + j) * 8 + (lane >> 3);
-    boff[j] = ((uint32_t)(r < E ? r : r - E) * (uint32_t)d + gt_slot(r, lane & 7) * 8) * 2u;
+    boff[j] = ((uint32_t)(r < E ? r : min(r - E, E - 1)) * (uint32_t)d + gt_slot(r, lane & 7) * 8) * 2u;
   }
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
                 st_ + (uint32_t)((wave_s * 2 + ((U) & 1)) * 8 * BK) * 2u);                         \
     } else {                                                                                       \
       const int jb_ = (U) >= 2 ? (U) - 2 : 0;                                                      \
-      const uint16_t* m_ = (wave_s * NF + jb_) * 8 < E ? w_cur : w_next;                           \
+      const uint16_t* m_ = (w_next == nullptr || (wave_s * NF + jb_) * 8 < E) ? w_cur : w_next;      \
       gt_copy16(boff[jb_], m_ + (size_t)kti_ * BK,                                                 \
                 st_ + (uint32_t)((GATE_BM + (wave_s * NF + jb_) * 8) * BK) * 2u);                  \
     }                                                                                              \
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
 #pragma unroll
   for (int ni = 0; ni < NF; ++ni) {
     const int col = wn * NF * 16 + ni * 16 + (lane & 15);
-    bias[ni] = col < E ? b_cur[col] : b_next[col - E];
+    bias[ni] = col < E ? b_cur[col] : (b_next ? b_next[col - E] : 0.f);
   }
   // scalar loads still in flight would turn every LDS wait of the loop into a full drain
   asm volatile("" ::"s"(idx), "s"(wts), "s"(idx_next), "s"(gap));
@@ -499,6 +515,14 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_f32_kernel(
 
 int zstride_for(int N) { return ((N + 63) / 64) * 64 + 4; }
 
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return cus;
+}
+
 template <int KL>
 int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
                 const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap,
@@ -537,14 +561,16 @@ int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w
 
 template <int NF, int KL, int S>
 int launch_dma_nf(const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur, const void* w_next,
-                  const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next, hipStream_t s) {
+                  const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next, bool split,
+                  hipStream_t s) {
   const int N = 64 * NF;
   const int zs = zstride_for(N);
   const size_t lds_main = (size_t)S * (GATE_BM + N) * 64 * 2;
   const size_t lds_z = 64ull * zs * 4;
   const size_t lds = lds_main > lds_z ? lds_main : lds_z;
   if (!moelb_allow_lds(gate_topk_dma_kernel<NF, KL, S>, lds)) return MOELB_ELAUNCH;
-  hipLaunchKernelGGL((gate_topk_dma_kernel<NF, KL, S>), dim3((T + GATE_BM - 1) / GATE_BM), dim3(GATE_THREADS), lds, s,
+  hipLaunchKernelGGL((gate_topk_dma_kernel<NF, KL, S>), dim3((T + GATE_BM - 1) / GATE_BM, split ? 2 : 1),
+                     dim3(GATE_THREADS), lds, s,
                      static_cast<const uint16_t*>(h), T, d, E, k, static_cast<const uint16_t*>(w_cur), b_cur,
                      static_cast<const uint16_t*>(w_next), b_next, idx, wts, gap, idx_next, zs);
   MOELB_CHECK_LAUNCH();
@@ -555,15 +581,15 @@ int launch_dma_nf(const void* h, int T, int d, int E, int k, const void* w_cur, 
 template <int KL>
 int launch_dma(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
                const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next,
-               hipStream_t s) {
+               bool split, hipStream_t s) {
   switch (NF) {
-    case 1: return launch_dma_nf<1, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 2: return launch_dma_nf<2, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 3: return launch_dma_nf<3, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 4: return launch_dma_nf<4, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 5: return launch_dma_nf<5, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 6: return launch_dma_nf<6, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    case 7: return launch_dma_nf<7, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    case 1: return launch_dma_nf<1, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 2: return launch_dma_nf<2, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 3: return launch_dma_nf<3, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 4: return launch_dma_nf<4, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 5: return launch_dma_nf<5, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 6: return launch_dma_nf<6, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 7: return launch_dma_nf<7, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
     default: return MOELB_EINVAL;
   }
 }
@@ -601,11 +627,20 @@ extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dt
   if (dtype == MOELB_BF16) {
     const int N = w_next ? 2 * E : E;
     const int NF = (N + 63) / 64;
-    if (N % 64 == 0 && NF <= (k <= 8 ? 7 : 6) && d % 64 == 0 && (size_t)T * d * 2 < (1ull << 32)) {
-      if (k <= 2) return launch_dma<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-      if (k <= 4) return launch_dma<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-      if (k <= 8) return launch_dma<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-      return launch_dma<17>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    const int nfmax = k <= 8 ? 7 : 6;
+    const bool dma_ok = d % 64 == 0 && (size_t)T * d * 2 < (1ull << 32);
+    // few token blocks: one workgroup per router and block (twice the
+    // workgroups, each reading half the router rows)
+    const int blocks = (T + GATE_BM - 1) / GATE_BM;
+    const int NFs = (E + 63) / 64;
+    const bool split = w_next && dma_ok && NFs <= nfmax && 2 * blocks <= compute_units();
+    const bool fused = dma_ok && N % 64 == 0 && NF <= nfmax;
+    if (split || fused) {
+      const int nf = split ? NFs : NF;
+      if (k <= 2) return launch_dma<3>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 4) return launch_dma<5>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 8) return launch_dma<9>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      return launch_dma<17>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
     }
     if (k <= 2) return launch_bf16<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
     if (k <= 4) return launch_bf16<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
