@@ -6,7 +6,9 @@
 // host chosen by the per-step split (Relief, "The Relief Algorithm").
 //
 // Deterministic stable counting sort in four launches:
-//   1. count: one workgroup per chunk of CHUNK tokens (chunks never straddle a
+//   1. count: one workgroup per chunk of up to MAX_CHUNK tokens (chunk_tokens()
+//      shrinks it for small batches so the ranking runs on more workgroups
+//      with shorter serial loops; chunks never straddle a
 //      rank), LDS histogram of the chunk's experts;
 //   2. scan: one workgroup per expert scans its chunk counts in token order,
 //      giving each chunk's base rank inside its local group (reset per rank)
@@ -29,7 +31,16 @@
 
 namespace {
 
-constexpr int CHUNK = 128;
+constexpr int MAX_CHUNK = 128;
+
+// Tokens per chunk: enough chunks (about 256) to spread the ranking over the
+// GPU, between 16 and MAX_CHUNK tokens.
+inline int chunk_tokens(int T, int G) {
+  const int per = T / G;
+  const int want = (256 + G - 1) / G;  // chunks per rank
+  const int c = (per + want - 1) / want;
+  return c < 16 ? 16 : (c > MAX_CHUNK ? MAX_CHUNK : c);
+}
 constexpr int SCAN_THREADS = 1024;
 
 struct PermuteWs {
@@ -45,7 +56,8 @@ struct PermuteWs {
 
 inline size_t ws_layout(int T, int k, int E, int G, PermuteWs* w, char* base) {
   const int per = T / G;
-  const int nchr = (per + CHUNK - 1) / CHUNK;
+  const int chunk = chunk_tokens(T, G);
+  const int nchr = (per + chunk - 1) / chunk;
   const size_t nchunks = (size_t)G * (nchr > 0 ? nchr : 1);
   size_t off = 0;
   auto take = [&](int32_t** p, size_t n) {
@@ -76,13 +88,13 @@ __device__ __forceinline__ uint64_t host_mask(const int32_t* home, const int32_t
 }
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int T, int k, int E, int G,
-                                                    int nchr, int32_t* __restrict__ chunk_counts) {
+                                                    int chunk, int nchr, int32_t* __restrict__ chunk_counts) {
   __shared__ int bins[MOELB_MAX_E];
   const int c = blockIdx.x;
   const int s = c / nchr, ci = c % nchr;
   const int per = T / G;
-  const int t0 = s * per + ci * CHUNK;
-  const int t1 = min(t0 + CHUNK, (s + 1) * per);
+  const int t0 = s * per + ci * chunk;
+  const int t1 = min(t0 + chunk, (s + 1) * per);
   for (int e = threadIdx.x; e < E; e += blockDim.x) bins[e] = 0;
   __syncthreads();
   const int np = max(0, t1 - t0) * k;
@@ -242,7 +254,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void group_scan_kernel(const int32_t*
 // copy for them yet.
 template <typename T, bool LOCAL_ONLY>
 __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__ h, const int32_t* __restrict__ idx,
-                                                           int Ttok, int d, int k, int E, int G, int N, int nchr,
+                                                           int Ttok, int d, int k, int E, int G, int N, int chunk,
+                                                           int nchr,
                                                            const int32_t* __restrict__ home,
                                                            const int32_t* __restrict__ replica, PermuteWs ws,
                                                            const int32_t* __restrict__ group_off,
@@ -250,12 +263,12 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
                                                            T* __restrict__ x_perm) {
   __shared__ int cnt[MOELB_MAX_E];
   __shared__ uint64_t hmask[MOELB_MAX_E];
-  __shared__ int qpos[CHUNK * MOELB_MAX_K];
+  __shared__ int qpos[MAX_CHUNK * MOELB_MAX_K];
   const int c = blockIdx.x;
   const int s = c / nchr, ci = c % nchr;
   const int per = Ttok / G;
-  const int t0 = s * per + ci * CHUNK;
-  const int t1 = min(t0 + CHUNK, (s + 1) * per);
+  const int t0 = s * per + ci * chunk;
+  const int t1 = min(t0 + chunk, (s + 1) * per);
   const int ntok = max(0, t1 - t0);
   const int np = ntok * k;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -401,10 +414,11 @@ static int permute_launch(bool local_only, const void* h, const int32_t* idx, in
   PermuteWs w;
   ws_layout(T, k, E, G, &w, static_cast<char*>(ws));
   const int per = T / G;
-  const int nchr = per > 0 ? (per + CHUNK - 1) / CHUNK : 1;
+  const int chunk = chunk_tokens(T, G);
+  const int nchr = per > 0 ? (per + chunk - 1) / chunk : 1;
   const int nchunks = G * nchr;
   const int32_t* rep = N > 0 ? replica : home;
-  hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(256), 0, s, idx, T, k, E, G, nchr, w.chunk_counts);
+  hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(256), 0, s, idx, T, k, E, G, chunk, nchr, w.chunk_counts);
   MOELB_CHECK_LAUNCH();
   hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(ESCAN_THREADS), 0, s, home, rep,
                      local_only ? nullptr : host_count, E, G, N, nchr, w);
@@ -414,7 +428,7 @@ static int permute_launch(bool local_only, const void* h, const int32_t* idx, in
   MOELB_CHECK_LAUNCH();
 #define PERMUTE_SCATTER(TY, LO)                                                                                  \
   hipLaunchKernelGGL((rank_scatter_kernel<TY, LO>), dim3(nchunks), dim3(256), 0, s, static_cast<const TY*>(h), \
-                     idx, T, d, k, E, G, N, nchr, home, rep, w, group_off, perm, pos, static_cast<TY*>(x_perm))
+                     idx, T, d, k, E, G, N, chunk, nchr, home, rep, w, group_off, perm, pos, static_cast<TY*>(x_perm))
   if (dtype == MOELB_BF16) {
     if (local_only) PERMUTE_SCATTER(uint16_t, true); else PERMUTE_SCATTER(uint16_t, false);
   } else {
