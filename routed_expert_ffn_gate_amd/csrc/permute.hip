@@ -33,11 +33,11 @@ namespace {
 
 constexpr int MAX_CHUNK = 128;
 
-// Tokens per chunk: enough chunks (about 256) to spread the ranking over the
+// Tokens per chunk: enough chunks (about 1024) to spread the ranking over the
 // GPU, between 16 and MAX_CHUNK tokens.
 inline int chunk_tokens(int T, int G) {
   const int per = T / G;
-  const int want = (256 + G - 1) / G;  // chunks per rank
+  const int want = (1024 + G - 1) / G;  // chunks per rank
   const int c = (per + want - 1) / want;
   return c < 16 ? 16 : (c > MAX_CHUNK ? MAX_CHUNK : c);
 }
