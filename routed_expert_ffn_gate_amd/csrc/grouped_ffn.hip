@@ -91,71 +91,108 @@ inline size_t sched_layout(int rows, int num_groups, int E, int inter, int dtype
 
 // ---------------------------------------------------------------- schedule
 
+// Expert-major virtual row order: every selected group of expert e gets a
+// contiguous range inside e's range [eoff[e], eoff[e+1]); M tiles of BM rows
+// never straddle experts.  One workgroup; the group offsets are staged
+// through LDS in chunks (two passes: sizes per expert, then each group's
+// start), so no thread waits on a chain of global loads.
+constexpr int SCHED_CHUNK = 4096;
+
 __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ group_off, int num_groups, int E, int G,
                                                     int rank, int rows, int BM, FfnSched s) {
+  __shared__ int goff[SCHED_CHUNK + 1];
   __shared__ int ecount[MOELB_MAX_E];
   __shared__ int eoff[MOELB_MAX_E + 1];
   __shared__ int toff[MOELB_MAX_E + 1];
-  const int e = threadIdx.x;
-  if (e < E) {
-    int n = 0;
-    for (int g = e; g < num_groups; g += E) {
-      const bool sel = rank < 0 || ((g / E) % G) == rank;
-      const int lo = min(max(group_off[g], 0), rows);
-      const int hi = min(max(group_off[g + 1], lo), rows);
-      s.gvb[g] = sel ? n : -1;
-      if (sel) n += hi - lo;
+  const int tid = threadIdx.x;
+  const int e = tid;
+  // walk the selected groups of expert e, chunk by chunk: add each group's
+  // size to run, and (write) record the group's start first
+  auto walk = [&](bool write, int& run) {
+    for (int base = 0; base < num_groups; base += SCHED_CHUNK) {
+      const int cnt = min(SCHED_CHUNK, num_groups - base);
+      __syncthreads();
+      for (int i = tid; i <= cnt; i += blockDim.x) goff[i] = group_off[base + i];
+      __syncthreads();
+      if (e < E) {
+        for (int g = base + (e - base % E + E) % E; g < base + cnt; g += E) {
+          const bool sel = rank < 0 || ((g / E) % G) == rank;
+          const int lo = min(max(goff[g - base], 0), rows);
+          const int hi = min(max(goff[g - base + 1], lo), rows);
+          if (write) s.gvb[g] = sel ? run : -1;
+          if (sel) run += hi - lo;
+        }
+      }
     }
-    ecount[e] = n;
+  };
+  int n = 0;
+  walk(false, n);
+  // expert offsets (clamped to rows) and M-tile offsets: two block scans
+  // (Hillis-Steele over the 256 threads, one per expert)
+  auto scan = [&](long long v) {  // inclusive prefix of v over threads
+    __shared__ long long part[256];
+    part[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const long long add = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    return part[tid];
+  };
+  const long long incl = scan(e < E ? n : 0);
+  const int lo_row = (int)min(incl - (e < E ? n : 0), (long long)rows);
+  const int hi_row = (int)min(incl, (long long)rows);
+  const int ntile = e < E ? (hi_row - lo_row + BM - 1) / BM : 0;
+  const long long tincl = scan(ntile);
+  if (e < E) {
+    eoff[e] = lo_row;
+    toff[e] = (int)(tincl - ntile);
+  }
+  if (e == E - 1) {
+    eoff[E] = hi_row;
+    toff[E] = (int)tincl;
+    *s.n_mtiles = (int)tincl;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    long long run = 0;
-    int trun = 0;
-    for (int x = 0; x < E; ++x) {
-      eoff[x] = (int)min(run, (long long)rows);
-      toff[x] = trun;
-      run += ecount[x];
-      const int nx = (int)min(run, (long long)rows) - eoff[x];
-      trun += (nx + BM - 1) / BM;
-    }
-    eoff[E] = (int)min(run, (long long)rows);
-    toff[E] = trun;
-    *s.n_mtiles = trun;
-  }
-  __syncthreads();
-  if (e < E) s.eoff[e] = eoff[e];
-  if (e == 0) s.eoff[E] = eoff[E];
+  int start = e < E ? eoff[e] : 0;
+  walk(true, start);
   if (e < E) {
-    for (int g = e; g < num_groups; g += E)
-      if (s.gvb[g] >= 0) s.gvb[g] += eoff[e];
+    s.eoff[e] = eoff[e];
     for (int i = toff[e]; i < toff[e + 1]; ++i) {
       s.mt_e[i] = e;
       s.mt_v0[i] = eoff[e] + (i - toff[e]) * BM;
     }
   }
+  if (e == 0) s.eoff[E] = eoff[E];
 }
 
 // Virtual -> physical row map, and the row of x each virtual row reads (through
 // the gather, when the rows come straight from the unpermuted hidden states).
-__global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__ group_off, int E, int rows,
-                                                     const int32_t* __restrict__ gather, int gather_k, int rows_x,
-                                                     FfnSched s) {
-  const int g = blockIdx.x;
+// One thread per physical row q: its group by binary search over group_off.
+__global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__ group_off, int num_groups, int E,
+                                                     int rows, const int32_t* __restrict__ gather, int gather_k,
+                                                     int rows_x, FfnSched s) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= rows) return;
+  // last group g with clamp(group_off[g]) <= q (clamped offsets are non-decreasing)
+  int lo = 0, hi = num_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (min(max(group_off[mid], 0), rows) <= q) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int glo = min(max(group_off[g], 0), rows);
+  const int ghi = min(max(group_off[g + 1], glo), rows);
+  if (q < glo || q >= ghi) return;  // in no group (or an empty one)
   const int vb = s.gvb[g];
   if (vb < 0) return;
-  const int e = g % E;
-  const int vend = s.eoff[e + 1];
-  const int lo = min(max(group_off[g], 0), rows);
-  const int hi = min(max(group_off[g + 1], lo), rows);
-  for (int q = lo + threadIdx.x; q < hi; q += blockDim.x) {
-    const int v = vb + (q - lo);
-    if (v < vend) {
-      s.rowmap[v] = q;
-      const int src = gather ? gather[q] / gather_k : q;
-      s.asrc[v] = (src >= 0 && src < rows_x) ? src : 0;
-    }
-  }
+  const int v = vb + (q - glo);
+  if (v >= s.eoff[g % E + 1]) return;
+  s.rowmap[v] = q;
+  const int src = gather ? gather[q] / gather_k : q;
+  s.asrc[v] = (src >= 0 && src < rows_x) ? src : 0;
 }
 
 // XCD-aware tile id: workgroups go round-robin over 8 XCDs; give each XCD a
@@ -1041,8 +1078,9 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows, BM,
                      sc);
   MOELB_CHECK_LAUNCH();
-  hipLaunchKernelGGL(rowmap_kernel, dim3(num_groups), dim3(256), 0, s, group_off, E, rows, gather, gather_k, rows_x,
-                     sc);
+  if (rows > 0)
+    hipLaunchKernelGGL(rowmap_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, group_off, num_groups, E, rows, gather,
+                       gather_k, rows_x, sc);
   MOELB_CHECK_LAUNCH();
   const size_t mtiles = (size_t)(rows + BM - 1) / BM + E;
   if (bf) {
