@@ -25,6 +25,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no packed-fp32 instructions (v_pk_*_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics on one address from many lanes: combine the lanes with DPP
+    # (a few cross-lane steps) rather than a loop over the active lanes
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",
     "-I", os.path.join(ROOT, "include"),
 ]
 COMPILE_TIMEOUT = 900

@@ -483,24 +483,32 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   if (rs1 >= 0 && rs1 < E) atomicOr(&hostmask[rs1], 1ull << ((tid + SPLIT_THREADS) / N));
   __syncthreads();
 
-  // fixed loads, initial even split, unreplicated pools
+  // fixed loads, initial even split, unreplicated pools.  Counts are loaded 8
+  // ranks at a time (independent loads in flight together).
   uint64_t mask = 0;
   int R = 0, m = 0;
   if (e < E) {
     mask = hostmask[e];
     m = __popcll(mask);
-    for (int s2 = 0; s2 < G; ++s2) {
-      const int cs = counts[(size_t)s2 * E + e];
-      if ((mask >> s2) & 1ull)
-        atomicAdd(&load[s2], cs);
-      else
-        R += cs;
+  }
+  for (int s0 = 0; s0 < G; s0 += 8) {
+    int cs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cs[i] = (e < E && s0 + i < G) ? counts[(size_t)(s0 + i) * E + e] : 0;
+    if (e < E) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (s0 + i >= G) break;
+        if ((mask >> (s0 + i)) & 1ull)
+          atomicAdd(&load[s0 + i], cs[i]);
+        else
+          R += cs[i];
+      }
     }
+  }
+  if (e < E) {
     for (int r = 0; r < G; ++r) host_count[(size_t)e * G + r] = 0;
-    if (m == 1) {
-      atomicAdd(&load[my_home], R);
-      host_count[(size_t)e * G + my_home] = R;
-    }
+    if (m == 1) host_count[(size_t)e * G + my_home] = R;  // its load is added with the shares below
   }
   // transfer list: (home(e), v, e) for e ascending, v ascending; offsets by a block scan
   {
@@ -519,23 +527,29 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
     if (tid == SPLIT_THREADS - 1) toff[E] = base + incl;  // E <= SPLIT_THREADS
   }
   __syncthreads();
-  if (e < E && m > 1) {
-    int t = toff[e], pos = 0;
+  {
+    // shares of the pools (even split, or for the greedy the whole pool on the
+    // home; an unreplicated pool all at its home), summed over the wave per rank
+    const bool repl = e < E && m > 1;
+    int t = repl ? toff[e] : 0, pos = 0;
     for (int r = 0; r < G; ++r) {
-      if (!((mask >> r) & 1ull)) continue;
-      // even split, or (greedy) the whole pool on the home
-      const int share = greedy ? (r == my_home ? R : 0) : even_share(R, m, pos);
-      ++pos;
-      atomicAdd(&load[r], share);
-      if (r == my_home) {
-        xhome[e] = share;
-      } else {
-        t_u[t] = my_home;
-        t_v[t] = r;
-        t_e[t] = e;
-        t_x[t] = share;
-        ++t;
+      int share = 0;
+      if (repl && ((mask >> r) & 1ull)) {
+        share = greedy ? (r == my_home ? R : 0) : even_share(R, m, pos);
+        ++pos;
+        if (r == my_home) {
+          xhome[e] = share;
+        } else {
+          t_u[t] = my_home;
+          t_v[t] = r;
+          t_e[t] = e;
+          t_x[t] = share;
+          ++t;
+        }
+      } else if (e < E && m == 1 && r == my_home) {
+        share = R;
       }
+      if (share != 0) atomicAdd(&load[r], share);
     }
   }
   const int n = toff[E];
