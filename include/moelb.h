@@ -205,6 +205,24 @@ int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int G, int E, i
  * Same arguments, outputs and requirements as moelb_split; counts must be
  * non-negative.  An unknown variant returns MOELB_EINVAL.
  */
+/*
+ * Round schedule of the split (Relief, "The Relief Algorithm": the edge
+ * colouring depends on the placement only and is computed once per placement
+ * change, not per step).  moelb_split_schedule writes, for home/replica, the
+ * transfer list and its greedy colouring into `schedule` (MOELB_SPLIT_SCHEDULE_INTS
+ * int32: n, number of colours, then (u, v, colour) per transfer).
+ * moelb_split_scheduled is moelb_split_variant with such a schedule: if it
+ * lists exactly this placement's transfers, the split uses its colours (the
+ * same ones it would compute); otherwise (or with schedule = NULL) it colours
+ * the transfers itself.  Outputs are identical either way.
+ */
+#define MOELB_SPLIT_SCHEDULE_INTS (2 + 3 * MOELB_MAX_G * MOELB_MAX_N)
+int moelb_split_schedule(const int32_t* home, const int32_t* replica, int G, int E, int N,
+                         int32_t* schedule, void* stream);
+int moelb_split_scheduled(const int32_t* counts, const int32_t* home, const int32_t* replica,
+                          const int32_t* schedule, int G, int E, int N, int passes, int eps,
+                          int variant, int32_t* host_count, int32_t* load, void* stream);
+
 enum moelb_split_variant {
   MOELB_SPLIT_RELIEF = 0,
   MOELB_SPLIT_NO_REVERSE = 1,

@@ -449,6 +449,8 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
                                                                const int32_t* __restrict__ home,
                                                                const int32_t* __restrict__ replica, int G, int E,
                                                                int N, int passes, int eps, int variant,
+                                                               const int32_t* __restrict__ sched_in,
+                                                               int32_t* __restrict__ sched_out,
                                                                int32_t* __restrict__ host_count,
                                                                int32_t* __restrict__ load_out) {
   __shared__ unsigned long long hostmask[MOELB_MAX_E];
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   for (int s0 = 0; s0 < G; s0 += 8) {
     int cs[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cs[i] = (e < E && s0 + i < G) ? counts[(size_t)(s0 + i) * E + e] : 0;
+    for (int i = 0; i < 8; ++i) cs[i] = (counts && e < E && s0 + i < G) ? counts[(size_t)(s0 + i) * E + e] : 0;
     if (e < E) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
       }
     }
   }
-  if (e < E) {
+  if (e < E && host_count) {
     for (int r = 0; r < G; ++r) host_count[(size_t)e * G + r] = 0;
     if (m == 1) host_count[(size_t)e * G + my_home] = R;  // its load is added with the shares below
   }
@@ -630,13 +632,32 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
     return;
   }
 
-  // One wave from here.  Greedy edge colouring in list order.  Fast path: lane
-  // r holds rank r's used colours below 64 in a register; if some transfer
-  // finds none free, the colouring is redone with LDS words (1024 colours).
+  // One wave from here.  The round schedule depends on the placement only: a
+  // schedule from moelb_split_schedule for this same transfer list is used as
+  // it is (checked transfer by transfer); otherwise greedy edge colouring in
+  // list order.  Fast path: lane r holds rank r's used colours below 64 in a
+  // register; if some transfer finds none free, the colouring is redone with
+  // LDS words (1024 colours).
   int my_col[TR_PER_LANE];
+#pragma unroll
+  for (int q = 0; q < TR_PER_LANE; ++q) my_col[q] = 0;
   int ncol = 0;
   bool wide = false;
-  {
+  bool scheduled = false;
+  if (sched_in && sched_in[0] == n && sched_in[1] >= 0 && sched_in[1] <= n) {
+    bool diff = false;
+    for (int t = lane; t < n; t += 64)
+      diff |= sched_in[2 + 3 * t] != t_u[t] || sched_in[3 + 3 * t] != t_v[t] || sched_in[4 + 3 * t] < 0 ||
+              sched_in[4 + 3 * t] >= sched_in[1];
+    scheduled = __ballot(diff) == 0ull;
+    if (scheduled) {
+      ncol = sched_in[1];
+#pragma unroll
+      for (int q = 0; q < TR_PER_LANE; ++q)
+        if (lane + 64 * q < n) my_col[q] = sched_in[4 + 3 * (lane + 64 * q)];
+    }
+  }
+  if (!scheduled) {
     uint32_t used_lo = 0u, used_hi = 0u;  // rank `lane`'s used colours 0..63
     const int my_u = lane < n ? t_u[lane] : 0, my_v = lane < n ? t_v[lane] : 0;
     for (int t = 0; t < n; ++t) {
@@ -670,7 +691,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
       ncol = max(ncol, col + 1);
     }
   }
-  if (wide) {
+  if (!scheduled && wide) {
     ncol = 0;
     for (int t = 0; t < n; ++t) {
       const int u = t_u[t], v = t_v[t];
@@ -687,6 +708,23 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
         if (t == lane + 64 * q) my_col[q] = col;
       ncol = max(ncol, col + 1);
     }
+  }
+  if (sched_out) {
+    // schedule only: the transfer list and its colours, nothing else
+    if (lane == 0) {
+      sched_out[0] = n;
+      sched_out[1] = ncol;
+    }
+#pragma unroll
+    for (int q = 0; q < TR_PER_LANE; ++q) {
+      const int t = lane + 64 * q;
+      if (t < n) {
+        sched_out[2 + 3 * t] = t_u[t];
+        sched_out[3 + 3 * t] = t_v[t];
+        sched_out[4 + 3 * t] = my_col[q];
+      }
+    }
+    return;
   }
   // relaxation: passes x rounds; the transfers of a round touch disjoint
   // ranks (and experts), and one wave applies them in order with its own LDS
@@ -805,16 +843,34 @@ extern "C" int moelb_plan(const int32_t* counts, const int32_t* home, int G, int
   return MOELB_OK;
 }
 
-extern "C" int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica, int G,
-                                   int E, int N, int passes, int eps, int variant, int32_t* host_count,
-                                   int32_t* load, void* stream) {
+extern "C" int moelb_split_scheduled(const int32_t* counts, const int32_t* home, const int32_t* replica,
+                                     const int32_t* schedule, int G, int E, int N, int passes, int eps, int variant,
+                                     int32_t* host_count, int32_t* load, void* stream) {
   if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
   if (passes < 0 || passes > 1024 || eps < 0) return MOELB_EINVAL;
   if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_LIBRA_GREEDY) return MOELB_EINVAL;
   if (!counts || !home || (N > 0 && !replica) || !host_count || !load) return MOELB_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(split_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home, N > 0 ? replica : home, G, E,
-                     N, passes, eps, variant, host_count, load);
+                     N, passes, eps, variant, schedule, nullptr, host_count, load);
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+extern "C" int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica, int G,
+                                   int E, int N, int passes, int eps, int variant, int32_t* host_count,
+                                   int32_t* load, void* stream) {
+  return moelb_split_scheduled(counts, home, replica, nullptr, G, E, N, passes, eps, variant, host_count, load,
+                               stream);
+}
+
+extern "C" int moelb_split_schedule(const int32_t* home, const int32_t* replica, int G, int E, int N,
+                                    int32_t* schedule, void* stream) {
+  if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
+  if (!home || (N > 0 && !replica) || !schedule) return MOELB_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(split_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, nullptr, home, N > 0 ? replica : home, G, E,
+                     N, 0, 0, (int)MOELB_SPLIT_RELIEF, nullptr, schedule, nullptr, nullptr);
   MOELB_CHECK_LAUNCH();
   return MOELB_OK;
 }

@@ -161,6 +161,10 @@ class MoELayer:
         self.ev_hist = torch.cuda.Event()
         self.ev_local = torch.cuda.Event()
         self.ev_remote = torch.cuda.Event()
+        # round schedules of the split, made once per placement (Relief): for
+        # the placement in force and for the next layer's
+        self.sched_cur = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, **i32)
+        self.sched_next = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, **i32)
         if balancer == "freebalance":
             self.home_next = torch.empty((E,), **i32)
             self.swaps_next = torch.empty((E // 2 + 1, 2), **i32)
@@ -179,6 +183,7 @@ class MoELayer:
         M.moelb_gate_topk(h_prev, w_cur, b_cur, None, None, self.idx_next, self.wts, None, None, stream=stream)
         M.moelb_histogram(self.idx_next, self.G, self.counts_next, stream=stream)
         M.moelb_plan(self.counts_next, home, self.L, replica_out, None, stream=stream)
+        M.moelb_split_schedule(home, replica_out, self.sched_cur, self.G, stream=stream)
 
     def predict_placement(self, h_prev, w_cur, b_cur, home_base, home_out, stream=None):
         """FreeBalance prologue: the early router (this layer's gate on the
@@ -201,6 +206,7 @@ class MoELayer:
             self._plan_swaps(self.home_next, self.side)
         else:
             M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
+            M.moelb_split_schedule(home, self.replica_next, self.sched_next, self.G, stream=self.side)
 
     def _out(self):
         return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
@@ -234,7 +240,8 @@ class MoELayer:
         mark(1)
         M.moelb_histogram(self.idx, self.G, self.counts, stream=s0)
         mark(2)
-        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes, stream=s0)
+        M.moelb_split_scheduled(self.counts, home, replica_cur, self.sched_cur, self.host_count, self.load,
+                                passes=self.passes, stream=s0)
         mark(3)
         copy_rows = not self.gather_rows  # the gather GEMM reads h through perm instead
         M.moelb_permute(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
@@ -303,8 +310,8 @@ class MoELayer:
         # split stream: the split needs only the counts
         self.side2.wait_event(self.ev_hist)
         mark(9, self.side2)
-        M.moelb_split(self.counts, home, replica_cur, self.host_count, self.load, passes=self.passes,
-                      stream=self.side2)
+        M.moelb_split_scheduled(self.counts, home, replica_cur, self.sched_cur, self.host_count, self.load,
+                                passes=self.passes, stream=self.side2)
         mark(10, self.side2)
         M.moelb_permute_local(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.ws_perm,
                               self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None, d=self.d,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "moelb_plan": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split_variant": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moelb_split_schedule": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "moelb_split_scheduled": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_plan_swaps": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moelb_permute_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moelb_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
@@ -132,6 +134,24 @@ def moelb_split_variant(counts, home, replica, host_count, load, variant, passes
     N = replica.shape[1]
     _check(lib().moelb_split_variant(_p(counts), _p(home), _p(replica), G, E, N, passes, eps, variant,
                                      _p(host_count), _p(load), _stream(stream)), "moelb_split_variant")
+
+
+MOELB_SPLIT_SCHEDULE_INTS = 2 + 3 * 64 * 8
+
+
+def moelb_split_schedule(home, replica, schedule, G, stream=None):
+    E = home.shape[0]
+    N = replica.shape[1]
+    _check(lib().moelb_split_schedule(_p(home), _p(replica), G, E, N, _p(schedule), _stream(stream)),
+           "moelb_split_schedule")
+
+
+def moelb_split_scheduled(counts, home, replica, schedule, host_count, load, variant=0, passes=12, eps=0,
+                          stream=None):
+    G, E = counts.shape
+    N = replica.shape[1]
+    _check(lib().moelb_split_scheduled(_p(counts), _p(home), _p(replica), _p(schedule), G, E, N, passes, eps, variant,
+                                       _p(host_count), _p(load), _stream(stream)), "moelb_split_scheduled")
 
 
 def moelb_plan_swaps(counts, home, home_out, load, tau=0, gamma=(0, 1), max_swaps_per_rank=1 << 30, swaps=None,

@@ -341,6 +341,49 @@ def test_swap_planner_random_instances(moelb):
         assert [tuple(r) for r in sw.cpu().numpy()[:k].tolist()] == swaps, trial
 
 
+def test_split_with_schedule_equals_without(moelb):
+    """A schedule made for the placement gives the same split; one made for
+    another placement (or garbage) is ignored and the split colours itself."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(23)
+    for trial in range(20):
+        G = int(rng.choice([2, 4, 8, 16, 64]))
+        E = G * int(rng.choice([1, 2, 4])) if G < 64 else 256
+        N = int(rng.integers(1, 9 if G >= 16 else 4))
+        pop = 1.0 / (1 + rng.permutation(E)) ** 1.2
+        c = np.stack([rng.multinomial(2000, pop / pop.sum()) for _ in range(G)]).astype(np.int32)
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = O.plan(c, home, G, E, N, N // 2)
+        rep2 = O.plan(c[:, ::-1].copy(), home, G, E, N, N // 2)
+        ct, ht, rt, rt2 = (torch.from_numpy(a).to(dev) for a in (c, home, rep, rep2))
+        ref_hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ref_ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split(ct, ht, rt, ref_hc, ref_ld, passes=12)
+        sched = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, dtype=torch.int32, device=dev)
+        other = torch.full_like(sched, -1)
+        M.moelb_split_schedule(ht, rt, sched, G)
+        M.moelb_split_schedule(ht, rt2, other, G)
+        garbage = torch.from_numpy(rng.integers(-5, 40, M.MOELB_SPLIT_SCHEDULE_INTS).astype(np.int32)).to(dev)
+        for sc in (sched, other, garbage, None):
+            hc = torch.empty_like(ref_hc)
+            ld = torch.empty_like(ref_ld)
+            M.moelb_split_scheduled(ct, ht, rt, sc, hc, ld, passes=12)
+            assert torch.equal(hc, ref_hc) and torch.equal(ld, ref_ld), trial
+        # the schedule itself: n transfers, each colour class rank-disjoint
+        sh = sched.cpu().numpy()
+        n, ncol = int(sh[0]), int(sh[1])
+        tr = sh[2:2 + 3 * n].reshape(n, 3) if n else np.zeros((0, 3), np.int32)
+        transfers = O.split_transfers(home, O.host_sets(home, rep, E), E)
+        assert n == len(transfers)
+        assert [(int(u), int(v)) for u, v, _ in tr] == [(u, v) for u, v, _ in transfers]
+        assert tr[:, 2].tolist() == O.colour_transfers(transfers)
+        for col in range(ncol):
+            ranks = tr[tr[:, 2] == col][:, :2].ravel()
+            assert len(ranks) == len(set(ranks.tolist())), (trial, col)
+
+
 def test_split_heavily_replicated_home(moelb):
     """Every rank replicates the four experts of rank 0: rank 0 ends up in one
     transfer per replica, which takes the split past 64 edge colours (and, at
