@@ -22,11 +22,13 @@
 //    order (contiguous for the next GEMM).
 //  * Down GEMM: a (contiguous) x W2^T, N tile 256, scatters y rows back to
 //    their physical (permuted) rows.
-//  * Both GEMMs: 512 threads (8 waves, 2 x 4), wave tile 128 x 64 on bf16
-//    MFMA 32x32x16 with fp32 accumulators, A and B tiles of 256 x 64 staged
-//    through LDS (double buffered, 144 KiB, one barrier per K step, rows padded
-//    by 16 B against bank conflicts), global loads for step k+1 in flight
-//    while step k computes.  Tile ids are remapped so each XCD (workgroups go
+//  * Both GEMMs: 256 threads (4 waves, 2 x 2), wave tile 128 x 128 on bf16
+//    MFMA 32x32x16 with fp32 accumulators (256 per lane).  With K a multiple
+//    of 64, A and B tiles of 256 x 64 stream global -> LDS by direct-to-LDS
+//    loads through a ring of five 32 KiB half-stages (ffn_mfma_dma_kernel; the
+//    down GEMM as a persistent kernel when K / 64 >= 3); otherwise they are
+//    staged through registers into a double-buffered 144 KiB LDS tile
+//    (ffn_mfma_kernel).  Tile ids are remapped so each XCD (workgroups go
 //    round-robin over the 8 XCDs) works on a contiguous tile range, keeping A
 //    blocks and weight slices in its own L2.
 //  * fp32 storage uses a SIMT fp32 GEMM with the same schedule.
