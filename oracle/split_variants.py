@@ -221,33 +221,42 @@ def split_variant(c, home, replica, G: int, E: int, variant: str, passes: int = 
     raise ValueError(variant)
 
 
-def stale_loads(c, home, replica, host_count_prev, G: int, E: int) -> np.ndarray:
-    """Rank loads when the split fractions of an earlier step are reused
-    (Relief, "Failure of Existing Approaches", decision frequency).  Reading:
-    same placement; each replicated expert's new pool R is dealt in the
-    fractions host_count_prev[e][h] / (its earlier pool), whole tokens by
-    largest remainder (ties: lower rank); an expert whose earlier pool was
-    empty deals evenly."""
+def stale_split(c, home, replica, host_count_prev, G: int, E: int):
+    """The split of an earlier step reused (Relief, "Failure of Existing
+    Approaches", decision frequency).  Reading: same placement; each
+    replicated expert's new remote pool R is dealt in the fractions
+    host_count_prev[e][h] / (sum of host_count_prev[e] over e's current
+    hosts), whole tokens by largest remainder (ties: lower rank); an expert
+    whose earlier pool on its hosts was empty deals evenly; an unreplicated
+    expert keeps its whole pool at home.  Returns (host_count[E][G], load[G])
+    in the split's conventions."""
     hosts = host_sets(home, replica, E)
     load = [0] * G
+    host_count = np.zeros((E, G), dtype=np.int64)
     for e in range(E):
         R = _remote_pool(c, hosts[e], e, G)
         for s in hosts[e]:
             load[s] += int(c[s][e])
         Hs = sorted(hosts[e])
         if len(Hs) == 1:
-            load[Hs[0]] += R
-            continue
-        prev = {h: int(host_count_prev[e][h]) for h in Hs}
-        tot = sum(prev.values())
-        if tot == 0:
-            give = even_split(R, Hs)
+            give = {Hs[0]: R}
         else:
-            give = {h: (R * prev[h]) // tot for h in Hs}
-            rem = {h: (R * prev[h]) % tot for h in Hs}
-            left = R - sum(give.values())
-            for h in sorted(Hs, key=lambda h: (-rem[h], h))[:left]:
-                give[h] += 1
+            prev = {h: int(host_count_prev[e][h]) for h in Hs}
+            tot = sum(prev.values())
+            if tot == 0:
+                give = even_split(R, Hs)
+            else:
+                give = {h: (R * prev[h]) // tot for h in Hs}
+                rem = {h: (R * prev[h]) % tot for h in Hs}
+                left = R - sum(give.values())
+                for h in sorted(Hs, key=lambda h: (-rem[h], h))[:left]:
+                    give[h] += 1
         for h, m in give.items():
             load[h] += m
-    return np.array(load, dtype=np.int64)
+            host_count[e][h] = m
+    return host_count, np.array(load, dtype=np.int64)
+
+
+def stale_loads(c, home, replica, host_count_prev, G: int, E: int) -> np.ndarray:
+    """Rank loads of ``stale_split``."""
+    return stale_split(c, home, replica, host_count_prev, G, E)[1]

@@ -169,3 +169,30 @@ def test_stale_loads_reduce_to_the_split():
         # exactly doubled shares
         assert np.array_equal(V.stale_loads(c, home, rep, hc, G, E), ld)
         assert np.array_equal(V.stale_loads(2 * c, home, rep, hc, G, E), 2 * ld)
+        hc2, ld2 = V.stale_split(c, home, rep, hc, G, E)
+        assert np.array_equal(hc2, hc) and np.array_equal(ld2, ld)
+
+
+def test_stale_split_by_hand():
+    # expert 0 lives on rank 0 with replicas on ranks 1 and 2; its remote
+    # pool is rank 3's pairs.  Expert 1 (home 1, no replica) gets rank 0's 4.
+    G, E = 4, 4
+    home = np.arange(4, dtype=np.int32)
+    rep = np.array([[-1], [0], [0], [-1]], dtype=np.int32)
+    c = np.zeros((G, E), np.int64)
+    c[0][0], c[2][0], c[3][0], c[0][1] = 1, 2, 10, 4
+    prev = np.zeros((E, G), np.int64)
+    prev[0] = [1, 2, 0, 5]  # rank 3 is no host of expert 0: ignored
+    hc, ld = V.stale_split(c, home, rep, prev, G, E)
+    # 10 * (1, 2, 0) / 3 = (3, 6, 0) rem (1, 2, 0): the one left goes to rank 1
+    assert hc[0].tolist() == [3, 7, 0, 0] and hc[1].tolist() == [0, 4, 0, 0]
+    assert ld.tolist() == [1 + 3, 7 + 4, 2, 0]
+    # equal remainders go to the lower ranks
+    c[3][0] = 5
+    prev[0] = [1, 1, 1, 0]
+    assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [2, 2, 1, 0]
+    # no earlier pool on the current hosts: the even split
+    prev[0] = [0, 0, 0, 9]
+    assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [2, 2, 1, 0]
+    c[3][0] = 7
+    assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [3, 2, 2, 0]
