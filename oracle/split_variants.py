@@ -226,9 +226,9 @@ def stale_split(c, home, replica, host_count_prev, G: int, E: int):
     Approaches", decision frequency).  Reading: same placement; each
     replicated expert's new remote pool R is dealt in the fractions
     host_count_prev[e][h] / (sum of host_count_prev[e] over e's current
-    hosts), whole tokens by largest remainder (ties: lower rank); an expert
-    whose earlier pool on its hosts was empty deals evenly; an unreplicated
-    expert keeps its whole pool at home.  Returns (host_count[E][G], load[G])
+    hosts; negative entries read as 0), whole tokens by largest remainder
+    (ties: lower rank); an expert whose earlier pool on its hosts was empty
+    deals evenly; an unreplicated expert keeps its whole pool at home.  Returns (host_count[E][G], load[G])
     in the split's conventions."""
     hosts = host_sets(home, replica, E)
     load = [0] * G
@@ -241,7 +241,7 @@ def stale_split(c, home, replica, host_count_prev, G: int, E: int):
         if len(Hs) == 1:
             give = {Hs[0]: R}
         else:
-            prev = {h: int(host_count_prev[e][h]) for h in Hs}
+            prev = {h: max(0, int(host_count_prev[e][h])) for h in Hs}
             tot = sum(prev.values())
             if tot == 0:
                 give = even_split(R, Hs)

@@ -196,3 +196,6 @@ def test_stale_split_by_hand():
     assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [2, 2, 1, 0]
     c[3][0] = 7
     assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [3, 2, 2, 0]
+    # negative entries read as 0: 7 * (0, 1, 1) / 2 = (0, 3, 3) rem (0, 1, 1)
+    prev[0] = [-4, 1, 1, 0]
+    assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [0, 4, 3, 0]
