@@ -159,6 +159,77 @@ def time_split_variants(layer, home, replica_cur, stream, reps=20):
     return out
 
 
+def time_stale_split(cfg, dev, stream, reps=20):
+    """How often the split must be decided (Relief, "Failure of Existing
+    Approaches"), over the workload's decode steps: each step plans its
+    placement from its lookahead routing (the current router on the previous
+    layer's input) and splits its actual counts fresh (Relief), evenly, and
+    stale (the previous step's shares dealt by moelb_split_stale).  Reports
+    the mean spatial balance sum(L)/(G max L) of each, the share of the fresh
+    split's gain over the even split that the stale one gives up, and both
+    kernels' times on the last step."""
+    import torch
+    from synth import workloads as W
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import HipEvents, to_device
+    S = cfg.steps
+    if S < 2:
+        return None
+    G, E, k, T = cfg.G, cfg.E, cfg.k, cfg.T
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx, idx_pred = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, counts_pred = torch.empty((G, E), **i32), torch.empty((G, E), **i32)
+    rep = torch.empty((G, cfg.N), **i32)
+    hc, hc_prev, hc_st = torch.empty((E, G), **i32), torch.empty((E, G), **i32), torch.empty((E, G), **i32)
+    ld = torch.empty(G, **i32)
+    sp = lambda l: float(l.double().sum() / (G * l.double().max().clamp(min=1)))  # noqa: E731
+    acc = {"fresh": [], "even": [], "stale": [], "static": [], "loss_vs_even": []}
+    for s in range(S):
+        li = W.layer_inputs(cfg, step=s)
+        up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
+        h, h_prev, wc, bc, home = up(li.h), up(li.h_prev), up(li.w_cur), up(li.b_cur), up(li.home)
+        M.moelb_gate_topk(h_prev, wc, bc, None, None, idx_pred, wts, stream=stream)
+        M.moelb_histogram(idx_pred, G, counts_pred, stream=stream)
+        M.moelb_plan(counts_pred, home, cfg.L, rep, stream=stream)
+        M.moelb_gate_topk(h, wc, bc, None, None, idx, wts, stream=stream)
+        M.moelb_histogram(idx, G, counts, stream=stream)
+        M.moelb_split(counts, home, rep, hc, ld, passes=0, stream=stream)
+        even = ld.clone()
+        if s > 0:
+            M.moelb_split_stale(counts, home, rep, hc_prev, hc_st, ld, stream=stream)
+            stale = ld.clone()
+        M.moelb_split(counts, home, rep, hc, ld, stream=stream)
+        fresh = ld.clone()
+        static = torch.zeros(G, dtype=torch.long, device=dev).index_add_(0, home.long(), counts.long().sum(0))
+        if s > 0:
+            acc["fresh"].append(sp(fresh))
+            acc["even"].append(sp(even))
+            acc["stale"].append(sp(stale))
+            acc["static"].append(sp(static))
+            f, e_, st = int(fresh.max()), int(even.max()), int(stale.max())
+            if e_ > f:
+                acc["loss_vs_even"].append((st - f) / (e_ - f))
+        hc_prev.copy_(hc)
+    ev = HipEvents(4)
+    ev.record(0, stream)
+    for _ in range(reps):
+        M.moelb_split(counts, home, rep, hc, ld, stream=stream)
+    ev.record(1, stream)
+    ev.record(2, stream)
+    for _ in range(reps):
+        M.moelb_split_stale(counts, home, rep, hc_prev, hc_st, ld, stream=stream)
+    ev.record(3, stream)
+    torch.cuda.synchronize()
+    out = {"steps": S - 1}
+    for key, v in acc.items():
+        out[key] = round(sum(v) / len(v), 4) if v else None
+    out["relief_us"] = round(1e3 * ev.elapsed_ms(0, 1) / reps, 2)
+    out["stale_us"] = round(1e3 * ev.elapsed_ms(2, 3) / reps, 2)
+    ev.close()
+    return out
+
+
 def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20):
     """The same step with FreeBalance's expert swaps in place of replication
     (budget: the N replica slots as swaps per rank; gamma = 1 / mean rank
@@ -303,6 +374,7 @@ def main():
         studies["split_variants"] = time_split_variants(layer, home, replica_cur, stream)
         studies["freebalance"] = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K,
                                                   args.warmup, stream, gather_rows=args.rows == "gather")
+        studies["stale_split"] = time_stale_split(cfg, dev, stream)
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)

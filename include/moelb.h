@@ -234,6 +234,27 @@ int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_
                         int32_t* host_count, int32_t* load, void* stream);
 
 /*
+ * Stale split: an earlier step's split dealt again on this step's counts
+ * (Relief, "Failure of Existing Approaches": deciding the split less often
+ * than every step).  Same placement conventions and outputs as moelb_split.
+ * Each replicated expert's remote pool R (its pairs owned by non-hosts) is
+ * dealt over its current hosts in the fractions p_h / P, p_h =
+ * max(host_count_prev[e,h], 0), P = sum of p_h over those hosts: host h gets
+ * floor(R p_h / P), and the R - sum(floors) hosts with the largest remainders
+ * (ties: lower rank) one more; if P = 0 the pool is split evenly (R div m
+ * each, the lowest R mod m hosts one more).  Unreplicated pools stay at home.
+ *  host_count_prev [E,G] int32  shares of the earlier step (moelb_split's
+ *                               host_count); must not overlap host_count
+ *  counts [G,E] int32 >= 0 (totalling below 2^31), home [E], replica [G,N]
+ *  host_count [E,G] int32 out, load [G] int32 out
+ * Requires G <= 64, N <= 8, E <= 256; host_count == host_count_prev returns
+ * MOELB_EINVAL.
+ */
+int moelb_split_stale(const int32_t* counts, const int32_t* home, const int32_t* replica,
+                      int G, int E, int N, const int32_t* host_count_prev,
+                      int32_t* host_count, int32_t* load, void* stream);
+
+/*
  * Local/remote permutation (Libra README "Key Ideas": two-stage locality-aware
  * execution, MoE_local on the token's own GPU, MoE_remote on the others).
  *  Pair p = t*k + j, expert e = idx[t,j], owner s = t div (T/G).  Local

@@ -811,6 +811,89 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   for (int r = lane; r < G; r += 64) load_out[r] = load[r];
 }
 
+// ---------------------------------------------------------------- stale split
+
+// The split of an earlier step reused (Relief, "Failure of Existing
+// Approaches": how often the split is decided).  One thread per expert: the
+// hosts (home + replica slots) serve their own pairs; a replicated expert's
+// remote pool R is dealt in the fractions of host_count_prev over its current
+// hosts (negative entries read as 0), floor(R p_h / P) each plus one for the
+// R - sum(floors) hosts with the largest remainders (ties: lower rank), or
+// evenly if P = 0; an unreplicated pool stays at home.
+__global__ __launch_bounds__(SPLIT_THREADS) void split_stale_kernel(const int32_t* __restrict__ counts,
+                                                                     const int32_t* __restrict__ home,
+                                                                     const int32_t* __restrict__ replica, int G,
+                                                                     int E, int N,
+                                                                     const int32_t* __restrict__ prev,
+                                                                     int32_t* __restrict__ host_count,
+                                                                     int32_t* __restrict__ load_out) {
+  __shared__ unsigned long long hostmask[MOELB_MAX_E];
+  __shared__ int load[MOELB_MAX_G];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
+  const int rs0 = tid < G * N ? replica[tid] : -1;
+  const int rs1 = tid + SPLIT_THREADS < G * N ? replica[tid + SPLIT_THREADS] : -1;
+  int my_home = 0;
+  if (e < E) {
+    my_home = clamp_rank(home[e], G);
+    hostmask[e] = 1ull << my_home;
+  }
+  __syncthreads();
+  if (rs0 >= 0 && rs0 < E) atomicOr(&hostmask[rs0], 1ull << (tid / N));
+  if (rs1 >= 0 && rs1 < E) atomicOr(&hostmask[rs1], 1ull << ((tid + SPLIT_THREADS) / N));
+  __syncthreads();
+  if (e < E) {
+    const uint64_t mask = hostmask[e];
+    const int m = __popcll(mask);
+    int R = 0;
+    for (int s = 0; s < G; ++s) {
+      const int c = counts[(size_t)s * E + e];
+      if ((mask >> s) & 1ull)
+        atomicAdd(&load[s], c);
+      else
+        R += c;
+    }
+    const int32_t* pe = prev + (size_t)e * G;
+    long long P = 0;
+    if (m > 1)
+      for (int h = 0; h < G; ++h)
+        if ((mask >> h) & 1ull) P += max(pe[h], 0);
+    long long given = 0;  // sum of the floors
+    if (m > 1 && P > 0)
+      for (int h = 0; h < G; ++h)
+        if ((mask >> h) & 1ull) given += (long long)R * max(pe[h], 0) / P;
+    const long long left = R - given;
+    int pos = 0;
+    for (int h = 0; h < G; ++h) {
+      int share = 0;
+      if ((mask >> h) & 1ull) {
+        if (m == 1) {
+          share = R;
+        } else if (P == 0) {
+          share = even_share(R, m, pos);
+        } else {
+          const long long q = (long long)R * max(pe[h], 0);
+          const long long rem = q % P;
+          // place of h among the hosts by (remainder descending, rank ascending)
+          int before = 0;
+          for (int g = 0; g < G; ++g) {
+            if (g == h || !((mask >> g) & 1ull)) continue;
+            const long long rg = (long long)R * max(pe[g], 0) % P;
+            before += (rg > rem || (rg == rem && g < h)) ? 1 : 0;
+          }
+          share = (int)(q / P) + (before < left ? 1 : 0);
+        }
+        ++pos;
+        atomicAdd(&load[h], share);
+      }
+      host_count[(size_t)e * G + h] = share;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < G; r += blockDim.x) load_out[r] = load[r];
+}
+
 }  // namespace
 
 extern "C" int moelb_histogram(const int32_t* idx, int T, int k, int E, int G, int32_t* counts,
@@ -892,6 +975,19 @@ extern "C" int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(swap_plan_kernel, dim3(1), dim3(SWAP_THREADS), 0, s, counts, home, G, E, tau, gamma_num,
                      gamma_den, max_swaps_per_rank, home_out, swaps, n_swaps, load);
+  MOELB_CHECK_LAUNCH();
+  return MOELB_OK;
+}
+
+extern "C" int moelb_split_stale(const int32_t* counts, const int32_t* home, const int32_t* replica, int G, int E,
+                                 int N, const int32_t* host_count_prev, int32_t* host_count, int32_t* load,
+                                 void* stream) {
+  if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
+  if (!counts || !home || (N > 0 && !replica) || !host_count_prev || !host_count || !load) return MOELB_EINVAL;
+  if (host_count == host_count_prev) return MOELB_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(split_stale_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home, N > 0 ? replica : home,
+                     G, E, N, host_count_prev, host_count, load);
   MOELB_CHECK_LAUNCH();
   return MOELB_OK;
 }

@@ -32,6 +32,7 @@ SIGNATURES = {
     "moelb_split_variant": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moelb_split_schedule": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moelb_split_scheduled": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moelb_split_stale": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "moelb_plan_swaps": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moelb_permute_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moelb_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
@@ -152,6 +153,13 @@ def moelb_split_scheduled(counts, home, replica, schedule, host_count, load, var
     N = replica.shape[1]
     _check(lib().moelb_split_scheduled(_p(counts), _p(home), _p(replica), _p(schedule), G, E, N, passes, eps, variant,
                                        _p(host_count), _p(load), _stream(stream)), "moelb_split_scheduled")
+
+
+def moelb_split_stale(counts, home, replica, host_count_prev, host_count, load, stream=None):
+    G, E = counts.shape
+    N = replica.shape[1]
+    _check(lib().moelb_split_stale(_p(counts), _p(home), _p(replica), G, E, N, _p(host_count_prev), _p(host_count),
+                                   _p(load), _stream(stream)), "moelb_split_stale")
 
 
 def moelb_plan_swaps(counts, home, home_out, load, tau=0, gamma=(0, 1), max_swaps_per_rank=1 << 30, swaps=None,

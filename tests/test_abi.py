@@ -63,6 +63,9 @@ def test_invalid_arguments_rejected_before_launch(lib):
     # unknown split variant; negative passes for a variant
     assert lib.moelb_split_variant(P, P, P, 4, 8, 1, 12, 0, 4, P, P, N) == 1
     assert lib.moelb_split_variant(P, P, P, 4, 8, 1, -1, 0, 3, P, P, N) == 1
+    # stale split: shares written over the earlier ones; no earlier shares
+    assert lib.moelb_split_stale(P, P, P, 4, 8, 1, P, P, P, N) == 1
+    assert lib.moelb_split_stale(P, P, P, 4, 8, 1, N, ctypes.c_void_p(32), P, N) == 1
     # swap planner: gamma denominator 0; numerator above 2^12
     assert lib.moelb_plan_swaps(P, P, 4, 8, 0, 1, 0, 2, P, N, N, P, N) == 1
     assert lib.moelb_plan_swaps(P, P, 4, 8, 0, 5000, 1, 2, P, N, N, P, N) == 1

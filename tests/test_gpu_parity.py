@@ -308,6 +308,50 @@ def test_split_variants_random_instances(moelb):
             assert np.array_equal(ld.cpu().numpy(), ld_o), (trial, name)
 
 
+def test_split_stale_random_instances(moelb):
+    """The stale split (an earlier step's shares dealt on new counts) against
+    its oracle, bit for bit: earlier shares from the split of other counts on
+    the same placement, from another placement, or random with zero and
+    negative entries."""
+    from oracle import moe_oracle as O
+    from oracle import split_variants as V
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(41)
+    for trial in range(40):
+        G = int(rng.choice([2, 4, 8, 16, 64]))
+        E = G * int(rng.choice([1, 2, 4])) if G < 64 else int(rng.choice([64, 128, 256]))
+        N = int(rng.integers(1, 9 if G >= 16 else 4))
+        L = int(rng.integers(0, N + 1))
+        pop = 1.0 / (1 + rng.permutation(E)) ** rng.uniform(0.5, 1.6)
+        c0, c1 = (np.stack([rng.multinomial(int(rng.integers(0, 5000)), pop / pop.sum()) for _ in range(G)])
+                  .astype(np.int32) for _ in range(2))
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = O.plan(c0, home, G, E, N, L)
+        kind = trial % 3
+        if kind == 0:
+            prev, _ = O.split(c0, home, rep, G, E)
+        elif kind == 1:
+            prev, _ = O.split(c0, home, O.plan(c1, home, G, E, N, L), G, E)
+        else:
+            prev = rng.integers(-3, 50, (E, G))
+            prev[rng.random((E, G)) < 0.3] = 0
+        prev = prev.astype(np.int32)
+        ct, ht, rt, pt = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (c1, home, rep, prev))
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split_stale(ct, ht, rt, pt, hc, ld)
+        hc_o, ld_o = V.stale_split(c1, home, rep, prev, G, E)
+        assert np.array_equal(hc.cpu().numpy(), hc_o), (trial, kind, G, E, N)
+        assert np.array_equal(ld.cpu().numpy(), ld_o), (trial, kind)
+        # the same step's shares reproduce the fresh split exactly
+        if kind == 0:
+            hcf = torch.empty_like(hc)
+            M.moelb_split(torch.from_numpy(c0).to(dev), ht, rt, hcf, ld)
+            M.moelb_split_stale(torch.from_numpy(c0).to(dev), ht, rt, hcf, hc, ld)
+            assert torch.equal(hc, hcf), trial
+
+
 def test_swap_planner_random_instances(moelb):
     """FreeBalance's swap planner against its oracle, bit for bit: placement,
     swap sequence and loads."""
