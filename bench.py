@@ -145,6 +145,7 @@ def time_split_variants(layer, home, replica_cur, stream, reps=20):
                                ("no_reverse", M.MOELB_SPLIT_NO_REVERSE, layer.passes),
                                ("jacobi", M.MOELB_SPLIT_JACOBI, layer.passes),
                                ("libra_greedy", M.MOELB_SPLIT_LIBRA_GREEDY, layer.passes),
+                               ("water_fill", M.MOELB_SPLIT_WATER_FILL, layer.passes),
                                ("hash", M.MOELB_SPLIT_RELIEF, 0)):
         ev = HipEvents(2)
         ev.record(0, stream)

@@ -202,6 +202,14 @@ int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int G, int E, i
  *                           host b (ties: lower rank), if load[a]-load[b] >= 2;
  *                           at most passes x (number of replica transfers)
  *                           moves.
+ *  MOELB_SPLIT_WATER_FILL   pools start from the even split; each pass every
+ *                           replicated expert re-deals its whole pool R from
+ *                           one snapshot of the loads, over levels l_h = load
+ *                           - own mass on host h: the largest z with sum of
+ *                           max(0, z - l_h) <= R is filled, the tokens left go
+ *                           one each to hosts with l_h <= z (ascending rank);
+ *                           stops after a pass that changes nothing (eps and
+ *                           the schedule are not used).
  * Same arguments, outputs and requirements as moelb_split; counts must be
  * non-negative.  An unknown variant returns MOELB_EINVAL.
  */
@@ -227,7 +235,8 @@ enum moelb_split_variant {
   MOELB_SPLIT_RELIEF = 0,
   MOELB_SPLIT_NO_REVERSE = 1,
   MOELB_SPLIT_JACOBI = 2,
-  MOELB_SPLIT_LIBRA_GREEDY = 3
+  MOELB_SPLIT_LIBRA_GREEDY = 3,
+  MOELB_SPLIT_WATER_FILL = 4
 };
 int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica,
                         int G, int E, int N, int passes, int eps, int variant,

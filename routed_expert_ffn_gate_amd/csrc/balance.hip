@@ -811,6 +811,110 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   for (int r = lane; r < G; r += 64) load_out[r] = load[r];
 }
 
+// ---------------------------------------------------------------- water-filling split
+
+// Relief's water-filling ablation ("Ablation Results (Table III)"; the rule is
+// a reading): replicated pools start from the even split; each pass, every
+// replicated expert redistributes its whole pool R over its hosts from one
+// snapshot of the loads, less its own mass on each host (levels l_h): the
+// largest level z with sum_h max(0, z - l_h) <= R is filled, and the tokens
+// left go one each to the hosts with l_h <= z in ascending rank.  Stops after
+// a pass that changes nothing.  One thread per expert; host_count holds the
+// masses between passes.
+__global__ __launch_bounds__(SPLIT_THREADS) void split_water_fill_kernel(const int32_t* __restrict__ counts,
+                                                                          const int32_t* __restrict__ home,
+                                                                          const int32_t* __restrict__ replica,
+                                                                          int G, int E, int N, int passes,
+                                                                          int32_t* __restrict__ host_count,
+                                                                          int32_t* __restrict__ load_out) {
+  __shared__ unsigned long long hostmask[MOELB_MAX_E];
+  __shared__ int load[MOELB_MAX_G];
+  __shared__ int snap[MOELB_MAX_G];
+  __shared__ int changed;
+  const int tid = threadIdx.x;
+  const int e = tid;
+  for (int r = tid; r < G; r += blockDim.x) load[r] = 0;
+  const int rs0 = tid < G * N ? replica[tid] : -1;
+  const int rs1 = tid + SPLIT_THREADS < G * N ? replica[tid + SPLIT_THREADS] : -1;
+  int my_home = 0;
+  if (e < E) {
+    my_home = clamp_rank(home[e], G);
+    hostmask[e] = 1ull << my_home;
+  }
+  __syncthreads();
+  if (rs0 >= 0 && rs0 < E) atomicOr(&hostmask[rs0], 1ull << (tid / N));
+  if (rs1 >= 0 && rs1 < E) atomicOr(&hostmask[rs1], 1ull << ((tid + SPLIT_THREADS) / N));
+  __syncthreads();
+  uint64_t mask = 0;
+  int m = 0, R = 0;
+  int32_t* x = host_count + (size_t)(e < E ? e : 0) * G;
+  if (e < E) {
+    mask = hostmask[e];
+    m = __popcll(mask);
+    for (int s = 0; s < G; ++s) {
+      const int c = counts[(size_t)s * E + e];
+      if ((mask >> s) & 1ull)
+        atomicAdd(&load[s], c);
+      else
+        R += c;
+    }
+    int pos = 0;
+    for (int h = 0; h < G; ++h) {
+      int share = 0;
+      if ((mask >> h) & 1ull) {
+        share = m == 1 ? R : even_share(R, m, pos);
+        ++pos;
+        atomicAdd(&load[h], share);
+      }
+      x[h] = share;
+    }
+  }
+  const bool repl = e < E && m > 1;
+  for (int p = 0; p < passes; ++p) {
+    __syncthreads();
+    for (int r = tid; r < G; r += blockDim.x) snap[r] = load[r];
+    if (tid == 0) changed = 0;
+    __syncthreads();
+    if (repl) {
+      int lo = INT_MAX;
+      for (int h = 0; h < G; ++h)
+        if ((mask >> h) & 1ull) lo = min(lo, snap[h] - x[h]);
+      int hi = lo + R;
+      while (lo < hi) {  // largest affordable level
+        const int mid = lo + (hi - lo + 1) / 2;
+        long long need = 0;
+        for (int h = 0; h < G; ++h)
+          if ((mask >> h) & 1ull) need += max(0, mid - (snap[h] - x[h]));
+        if (need <= R)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      int left = R;
+      for (int h = 0; h < G; ++h)
+        if ((mask >> h) & 1ull) left -= max(0, lo - (snap[h] - x[h]));
+      for (int h = 0; h < G; ++h) {
+        if (!((mask >> h) & 1ull)) continue;
+        const int l = snap[h] - x[h];
+        int give = max(0, lo - l);
+        if (left > 0 && l <= lo) {
+          ++give;
+          --left;
+        }
+        if (give != x[h]) {
+          changed = 1;
+          atomicAdd(&load[h], give - x[h]);
+          x[h] = give;
+        }
+      }
+    }
+    __syncthreads();
+    if (!changed) break;
+  }
+  __syncthreads();
+  for (int r = tid; r < G; r += blockDim.x) load_out[r] = load[r];
+}
+
 // ---------------------------------------------------------------- stale split
 
 // The split of an earlier step reused (Relief, "Failure of Existing
@@ -931,9 +1035,15 @@ extern "C" int moelb_split_scheduled(const int32_t* counts, const int32_t* home,
                                      int32_t* host_count, int32_t* load, void* stream) {
   if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
   if (passes < 0 || passes > 1024 || eps < 0) return MOELB_EINVAL;
-  if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_LIBRA_GREEDY) return MOELB_EINVAL;
+  if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_WATER_FILL) return MOELB_EINVAL;
   if (!counts || !home || (N > 0 && !replica) || !host_count || !load) return MOELB_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (variant == MOELB_SPLIT_WATER_FILL) {
+    hipLaunchKernelGGL(split_water_fill_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home,
+                       N > 0 ? replica : home, G, E, N, passes, host_count, load);
+    MOELB_CHECK_LAUNCH();
+    return MOELB_OK;
+  }
   hipLaunchKernelGGL(split_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home, N > 0 ? replica : home, G, E,
                      N, passes, eps, variant, schedule, nullptr, host_count, load);
   MOELB_CHECK_LAUNCH();

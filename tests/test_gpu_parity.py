@@ -286,7 +286,8 @@ def test_split_variants_random_instances(moelb):
     dev = torch.device("cuda")
     rng = np.random.default_rng(17)
     codes = {"relief": M.MOELB_SPLIT_RELIEF, "no_reverse": M.MOELB_SPLIT_NO_REVERSE,
-             "jacobi": M.MOELB_SPLIT_JACOBI, "libra_greedy": M.MOELB_SPLIT_LIBRA_GREEDY}
+             "jacobi": M.MOELB_SPLIT_JACOBI, "libra_greedy": M.MOELB_SPLIT_LIBRA_GREEDY,
+             "water_fill": M.MOELB_SPLIT_WATER_FILL}
     for trial in range(48):
         G = int(rng.choice([2, 4, 8, 16, 64]))
         E = G * int(rng.choice([1, 2, 4])) if G < 64 else int(rng.choice([64, 128, 256]))
@@ -299,7 +300,7 @@ def test_split_variants_random_instances(moelb):
         passes = int(rng.choice([0, 1, 3, 12]))
         ct, ht, rt = (torch.from_numpy(a).to(dev) for a in (c, home, rep))
         for name, code in codes.items():
-            eps = 0 if name == "libra_greedy" else int(rng.choice([0, 0, 2]))
+            eps = 0 if name in ("libra_greedy", "water_fill") else int(rng.choice([0, 0, 2]))
             hc = torch.empty((E, G), dtype=torch.int32, device=dev)
             ld = torch.empty(G, dtype=torch.int32, device=dev)
             M.moelb_split_variant(ct, ht, rt, hc, ld, code, passes=passes, eps=eps)
