@@ -380,7 +380,16 @@ def main():
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
     gu_ms = sub["ffn_gate_up_gemm"]
-    achieved = f["ffn_gate_up_flop"] / (gu_ms * 1e-3) / 1e12
+    # the gate/up GEMM's bound: its algorithmic bytes are the weights of the
+    # experts that received pairs, the unique token rows and the SwiGLU output
+    active = int((layer.counts.long().sum(0) > 0).sum().item())
+    gu_bytes = active * 2.0 * cfg.inter * cfg.d * cfg.elem_bytes + cfg.T * cfg.d * cfg.elem_bytes + \
+        cfg.P * cfg.inter * cfg.elem_bytes
+    gu_hbm_bound = f["ffn_gate_up_flop"] / gu_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    if gu_hbm_bound:
+        achieved, peak, unit = gu_bytes / (gu_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = f["ffn_gate_up_flop"] / (gu_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     hbm = {
         "gate_topk": by["gate_topk"] / (stage["gate_topk"] * 1e-3) / 1e9,
         "permute_rows": by["permute_rows"] / (permute_rows_ms * 1e-3) / 1e9,
@@ -411,10 +420,13 @@ def main():
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
                    "ffn_rows": args.rows},
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-        "roofline": {"bound": "mfma", "kernel": GATE_UP_KERNEL + " (gate/up GEMM + SwiGLU)",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "flop_per_launch": f["ffn_gate_up_flop"], "avg_launch_ms": round(gu_ms, 4)},
+        "roofline": {"bound": "hbm" if gu_hbm_bound else "mfma",
+                     "kernel": (GATE_UP_KERNEL if cfg.dtype == "bf16" else "ffn_simt_kernel<0>") +
+                     " (gate/up GEMM + SwiGLU)",
+                     "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "flop_per_launch": f["ffn_gate_up_flop"], "bytes_per_launch": gu_bytes,
+                     "avg_launch_ms": round(gu_ms, 4)},
         "stages_ms": {k_: round(v, 4) for k_, v in {**stage, **sub, "permute_rows": permute_rows_ms}.items()},
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
         "routing": balance,
