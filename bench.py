@@ -160,6 +160,37 @@ def time_split_variants(layer, home, replica_cur, stream, reps=20):
     return out
 
 
+def time_graph(layer, tensors, K, W, stream):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph; the
+    lookahead stream forks and joins inside it by events) and replayed: the
+    per-step time without per-launch host overhead and launch gaps."""
+    import torch
+    from routed_expert_ffn_gate_amd.layer import HipEvents
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step(*tensors)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(*tensors)
+    torch.cuda.synchronize()
+    for _ in range(W):
+        g.replay()
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(K):
+        g.replay()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / K
+    ev.close()
+    del g
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(layer.T / (ms * 1e-3), 1)}
+
+
 def time_stale_split(cfg, dev, stream, reps=20):
     """How often the split must be decided (Relief, "Failure of Existing
     Approaches"), over the workload's decode steps: each step plans its
@@ -376,6 +407,8 @@ def main():
         studies["freebalance"] = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K,
                                                   args.warmup, stream, gather_rows=args.rows == "gather")
         studies["stale_split"] = time_stale_split(cfg, dev, stream)
+        studies["graph"] = time_graph(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K,
+                                      args.warmup, stream)
     f, by = algorithmic_work(cfg)
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)

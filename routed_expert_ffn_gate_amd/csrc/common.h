@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "../../include/moelb.h"
 
 #define MOELB_WAVE 64
@@ -77,10 +81,43 @@ static inline size_t moelb_align256(size_t n) { return (n + 255) & ~static_cast<
 static inline bool moelb_dtype_ok(int dtype) { return dtype == MOELB_F32 || dtype == MOELB_BF16; }
 static inline size_t moelb_elem_bytes(int dtype) { return dtype == MOELB_F32 ? 4 : 2; }
 
-// Kernels that use more than 64 KiB of dynamic LDS must opt in (gfx950 has 160 KiB per CU).
+// Compute units of the current device, queried once per device (so a launch
+// recorded by stream capture makes no device query); 256 if the query fails.
+static inline int moelb_compute_units() {
+  static std::mutex mu;
+  static std::vector<std::pair<int, int>> known;  // (device, compute units)
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& x : known)
+    if (x.first == dev) return x.second;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  known.emplace_back(dev, cus);
+  return cus;
+}
+
+// Kernels that use more than 64 KiB of dynamic LDS must opt in (gfx950 has 160
+// KiB per CU).  The attribute is set once per kernel, size and device and
+// remembered, so later launches -- including ones recorded by stream capture
+// into a graph -- make no attribute call.
 template <typename Kern>
 static inline bool moelb_allow_lds(Kern kernel, size_t bytes) {
   if (bytes <= 65536) return true;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(bytes)) == hipSuccess;
+  struct Done {
+    const void* fn;
+    size_t bytes;
+    int dev;
+  };
+  static std::mutex mu;
+  static std::vector<Done> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Done& x : done)
+    if (x.fn == fn && x.dev == dev && x.bytes >= bytes) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes)) != hipSuccess)
+    return false;
+  done.push_back({fn, bytes, dev});
+  return true;
 }

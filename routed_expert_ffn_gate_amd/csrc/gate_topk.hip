@@ -515,13 +515,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_f32_kernel(
 
 int zstride_for(int N) { return ((N + 63) / 64) * 64 + 4; }
 
-int compute_units() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  return cus;
-}
+int compute_units() { return moelb_compute_units(); }
 
 template <int KL>
 int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,

@@ -1036,11 +1036,8 @@ __global__ __launch_bounds__(256) void ffn_simt_kernel(const float* __restrict__
 
 // One workgroup per compute unit (a multiple of the 8 XCDs).
 static int persistent_grid() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    cus = 256;
-  return cus & ~7;
+  const int cus = moelb_compute_units();
+  return cus < 8 ? 256 : cus & ~7;
 }
 
 extern "C" size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, int E, int d, int inter, int dtype) {

@@ -128,6 +128,61 @@ def test_freebalance_layer_step(moelb, name, changes):
     assert np.array_equal(np.bincount(run.home_cur, minlength=cfg.G), np.bincount(run.li.home, minlength=cfg.G))
 
 
+GRAPH_OUTPUTS = ("idx", "wts", "gap", "idx_next", "counts", "counts_next", "replica_next", "plan_load_next",
+                 "host_count", "load", "group_off", "perm", "pos", "y", "out")
+
+
+@pytest.mark.parametrize("name,changes", [("c2_qwen3_30b_decode", {}), ("c4_glm45_prefill", dict(T=2048)),
+                                          ("c2_qwen3_30b_decode", RAGGED)])
+def test_graph_replay_equals_eager(moelb, name, changes):
+    """The layer step captured once in a HIP graph (torch.cuda.CUDAGraph on the
+    step's stream, the lookahead stream forked and joined by events) and
+    replayed three times, each replay after an eager step on other inputs
+    that overwrites every output: each replay reproduces the eager step's
+    outputs bit for bit."""
+    from routed_expert_ffn_gate_amd.layer import MoELayer, to_device
+    cfg = W.scaled(W.config(name), **changes)
+    log(f"[graph] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} shared={cfg.shared_inter}")
+    dev = torch.device("cuda")
+    up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
+    li, li2 = W.layer_inputs(cfg, step=0), W.layer_inputs(cfg, step=1)
+    w13, w2 = W.expert_weights_stacked(cfg, 1)
+    sh = W.shared_weights(cfg)
+    W13, W2 = up(w13), up(w2)
+    S13, S2 = (up(sh[0]), up(sh[1])) if sh is not None else (None, None)
+    args = [up(li.h), up(li.w_cur), up(li.b_cur), up(li.w_next), up(li.b_next), up(li.home)]
+    args2 = [up(li2.h), up(li2.w_cur), up(li2.b_cur), up(li2.w_next), up(li2.b_next), up(li2.home)]
+    L = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
+                 shared_inter=cfg.shared_inter, gather_rows=True, materialize_x=True)
+    rep = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
+    L.predict_plan(up(li.h_prev), args[1], args[2], args[5], rep)
+    step = lambda a: L.step(*a[:6], rep, W13, W2, S13, S2)  # noqa: E731
+    o = step(args)
+    torch.cuda.synchronize()
+    ref = {n: getattr(o, n).clone() for n in GRAPH_OUTPUTS}
+    if o.shared is not None:
+        ref["shared"] = o.shared.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(args)
+    torch.cuda.synchronize()
+    for i in range(3):
+        step(args2)
+        torch.cuda.synchronize()
+        assert not torch.equal(o.out, ref["out"])
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in ref.items():
+            assert torch.equal(getattr(o, n), t), (i, n)
+    del g
+
+
 def test_permute_two_phases_equal_one_call(moelb):
     from routed_expert_ffn_gate_amd import moelb as M
     dev = torch.device("cuda")
