@@ -581,31 +581,45 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + aro[0][i]);
     xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0][i]);
   }
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint16_t* sa = lds + ((2 * kt) % DL_SLOTS) * DL_HALF;
-    const uint16_t* sb = lds + ((2 * kt + 1) % DL_SLOTS) * DL_HALF;
-    const bool b1 = kt >= 1 && kt + 1 < KT;  // second half of B_kt+1
-    const bool a2 = kt >= 1 && kt + 2 < KT;  // A_kt+2
-    DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, b1, 2 * kt + 3, 4)
-    DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, a2, 2 * kt + 4, 0)
-    DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, a2, 2 * kt + 4, 4)
-    const bool more = kt + 1 < KT;
-    if (more) {
-      // A_kt+2 is the only half-stage issued after B_kt+1; lgkmcnt(0): this
-      // wave's reads of step kt have landed before any wave refills its slots
-      if (kt + 2 < KT)
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
-    // last sub-step: read step kt+1's first, refill A_kt's slot with the
-    // first half of B_kt+2
-    const uint16_t* na = lds + ((2 * kt + 2) % DL_SLOTS) * DL_HALF;
-    const uint16_t* nbs = lds + ((2 * kt + 3) % DL_SLOTS) * DL_HALF;
-    DL_SUB(ya, yb, xa, xb, na, nbs, 0, more, kt + 2 < KT, 2 * kt + 5, 0)
+  // One K step.  B1: issue the second half of B_kt+1; A2: issue A_kt+2; MORE:
+  // a step follows (wait for its stages, barrier, read its first fragments);
+  // B2: issue the first half of B_kt+2.  The loop runs the steps whose flags
+  // are all true with literal flags, so its body has no branches; the first
+  // and the last two steps are peeled.
+#define DL_STEP(KT_, B1, A2, MORE, B2)                                                                 \
+  {                                                                                                    \
+    const int kt_ = (KT_);                                                                             \
+    const uint16_t* sa = lds + ((2 * kt_) % DL_SLOTS) * DL_HALF;                                       \
+    const uint16_t* sb = lds + ((2 * kt_ + 1) % DL_SLOTS) * DL_HALF;                                   \
+    DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, B1, 2 * kt_ + 3, 4)                                        \
+    DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, A2, 2 * kt_ + 4, 0)                                        \
+    DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, A2, 2 * kt_ + 4, 4)                                        \
+    if (MORE) {                                                                                        \
+      /* A_kt+2 is the only half-stage issued after B_kt+1; lgkmcnt(0): this                           \
+         wave's reads of step kt have landed before any wave refills its slots */                      \
+      if (B2)                                                                                          \
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                                    \
+      else                                                                                             \
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                                    \
+      __builtin_amdgcn_s_barrier();                                                                    \
+      asm volatile("" ::: "memory");                                                                   \
+    }                                                                                                  \
+    /* last sub-step: read step kt+1's first, refill A_kt's slot with the                              \
+       first half of B_kt+2 */                                                                         \
+    const uint16_t* na = lds + ((2 * kt_ + 2) % DL_SLOTS) * DL_HALF;                                   \
+    const uint16_t* nbs = lds + ((2 * kt_ + 3) % DL_SLOTS) * DL_HALF;                                  \
+    DL_SUB(ya, yb, xa, xb, na, nbs, 0, MORE, B2, 2 * kt_ + 5, 0)                                       \
   }
+  if (KT >= 4) {
+    DL_STEP(0, false, false, true, true)
+    for (int kt = 1; kt + 2 < KT; ++kt) DL_STEP(kt, true, true, true, true)
+    DL_STEP(KT - 2, true, false, true, false)
+    DL_STEP(KT - 1, false, false, false, false)
+  } else {
+    for (int kt = 0; kt < KT; ++kt)
+      DL_STEP(kt, kt >= 1 && kt + 1 < KT, kt >= 1 && kt + 2 < KT, kt + 1 < KT, kt + 2 < KT)
+  }
+#undef DL_STEP
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef DL_COPY
 #undef DL_SUB
@@ -828,51 +842,59 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
     xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + aro[0] + i * 32 * DL_BK);
     xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0] + i * 32 * DL_BK);
   }
+  // One K step (step kt of the tile, step g of the stream).  B1: issue the
+  // second half of B_g+1; SWITCH: then point the refills at the next tile; A2:
+  // issue A_g+2; MORE: a step follows (wait for its stages, barrier); B2: issue
+  // the first half of B_g+2; RD0: read step g+1's first fragments (not at a
+  // tile's end: they are read after the epilogue).  Inside a tile, the steps
+  // 1 .. KT-3 have all flags true and run in a loop with literal flags, so its
+  // body has no branches; the first and the last two steps are peeled.
+#define DL_STEP(B1, SWITCH, A2, MORE, B2, RD0)                                                         \
+  {                                                                                                    \
+    /* ring slots of half-stages 2g .. 2g+4, places of steps g+1, g+2 in their tiles */                \
+    const int s0 = (2 * g) % DL_SLOTS;                                                                 \
+    const int s1 = s0 + 1 < DL_SLOTS ? s0 + 1 : s0 + 1 - DL_SLOTS;                                     \
+    const int s2 = s1 + 1 < DL_SLOTS ? s1 + 1 : s1 + 1 - DL_SLOTS;                                     \
+    const int s3 = s2 + 1 < DL_SLOTS ? s2 + 1 : s2 + 1 - DL_SLOTS;                                     \
+    const int s4 = s3 + 1 < DL_SLOTS ? s3 + 1 : s3 + 1 - DL_SLOTS;                                     \
+    const int k1 = kt + 1 < KT ? kt + 1 : kt + 1 - KT;                                                 \
+    const int k2 = kt + 2 < KT ? kt + 2 : kt + 2 - KT;                                                 \
+    /* slot offsets opaque to the compiler: it would otherwise precompute the                          \
+       fragment addresses of every slot and hold them all in registers */                              \
+    int o0 = s0 * DL_HALF, o1 = s1 * DL_HALF, o2 = s2 * DL_HALF, o3 = s3 * DL_HALF;                    \
+    asm volatile("" : "+s"(o0), "+s"(o1), "+s"(o2), "+s"(o3));                                         \
+    const uint16_t* sa = lds + o0;                                                                     \
+    const uint16_t* sb = lds + o1;                                                                     \
+    DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, B1, s3, k1, true, 4)                                       \
+    if (SWITCH) DL_OFFSETS(nxt)                                                                        \
+    DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, A2, s4, k2, false, 0)                                      \
+    DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, A2, s4, k2, false, 4)                                      \
+    if (MORE) {                                                                                        \
+      /* A_g+2 is the only half-stage issued after B_g+1; lgkmcnt(0): this                             \
+         wave's reads of step g have landed before any wave refills its slots */                       \
+      if (B2)                                                                                          \
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");                                    \
+      else                                                                                             \
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                                    \
+      __builtin_amdgcn_s_barrier();                                                                    \
+      asm volatile("" ::: "memory");                                                                   \
+    }                                                                                                  \
+    /* last sub-step: refill A_g's slot s0 with the first half of B_g+2 */                             \
+    const uint16_t* na = lds + o2;                                                                     \
+    const uint16_t* nbs = lds + o3;                                                                    \
+    DL_SUB(ya, yb, xa, xb, na, nbs, 0, RD0, B2, s0, k2, true, 0)                                       \
+  }
   int g = 0;  // step of the whole stream; half-stages 2g (A) and 2g+1 (B)
   for (int jcur = 0; jcur < ntiles; ++jcur) {
-    for (int kt = 0; kt < KT; ++kt, ++g) {
-      // ring slots of half-stages 2g .. 2g+4, places of steps g+1, g+2 in their tiles
-      const int s0 = (2 * g) % DL_SLOTS;
-      const int s1 = s0 + 1 < DL_SLOTS ? s0 + 1 : s0 + 1 - DL_SLOTS;
-      const int s2 = s1 + 1 < DL_SLOTS ? s1 + 1 : s1 + 1 - DL_SLOTS;
-      const int s3 = s2 + 1 < DL_SLOTS ? s2 + 1 : s2 + 1 - DL_SLOTS;
-      const int s4 = s3 + 1 < DL_SLOTS ? s3 + 1 : s3 + 1 - DL_SLOTS;
-      const int k1 = kt + 1 < KT ? kt + 1 : kt + 1 - KT;
-      const int k2 = kt + 2 < KT ? kt + 2 : kt + 2 - KT;
-      // slot offsets opaque to the compiler: it would otherwise precompute the
-      // fragment addresses of every slot and hold them all in registers
-      int o0 = s0 * DL_HALF, o1 = s1 * DL_HALF, o2 = s2 * DL_HALF, o3 = s3 * DL_HALF;
-      asm volatile("" : "+s"(o0), "+s"(o1), "+s"(o2), "+s"(o3));
-      const uint16_t* sa = lds + o0;
-      const uint16_t* sb = lds + o1;
-      const bool b1 = g >= 1 && g + 1 < nsteps;  // second half of B_g+1
-      const bool a2 = g >= 1 && g + 2 < nsteps;  // A_g+2
-      DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, b1, s3, k1, true, 4)
-      if (kt == KT - 2 && jcur + 1 < ntiles) {
-        // from here on, refills load the next tile
-        DL_OFFSETS(nxt)
-      }
-      DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, a2, s4, k2, false, 0)
-      DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, a2, s4, k2, false, 4)
-      const bool more = g + 1 < nsteps;
-      if (more) {
-        // A_g+2 is the only half-stage issued after B_g+1; lgkmcnt(0): this
-        // wave's reads of step g have landed before any wave refills its slots
-        if (g + 2 < nsteps)
-          asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-      }
-      const bool tile_end = kt == KT - 1;
-      // last sub-step: read step g+1's first fragments (not at a tile's end:
-      // they are read after the epilogue) and refill A_g's slot s0 with the
-      // first half of B_g+2
-      const uint16_t* na = lds + o2;
-      const uint16_t* nbs = lds + o3;
-      DL_SUB(ya, yb, xa, xb, na, nbs, 0, more && !tile_end, g + 2 < nsteps, s0, k2, true, 0)
-    }
+    // K / 64 >= 3: steps 0 (peeled), 1 .. KT-3 (loop), KT-2 and KT-1 (peeled)
+    const bool last = jcur + 1 == ntiles;
+    int kt = 0;
+    DL_STEP(g >= 1, false, g >= 1, true, true, true)
+    for (kt = 1, ++g; kt + 2 < KT; ++kt, ++g) DL_STEP(true, false, true, true, true, true)
+    DL_STEP(true, !last, !last, true, !last, true)
+    ++kt, ++g;
+    DL_STEP(!last, false, !last, !last, !last, false)
+    ++g;
     // ---- epilogue of tile jcur, staged through the slot of its last B
     // half-stage, 32 KiB per round
     const int gl = g - 1;
@@ -934,6 +956,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
 #undef DL_COPY
 #undef DL_SUB
 #undef DL_OFFSETS
+#undef DL_STEP
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
