@@ -31,7 +31,7 @@ METRIC = "MoE-layer tokens/s (route+plan+grouped FFN+combine), % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 DEFAULT_WORKLOAD = "c3_qwen3_235b_prefill"
-GATE_UP_KERNEL = "ffn_mfma_dma_kernel<0>"
+GATE_UP_KERNEL = "ffn_persistent_kernel<0>"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "ffn_gate_up_gemm_traffic.json")
 
 
@@ -499,7 +499,7 @@ def summarize_pmc(workload, fetch_csv, write_csv):
     out = {"workload": workload, "kernel": GATE_UP_KERNEL, "kernel_source_sha": _kernel_sha()}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _read_pmc(path, counter)
-        gu = [float(r["Counter_Value"]) for r in rows if "ffn_mfma_dma_kernel<0>" in r["Kernel_Name"]]
+        gu = [float(r["Counter_Value"]) for r in rows if GATE_UP_KERNEL in r["Kernel_Name"]]
         cp = [r for r in rows if "copy" in r["Kernel_Name"].lower()]
         if not gu or not cp:
             raise SystemExit(f"{path}: no gate/up or copy dispatch with {counter}")

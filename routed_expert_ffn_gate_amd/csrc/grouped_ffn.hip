@@ -677,19 +677,18 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
   }
 }
 
-// ---------------------------------------------------------------- persistent down GEMM
+// ---------------------------------------------------------------- persistent GEMMs
 //
-// The down GEMM (K = inter, output rows scattered through the row map) runs as
-// a persistent kernel: one workgroup per CU walks its tiles, and the K steps of
-// consecutive tiles form one stream through the same 5-slot LDS ring, so the
-// next tile's first steps load while the current tile finishes and stores.
-// The DMA offsets switch to the next tile two steps before a tile's end (from
-// then on every refill belongs to it).  The epilogue stages the output through
-// the ring slot of the tile's last B half-stage (free once its last sub-step
-// has read it; the A slot beside it already takes the next refill), in four
-// rounds of 64 rows with XOR-swizzled 16-byte chunks.  Requires inter / 64 >= 3.
-// (The gate/up GEMM keeps one workgroup per tile: its SiLU epilogue inside the
-// tile loop needs more registers than the pipeline leaves.)
+// With K / 64 >= 3 both GEMMs run as persistent kernels: one workgroup per CU
+// walks its tiles, and the K steps of consecutive tiles form one stream
+// through the same 5-slot LDS ring, so the next tile's first steps load while
+// the current tile finishes and stores.  The DMA offsets switch to the next
+// tile two steps before a tile's end (from then on every refill belongs to
+// it).  The epilogue stages the output through the ring slot of the tile's
+// last B half-stage (free once its last sub-step has read it; the A slot
+// beside it already takes the next refill), 32 KiB per round with XOR-swizzled
+// 16-byte chunks: the gate/up GEMM's SwiGLU output in two rounds of 128 rows,
+// the down GEMM's output in four rounds of 64 rows.
 
 struct DlTile {
   int nt, e, v0, vend;
@@ -727,16 +726,29 @@ __device__ __forceinline__ int dl_out_row(const DlTile& c, const FfnSched& s, in
   return v < c.vend ? min(max(s.rowmap[v], 0), rows_y - 1) : 0;
 }
 
-__global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const uint16_t* __restrict__ w, FfnSched s,
-                                                                        int rows_y, int d, int inter, int ntn,
-                                                                        uint16_t* __restrict__ y) {
+// Gate/up GEMM: the source rows of this lane's 8 DMA rows of tile c (rows
+// past the expert's end repeat its first row).
+__device__ __forceinline__ void dl_src_rows(const DlTile& c, const FfnSched& s, int wave, int lane, int (&src)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int v = c.v0 + (wave * 8 + j) * 8 + (lane >> 3);
+    v = v < c.vend ? v : c.v0;
+    src[j] = s.asrc[v];
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ w, FfnSched s,
+                                                                    int rows_y, int d, int inter, int ntn,
+                                                                    uint16_t* __restrict__ y) {
   extern __shared__ __align__(16) char smem[];
   const int n_mtiles = *s.n_mtiles;
   const int total = n_mtiles * ntn;
   int ntiles = 0;
   while (dl_tile_id(ntiles, total) >= 0) ++ntiles;
   if (ntiles == 0) return;
-  const int KT = inter / DL_BK;
+  const int KT = (MODE == 0 ? d : inter) / DL_BK;
   const int nsteps = ntiles * KT;
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
@@ -745,31 +757,43 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
   const int wave = tid >> 6, lane = tid & 63;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t* abase = static_cast<const uint16_t*>(s.amid);
+  const uint16_t* abase = MODE == 0 ? x : static_cast<const uint16_t*>(s.amid);
 
   // tile being stored (cur), the next one, and the DMA byte offsets of the
   // tile being loaded: block (wave*8 + j) of 8 rows, row (lane >> 3) in it,
-  // slot (lane & 7) <- global chunk dl_slot(row, slot)
+  // slot (lane & 7) <- global chunk dl_slot(row, slot).  Gate/up: A rows come
+  // through the source-row table (src holds the next tile's), B rows are 128
+  // gate rows then the matching 128 up rows.
   DlTile cur = dl_tile(dl_tile_id(0, total), n_mtiles, ntn, s);
   DlTile nxt = ntiles > 1 ? dl_tile(dl_tile_id(1, total), n_mtiles, ntn, s) : cur;
+  int src[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* bbase;
   uint32_t aoff[8], boff[8];
 #define DL_OFFSETS(C)                                                                                  \
   {                                                                                                    \
-    bbase = w + (size_t)(C).e * d * inter;                                                             \
+    bbase = w + (MODE == 0 ? (size_t)(C).e * 2 * inter * d : (size_t)(C).e * d * inter);               \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                    \
       const int r = (wave * 8 + j) * 8 + (lane >> 3);                                                  \
       const int chunk = dl_slot(r, lane & 7);                                                          \
-      int v = (C).v0 + r;                                                                              \
-      v = v < (C).vend ? v : (C).v0;                                                                   \
-      aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;                                      \
-      int col = (C).nt * 256 + r;                                                                      \
-      col = col < d ? col : 0;                                                                         \
-      boff[j] = ((uint32_t)col * (uint32_t)inter + chunk * 8) * 2u;                                    \
+      if (MODE == 0) {                                                                                 \
+        aoff[j] = ((uint32_t)src[j] * (uint32_t)d + chunk * 8) * 2u;                                   \
+        int col = (C).nt * 128 + (r & 127);                                                            \
+        col = col < inter ? col : 0;                                                                   \
+        boff[j] = ((uint32_t)((r < 128) ? col : inter + col) * (uint32_t)d + chunk * 8) * 2u;          \
+      } else {                                                                                         \
+        int v = (C).v0 + r;                                                                            \
+        v = v < (C).vend ? v : (C).v0;                                                                 \
+        aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;                                    \
+        int col = (C).nt * 256 + r;                                                                    \
+        col = col < d ? col : 0;                                                                       \
+        boff[j] = ((uint32_t)col * (uint32_t)inter + chunk * 8) * 2u;                                  \
+      }                                                                                                \
     }                                                                                                  \
   }
+  if (MODE == 0) dl_src_rows(cur, s, wave, lane, src);
   DL_OFFSETS(cur)
-  int out_row = dl_out_row(cur, s, rows_y, wave, lane);
+  if (MODE == 0 && ntiles > 1) dl_src_rows(nxt, s, wave, lane, src);
+  int out_row = MODE == 1 ? dl_out_row(cur, s, rows_y, wave, lane) : 0;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -787,8 +811,10 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
     dl_copy16((ISB) ? boff[JJ] : aoff[JJ], base_,                                                      \
               lds_u32 + (uint32_t)(((SLOT) * DL_HALF + (wave_s * 8 + (JJ)) * 8 * DL_BK) * 2));         \
   }
-  // LDS element offsets (inside a half-stage) of this lane's fragments: block
-  // i adds i * 32 rows (the swizzle of a row depends on row % 32 only)
+  // LDS element offsets (inside a half-stage) of this lane's fragments: A
+  // block i adds i * 32 rows, B block i DL_NBO(i) rows (the swizzle of a row
+  // depends on row % 32 only).  Gate/up: B blocks 0, 1 are gate rows, 2, 3 the
+  // matching up rows.
   const int fr = lane & 31;
   const int fh = lane >> 5;
   const int fsw = ((fr >> 1) ^ (fr << 2)) & 7;
@@ -796,8 +822,9 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     aro[ks] = (wm * 128 + fr) * DL_BK + (((ks * 2 + fh) ^ fsw) * 8);
-    bro[ks] = (wn * 128 + fr) * DL_BK + (((ks * 2 + fh) ^ fsw) * 8);
+    bro[ks] = ((MODE == 0 ? wn * 64 : wn * 128) + fr) * DL_BK + (((ks * 2 + fh) ^ fsw) * 8);
   }
+#define DL_NBO(I) (MODE == 0 ? (((I) & 1) * 32 + ((I) >> 1) * 128) : (I) * 32)
   bf16x8_t xa[4], xb[4], ya[4], yb[4];
   // One k sub-step: per 32-row block mi, read the next set's fragments (from
   // sub-step KS of half-stages SA/SB, if RD), run its 4 MFMAs on the current
@@ -807,7 +834,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
   _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                   \
     if (RD) {                                                                                          \
       NA[mi] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS] + mi * 32 * DL_BK);                   \
-      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + mi * 32 * DL_BK);                   \
+      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + DL_NBO(mi) * DL_BK);                \
     }                                                                                                  \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ni], FA[mi], acc[mi][ni], 0, 0, 0);     \
@@ -820,7 +847,8 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
   // the loop a full drain
   asm volatile("" ::"s"(y), "s"(rows_y), "s"(nxt.e), "s"(nxt.v0), "s"(nxt.vend), "s"(nxt.nt), "s"(cur.v0),
                "s"(cur.vend), "s"(cur.nt));
-  asm volatile("" ::"v"(out_row));
+  asm volatile("" ::"v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "v"(src[4]), "v"(src[5]), "v"(src[6]),
+               "v"(src[7]), "v"(out_row));
   const int nh = 2 * nsteps;
   for (int j = 0; j < DL_SLOTS && j < nh; ++j)  // steps 0..2 of the first tile (K/64 >= 3)
 #pragma unroll
@@ -840,7 +868,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + aro[0] + i * 32 * DL_BK);
-    xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0] + i * 32 * DL_BK);
+    xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + DL_HALF + bro[0] + DL_NBO(i) * DL_BK);
   }
   // One K step (step kt of the tile, step g of the stream).  B1: issue the
   // second half of B_g+1; SWITCH: then point the refills at the next tile; A2:
@@ -866,7 +894,13 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
     const uint16_t* sa = lds + o0;                                                                     \
     const uint16_t* sb = lds + o1;                                                                     \
     DL_SUB(xa, xb, ya, yb, sa, sb, 1, true, B1, s3, k1, true, 4)                                       \
-    if (SWITCH) DL_OFFSETS(nxt)                                                                        \
+    if (SWITCH) {                                                                                      \
+      /* the next tile's offsets are computed here, not hoisted: they would                            \
+         otherwise be held beside the current ones */                                                  \
+      asm volatile("" : "+v"(src[0]), "+v"(src[1]), "+v"(src[2]), "+v"(src[3]), "+v"(src[4]),         \
+                   "+v"(src[5]), "+v"(src[6]), "+v"(src[7]));                                          \
+      DL_OFFSETS(nxt)                                                                                  \
+    }                                                                                                  \
     DL_SUB(ya, yb, xa, xb, sa, sb, 2, true, A2, s4, k2, false, 0)                                      \
     DL_SUB(xa, xb, ya, yb, sa, sb, 3, true, A2, s4, k2, false, 4)                                      \
     if (MORE) {                                                                                        \
@@ -896,42 +930,83 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
     DL_STEP(!last, false, !last, !last, !last, false)
     ++g;
     // ---- epilogue of tile jcur, staged through the slot of its last B
-    // half-stage, 32 KiB per round
+    // half-stage (free once its last sub-step has read it; the A slot beside
+    // it already takes the next refill), 32 KiB per round
     const int gl = g - 1;
     uint16_t* Cs = lds + ((2 * gl + 1) % DL_SLOTS) * DL_HALF;
     __syncthreads();
     const bool has_nn = jcur + 2 < ntiles;
     const DlTile nn = has_nn ? dl_tile(dl_tile_id(jcur + 2, total), n_mtiles, ntn, s) : nxt;
-    const int next_out_row = jcur + 1 < ntiles ? dl_out_row(nxt, s, rows_y, wave, lane) : 0;
+    const int next_out_row = (MODE == 1 && jcur + 1 < ntiles) ? dl_out_row(nxt, s, rows_y, wave, lane) : 0;
     asm volatile("" ::"s"(nn.e), "s"(nn.v0), "s"(nn.vend), "s"(nn.nt));
-    const int n0 = cur.nt * 256;
-    // four rounds; in round rd every wave stages its block mi = rd: staging
-    // row wm*32 + fr (512 B, chunk c at c ^ (row & 15))
+    if (MODE == 0) {
+      // SwiGLU of the tile's 256 x 128 outputs in two rounds; in round rd
+      // every wave stages its blocks mi = 2rd, 2rd+1: staging row
+      // wm*64 + (mi-2rd)*32 + fr (256 B, chunk c at c ^ (row & 15))
+      const int n0 = cur.nt * 128;
 #pragma unroll
-    for (int rd = 0; rd < 4; ++rd) {
-      const int r = wm * 32 + fr;
+      for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int mi = 2 * rd + m2;
+          const int r = wm * 64 + m2 * 32 + fr;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const f32x16_t& a4 = acc[rd][ni];
-          const int chunk = wn * 16 + ni * 4 + q;
-          *reinterpret_cast<uint2*>(Cs + r * 256 + ((chunk ^ (r & 15)) * 8) + fh * 4) =
-              make_uint2(bf16x2_pack(a4[q * 4], a4[q * 4 + 1]), bf16x2_pack(a4[q * 4 + 2], a4[q * 4 + 3]));
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              float o[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = silu_f32(acc[mi][f][q * 4 + i]) * acc[mi][f + 2][q * 4 + i];
+              const int chunk = wn * 8 + f * 4 + q;
+              *reinterpret_cast<uint2*>(Cs + r * 128 + ((chunk ^ (r & 15)) * 8) + fh * 4) =
+                  make_uint2(bf16x2_pack(o[0], o[1]), bf16x2_pack(o[2], o[3]));
+            }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      __syncthreads();
+        __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = tid + MF_THREADS * i;
-        const int rl = c >> 5, ch = c & 31;  // rl = 2*wave + (lane >> 5) + 8*i
-        const int v = cur.v0 + (rl >> 5) * 128 + rd * 32 + (rl & 31);
-        const int col = n0 + ch * 8;
-        const int orow = __shfl(out_row, rd * 16 + (lane >> 5) * 8 + i, 64);
-        const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 256 + ((ch ^ (rl & 15)) * 8));
-        if (v < cur.vend && col < d) *reinterpret_cast<uint4*>(y + (size_t)orow * d + col) = val;
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + MF_THREADS * i;
+          const int rl = c >> 4, ch = c & 15;
+          const int v = cur.v0 + (rl >> 6) * 128 + rd * 64 + (rl & 63);
+          const int col = n0 + ch * 8;
+          const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 128 + ((ch ^ (rl & 15)) * 8));
+          if (v < cur.vend && col < inter) *reinterpret_cast<uint4*>(y + (size_t)v * inter + col) = val;
+        }
+        __syncthreads();
       }
-      __syncthreads();
+    } else {
+      // four rounds; in round rd every wave stages its block mi = rd: staging
+      // row wm*32 + fr (512 B, chunk c at c ^ (row & 15))
+      const int n0 = cur.nt * 256;
+#pragma unroll
+      for (int rd = 0; rd < 4; ++rd) {
+        const int r = wm * 32 + fr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+            const f32x16_t& a4 = acc[rd][ni];
+            const int chunk = wn * 16 + ni * 4 + q;
+            *reinterpret_cast<uint2*>(Cs + r * 256 + ((chunk ^ (r & 15)) * 8) + fh * 4) =
+                make_uint2(bf16x2_pack(a4[q * 4], a4[q * 4 + 1]), bf16x2_pack(a4[q * 4 + 2], a4[q * 4 + 3]));
+          }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + MF_THREADS * i;
+          const int rl = c >> 5, ch = c & 31;  // rl = 2*wave + (lane >> 5) + 8*i
+          const int v = cur.v0 + (rl >> 5) * 128 + rd * 32 + (rl & 31);
+          const int col = n0 + ch * 8;
+          const int orow = __shfl(out_row, rd * 16 + (lane >> 5) * 8 + i, 64);
+          const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 256 + ((ch ^ (rl & 15)) * 8));
+          if (v < cur.vend && col < d) *reinterpret_cast<uint4*>(y + (size_t)orow * d + col) = val;
+        }
+        __syncthreads();
+      }
     }
+    // source rows of the tile after next (first used at its offsets switch)
+    if (MODE == 0 && has_nn) dl_src_rows(nn, s, wave, lane, src);
     cur = nxt;
     nxt = nn;
     out_row = next_out_row;
@@ -948,7 +1023,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xa[i] = *reinterpret_cast<const bf16x8_t*>(na + aro[0] + i * 32 * DL_BK);
-        xb[i] = *reinterpret_cast<const bf16x8_t*>(nbs + bro[0] + i * 32 * DL_BK);
+        xb[i] = *reinterpret_cast<const bf16x8_t*>(nbs + bro[0] + DL_NBO(i) * DL_BK);
       }
     }
   }
@@ -957,6 +1032,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_down_persistent_kernel(const u
 #undef DL_SUB
 #undef DL_OFFSETS
 #undef DL_STEP
+#undef DL_NBO
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -1112,13 +1188,19 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
     const int ntn1 = (d + 255) / 256;
     // direct-to-LDS pipeline when K is a multiple of its 64-wide step
     const bool dma0 = d % DL_BK == 0, dma1 = inter % DL_BK == 0;  // else the register-staged kernel
-    const bool pers1 = dma1 && inter / DL_BK >= 3;                  // persistent down GEMM
+    const bool pers0 = dma0 && d / DL_BK >= 3;                      // persistent kernels
+    const bool pers1 = dma1 && inter / DL_BK >= 3;
     if ((dma0 && !moelb_allow_lds(ffn_mfma_dma_kernel<0>, DL_LDS_BYTES)) ||
         (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)) ||
-        (pers1 && !moelb_allow_lds(ffn_down_persistent_kernel, DL_LDS_BYTES)))
+        (pers0 && !moelb_allow_lds(ffn_persistent_kernel<0>, DL_LDS_BYTES)) ||
+        (pers1 && !moelb_allow_lds(ffn_persistent_kernel<1>, DL_LDS_BYTES)))
       return MOELB_ELAUNCH;
     rec(1);
-    if (dma0)
+    if (pers0)
+      hipLaunchKernelGGL(ffn_persistent_kernel<0>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13), sc, rows, d, inter, ntn0,
+                         static_cast<uint16_t*>(sc.amid));
+    else if (dma0)
       hipLaunchKernelGGL(ffn_mfma_dma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
                          static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13),
                          sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
@@ -1129,8 +1211,9 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
     MOELB_CHECK_LAUNCH();
     rec(2);
     if (pers1)
-      hipLaunchKernelGGL(ffn_down_persistent_kernel, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1, static_cast<uint16_t*>(y));
+      hipLaunchKernelGGL(ffn_persistent_kernel<1>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                         nullptr, static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1,
+                         static_cast<uint16_t*>(y));
     else if (dma1)
       hipLaunchKernelGGL(ffn_mfma_dma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
                          static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,

@@ -87,10 +87,11 @@ def test_drift_olmoe_shape_eight_layers(moelb):
         log(f"  {r} {f}")
 
 
-@pytest.mark.parametrize("d,inter", [(576, 192), (320, 320)])
-def test_down_gemm_short_k_several_tiles_per_workgroup(moelb, d, inter):
-    # the persistent down GEMM at its shortest K (3 and 5 steps of 64), with
-    # more output tiles than workgroups and a column tail in the last tile
+@pytest.mark.parametrize("d,inter", [(576, 192), (320, 320), (192, 448)])
+def test_persistent_gemms_short_k_several_tiles_per_workgroup(moelb, d, inter):
+    # the persistent GEMMs at their shortest K (down: 3 and 5 steps of 64;
+    # gate/up: 3 steps at d = 192), with more output tiles than workgroups and
+    # column tails (gate/up: 448 = 3.5 x 128; down: 192 < 256)
     cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=4096, d=d, E=32, k=8, inter=inter, G=8, N=2, L=1)
     _full_check(cfg, tokens=sample_tokens(cfg.T, 64))
 
