@@ -87,11 +87,12 @@ def test_drift_olmoe_shape_eight_layers(moelb):
         log(f"  {r} {f}")
 
 
-@pytest.mark.parametrize("d,inter", [(576, 192), (320, 320), (192, 448)])
+@pytest.mark.parametrize("d,inter", [(576, 192), (320, 320), (192, 448), (128, 64)])
 def test_persistent_gemms_short_k_several_tiles_per_workgroup(moelb, d, inter):
     # the persistent GEMMs at their shortest K (down: 3 and 5 steps of 64;
     # gate/up: 3 steps at d = 192), with more output tiles than workgroups and
-    # column tails (gate/up: 448 = 3.5 x 128; down: 192 < 256)
+    # column tails (gate/up: 448 = 3.5 x 128; down: 192 < 256); and below
+    # three steps (2 and 1), the one-workgroup-per-tile direct-to-LDS kernels
     cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=4096, d=d, E=32, k=8, inter=inter, G=8, N=2, L=1)
     _full_check(cfg, tokens=sample_tokens(cfg.T, 64))
 
