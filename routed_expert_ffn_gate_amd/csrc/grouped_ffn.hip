@@ -408,7 +408,9 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM, direct-to-LDS
 
-// Same tile, waves and epilogue as ffn_mfma_kernel, for K % 64 == 0.
+// Same tile, waves and epilogue as ffn_mfma_kernel, for K % 64 == 0 (one
+// workgroup per tile: used when K / 64 < 3; longer K runs in the persistent
+// kernels below, which share this pipeline).
 //  * Tiles of A and B stream global -> LDS with global_load_lds_dwordx4 (no
 //    staging registers, no ds_write), in 64-wide K steps: each row request is
 //    a whole 128-byte line, and each wave-instruction fills 1 KiB of LDS
