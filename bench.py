@@ -58,6 +58,22 @@ def algorithmic_work(cfg):
     return f, by
 
 
+def gate_up_roofline(cfg, active_experts, gu_ms):
+    """Bound of the gate/up GEMM and its rate against that bound.  Algorithmic
+    work: 4·P·d·I FLOP; algorithmic bytes: the weights of the experts that
+    received pairs (2·I·d each), the unique token rows (T·d) and the SwiGLU
+    output (P·I).  HBM-bound where FLOP / bytes is below the ridge
+    (peak FLOP/s / peak bytes/s).  Returns (hbm_bound, achieved, peak, unit,
+    bytes)."""
+    flop = 4.0 * cfg.P * cfg.d * cfg.inter
+    b = cfg.elem_bytes
+    nbytes = active_experts * 2.0 * cfg.inter * cfg.d * b + cfg.T * cfg.d * b + cfg.P * cfg.inter * b
+    hbm_bound = flop / nbytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        return True, nbytes / (gu_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", nbytes
+    return False, flop / (gu_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", nbytes
+
+
 def routing_stats(cfg, layer, idx_pred, home):
     """Reported alongside the throughput, from the step's device outputs:
     lookahead hit rate (fraction of the step's top-k assignments that the
@@ -413,16 +429,8 @@ def main():
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
     gu_ms = sub["ffn_gate_up_gemm"]
-    # the gate/up GEMM's bound: its algorithmic bytes are the weights of the
-    # experts that received pairs, the unique token rows and the SwiGLU output
     active = int((layer.counts.long().sum(0) > 0).sum().item())
-    gu_bytes = active * 2.0 * cfg.inter * cfg.d * cfg.elem_bytes + cfg.T * cfg.d * cfg.elem_bytes + \
-        cfg.P * cfg.inter * cfg.elem_bytes
-    gu_hbm_bound = f["ffn_gate_up_flop"] / gu_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    if gu_hbm_bound:
-        achieved, peak, unit = gu_bytes / (gu_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-    else:
-        achieved, peak, unit = f["ffn_gate_up_flop"] / (gu_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    gu_hbm_bound, achieved, peak, unit, gu_bytes = gate_up_roofline(cfg, active, gu_ms)
     hbm = {
         "gate_topk": by["gate_topk"] / (stage["gate_topk"] * 1e-3) / 1e9,
         "permute_rows": by["permute_rows"] / (permute_rows_ms * 1e-3) / 1e9,
