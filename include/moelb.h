@@ -12,6 +12,12 @@
  *   moelb_grouped_ffn masked grouped SwiGLU expert GEMMs
  *   moelb_combine     top-k weighted sum of expert outputs (+ shared expert)
  *
+ * and around them: the split's round schedule made once per placement
+ * (moelb_split_schedule, moelb_split_scheduled), split variants for
+ * comparison (moelb_split_variant), an earlier step's split dealt again
+ * (moelb_split_stale), FreeBalance's expert-swap planner (moelb_plan_swaps),
+ * and the permutation in two phases (moelb_permute_local, moelb_permute_remote).
+ *
  * Conventions for every entry point:
  *  - Plain C ABI.  Every pointer argument is DEVICE memory owned by the caller
  *    (e.g. a PyTorch tensor's data pointer), unless stated otherwise; the
