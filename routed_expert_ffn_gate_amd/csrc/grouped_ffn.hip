@@ -211,11 +211,11 @@ __device__ __forceinline__ int xcd_tile(int total) {
 // slices, which its L2 serves, instead of streaming a whole expert's weights
 // per M tile.
 constexpr int GROUP_M = 8;
-__device__ __forceinline__ void grouped_tile(int t, int n_mtiles, int ntn, int& mt, int& nt) {
-  const int group = t / (GROUP_M * ntn);
-  const int first = group * GROUP_M;
-  const int gm = min(GROUP_M, n_mtiles - first);
-  const int local = t - group * GROUP_M * ntn;
+__device__ __forceinline__ void grouped_tile(int t, int n_mtiles, int ntn, int& mt, int& nt, int GM = GROUP_M) {
+  const int group = t / (GM * ntn);
+  const int first = group * GM;
+  const int gm = min(GM, n_mtiles - first);
+  const int local = t - group * GM * ntn;
   nt = local / gm;
   mt = first + local % gm;
 }
@@ -706,10 +706,20 @@ __device__ __forceinline__ int dl_tile_id(int j, int total) {
   return (lo < per && t < total) ? t : -1;
 }
 
+// Group height of the persistent tile order: the gate/up GEMM groups 8 M
+// tiles; the down GEMM about 64 tiles per group (64 / N tiles, 2 .. 8 M tiles).
+// Measured against 8 for both: C3's down GEMM 3 % faster with 4 (16 N
+// tiles), C5's 3 % slower with 4 (8 N tiles), the gate/up GEMMs 1 % slower.
+template <int MODE>
+__device__ __forceinline__ int dl_group_m(int ntn) {
+  return MODE == 0 ? GROUP_M : min(8, max(2, 64 / ntn));
+}
+
+template <int MODE>
 __device__ __forceinline__ DlTile dl_tile(int t, int n_mtiles, int ntn, const FfnSched& s) {
   DlTile c;
   int mt, nt;
-  grouped_tile(t, n_mtiles, ntn, mt, nt);
+  grouped_tile(t, n_mtiles, ntn, mt, nt, dl_group_m<MODE>(ntn));
   c.nt = nt;
   c.e = s.mt_e[mt];
   c.v0 = s.mt_v0[mt];
@@ -766,8 +776,8 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
   // slot (lane & 7) <- global chunk dl_slot(row, slot).  Gate/up: A rows come
   // through the source-row table (src holds the next tile's), B rows are 128
   // gate rows then the matching 128 up rows.
-  DlTile cur = dl_tile(dl_tile_id(0, total), n_mtiles, ntn, s);
-  DlTile nxt = ntiles > 1 ? dl_tile(dl_tile_id(1, total), n_mtiles, ntn, s) : cur;
+  DlTile cur = dl_tile<MODE>(dl_tile_id(0, total), n_mtiles, ntn, s);
+  DlTile nxt = ntiles > 1 ? dl_tile<MODE>(dl_tile_id(1, total), n_mtiles, ntn, s) : cur;
   int src[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* bbase;
   uint32_t aoff[8], boff[8];
@@ -938,7 +948,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
     uint16_t* Cs = lds + ((2 * gl + 1) % DL_SLOTS) * DL_HALF;
     __syncthreads();
     const bool has_nn = jcur + 2 < ntiles;
-    const DlTile nn = has_nn ? dl_tile(dl_tile_id(jcur + 2, total), n_mtiles, ntn, s) : nxt;
+    const DlTile nn = has_nn ? dl_tile<MODE>(dl_tile_id(jcur + 2, total), n_mtiles, ntn, s) : nxt;
     const int next_out_row = (MODE == 1 && jcur + 1 < ntiles) ? dl_out_row(nxt, s, rows_y, wave, lane) : 0;
     asm volatile("" ::"s"(nn.e), "s"(nn.v0), "s"(nn.vend), "s"(nn.nt));
     if (MODE == 0) {
