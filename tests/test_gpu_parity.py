@@ -134,17 +134,19 @@ GRAPH_OUTPUTS = ("idx", "wts", "gap", "idx_next", "counts", "counts_next", "repl
                  "host_count", "load", "group_off", "perm", "pos", "y", "out")
 
 
-@pytest.mark.parametrize("name,changes", [("c2_qwen3_30b_decode", {}), ("c4_glm45_prefill", dict(T=2048)),
-                                          ("c2_qwen3_30b_decode", RAGGED)])
-def test_graph_replay_equals_eager(moelb, name, changes):
+@pytest.mark.parametrize("name,changes,two_stage", [("c2_qwen3_30b_decode", {}, False),
+                                                    ("c4_glm45_prefill", dict(T=2048), False),
+                                                    ("c2_qwen3_30b_decode", RAGGED, False),
+                                                    ("c4_glm45_prefill", dict(T=2048), True)])
+def test_graph_replay_equals_eager(moelb, name, changes, two_stage):
     """The layer step captured once in a HIP graph (torch.cuda.CUDAGraph on the
-    step's stream, the lookahead stream forked and joined by events) and
-    replayed three times, each replay after an eager step on other inputs
-    that overwrites every output: each replay reproduces the eager step's
-    outputs bit for bit."""
+    step's stream, the lookahead stream -- and for the two-stage step the
+    split stream -- forked and joined by events) and replayed three times,
+    each replay after an eager step on other inputs that overwrites every
+    output: each replay reproduces the eager step's outputs bit for bit."""
     from routed_expert_ffn_gate_amd.layer import MoELayer, to_device
     cfg = W.scaled(W.config(name), **changes)
-    log(f"[graph] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} shared={cfg.shared_inter}")
+    log(f"[graph] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} shared={cfg.shared_inter} two_stage={two_stage}")
     dev = torch.device("cuda")
     up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
     li, li2 = W.layer_inputs(cfg, step=0), W.layer_inputs(cfg, step=1)
@@ -158,7 +160,8 @@ def test_graph_replay_equals_eager(moelb, name, changes):
                  shared_inter=cfg.shared_inter, gather_rows=True, materialize_x=True)
     rep = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
     L.predict_plan(up(li.h_prev), args[1], args[2], args[5], rep)
-    step = lambda a: L.step(*a[:6], rep, W13, W2, S13, S2)  # noqa: E731
+    run = L.step_two_stage if two_stage else L.step
+    step = lambda a: run(*a[:6], rep, W13, W2, S13, S2)  # noqa: E731
     o = step(args)
     torch.cuda.synchronize()
     ref = {n: getattr(o, n).clone() for n in GRAPH_OUTPUTS}
