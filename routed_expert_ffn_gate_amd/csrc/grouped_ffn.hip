@@ -544,8 +544,15 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
 #define DL_SUB(FA, FB, NA, NB, SA, SB, KS, RD, DO, J, J0)                                              \
   _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                   \
     if (RD) {                                                                                          \
-      NA[mi] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS][mi]);                                 \
-      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS][mi]);                                 \
+      /* B fragments first (blocks 0, 1 then 2, 3), then A: every read lands                       \
+         at least 12 MFMAs before the next sub-step needs it */                                        \
+      if (mi < 2) {                                                                                    \
+        NB[2 * mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS][2 * mi]);                       \
+        NB[2 * mi + 1] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS][2 * mi + 1]);               \
+      } else {                                                                                         \
+        NA[2 * mi - 4] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS][2 * mi - 4]);               \
+        NA[2 * mi - 3] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS][2 * mi - 3]);               \
+      }                                                                                                \
     }                                                                                                  \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ni], FA[mi], acc[mi][ni], 0, 0, 0);     \
@@ -845,8 +852,15 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
 #define DL_SUB(FA, FB, NA, NB, SA, SB, KS, RD, DO, SLOT, KK, ISB, J0)                                  \
   _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                   \
     if (RD) {                                                                                          \
-      NA[mi] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS] + mi * 32 * DL_BK);                   \
-      NB[mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + DL_NBO(mi) * DL_BK);                \
+      /* B fragments first (blocks 0, 1 then 2, 3), then A: every read lands                       \
+         at least 12 MFMAs before the next sub-step needs it */                                        \
+      if (mi < 2) {                                                                                    \
+        NB[2 * mi] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + DL_NBO(2 * mi) * DL_BK);       \
+        NB[2 * mi + 1] = *reinterpret_cast<const bf16x8_t*>((SB) + bro[KS] + DL_NBO(2 * mi + 1) * DL_BK); \
+      } else {                                                                                         \
+        NA[2 * mi - 4] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS] + (2 * mi - 4) * 32 * DL_BK); \
+        NA[2 * mi - 3] = *reinterpret_cast<const bf16x8_t*>((SA) + aro[KS] + (2 * mi - 3) * 32 * DL_BK); \
+      }                                                                                                \
     }                                                                                                  \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                   \
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[ni], FA[mi], acc[mi][ni], 0, 0, 0);     \
