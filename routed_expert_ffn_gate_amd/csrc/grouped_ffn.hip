@@ -424,9 +424,11 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
 //    slot) and the first of t+1, A of step t+3 during the second and third
 //    sub-steps of t+1.
 //  * The four 16-wide k sub-steps of a step are software-pipelined over two
-//    fragment register sets (sub-step j+1 is read while j's MFMAs run).  One
-//    barrier per step, behind the third sub-step: every wave has read step
-//    t's stage and has its part of step t+1 landed.
+//    fragment register sets (sub-step j+1 is read while j's MFMAs run, its
+//    B fragments before its A fragments).  One barrier per step, behind the
+//    third sub-step: every wave has read step t's stage and has its part of
+//    step t+1 landed.  The persistent kernels peel the first and last steps,
+//    so the steps between run with literal flags and no branch.
 //  * The loads are issued from inline asm, so the compiler neither knows nor
 //    waits for them: the vmcnt waits are explicit, and the compiler's own LDS
 //    waits stay exact (a known LDS DMA makes it wait for every LDS read).
