@@ -22,8 +22,8 @@ plain counting and sorting.  Each function names the passage it follows:
 
 Where the pages leave a step open, the reading taken here is stated at the
 function.  Parity pins: every function here is pinned by ``-m "not gpu"``
-tests (closed forms, brute force, invariants, worked examples under
-``tests/golden/``); none is "parity unpinned".
+tests (hand-worked examples, closed forms, brute force, invariants); none
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -33,8 +33,8 @@ import numpy as np
 
 __all__ = [
     "widen", "router_logits", "softmax", "topk", "route", "lookahead_hit",
-    "owner_of", "histogram", "host_sets", "even_split", "modeled_loads", "plan",
-    "split", "split_transfers", "colour_transfers", "permute", "gather_rows",
+    "histogram", "host_sets", "even_split", "modeled_loads", "plan",
+    "signed_move", "split", "split_transfers", "colour_transfers", "permute", "gather_rows",
     "silu", "swiglu", "moe_dense", "moe_via_groups", "combine", "spatial",
     "static_loads",
 ]
@@ -122,15 +122,12 @@ def lookahead_hit(idx_pred: np.ndarray, idx: np.ndarray) -> float:
 #     FreeBalance eq. 5 (predicted workload vector n_e)
 
 
-def owner_of(t: int, T: int, G: int) -> int:
-    """Data-parallel token ownership: contiguous blocks of T/G tokens per rank."""
-    return t // (T // G)
-
-
 def histogram(idx: np.ndarray, G: int, E: int) -> np.ndarray:
-    """counts[s][e] = number of pairs (t, j) with owner(t) = s and idx[t,j] = e.
-    Column sums are FreeBalance's workload vector n_e (eq. 5).  Ids outside
-    [0, E) are not counted."""
+    """counts[s][e] = number of pairs (t, j) with owner(t) = s and idx[t,j] = e,
+    where tokens are owned in contiguous blocks of T/G (data-parallel
+    attention: rank s owns tokens [s*T/G, (s+1)*T/G)).  Column sums are
+    FreeBalance's workload vector n_e (eq. 5).  Ids outside [0, E) are not
+    counted."""
     T = idx.shape[0]
     per = T // G
     counts = np.zeros((G, E), dtype=np.int64)
@@ -300,6 +297,18 @@ def colour_transfers(transfers) -> List[int]:
     return colours
 
 
+def signed_move(gap: int, shift: int, mass_u: int, mass_v: int) -> int:
+    """Tokens one transfer moves from u to v (negative: from v to u), given
+    gap = load[u] - load[v]: the gap divided by 2**shift and rounded toward
+    zero (shift 1: half the gap, so the pair's larger load can only fall),
+    then kept within the mass the giving side holds of the expert's pool,
+    i.e. clamped to [-mass_v, mass_u]."""
+    f = abs(gap) >> shift
+    if gap < 0:
+        f = -f
+    return max(-mass_v, min(mass_u, f))
+
+
 def split(c, home, replica, G: int, E: int, passes: int = 12, eps: int = 0,
           trace: Optional[list] = None):
     """All-integer per-step split of every replicated expert's remote pool
@@ -310,12 +319,11 @@ def split(c, home, replica, G: int, E: int, passes: int = 12, eps: int = 0,
     * Replicated experts start from the even split of the remote pool (hosts by
       ascending rank).  mass x[e][h] = pairs of e's pool currently on host h.
     * For each pass, for each round (colour) in order, for each transfer
-      t = (u, v, e) of the round (Relief Algorithm 1):
-        gap = load[u] - load[v];  delta = |gap| >> 1;
-        limit = mass on the heavier side (x[e][u] if gap > 0 else x[e][v]);
-        delta = min(delta, limit);
-        if delta > eps: move delta pairs from the heavier to the lighter rank,
-        updating load and x at once (Gauss-Seidel; the next round reads it).
+      t = (u, v, e) of the round (Relief, "The Relief Algorithm"): one signed
+      flow of e's pool between u and v -- half the load difference, rounded
+      toward zero and capped by what the giving side holds (``signed_move``)
+      -- applied at once if it exceeds eps in magnitude, so the next
+      transfer and round read the updated loads (Gauss-Seidel).
       Reading for experts with more than two hosts: the replica edges form a
       star around the home, and the limit is the giving host's own mass.
       Whole tokens instead of Q11.20, since hot experts exceed 2047 pairs.
@@ -350,21 +358,12 @@ def split(c, home, replica, G: int, E: int, passes: int = 12, eps: int = 0,
     for _p in range(passes):
         for rnd in rounds:
             for (u, v, e) in rnd:
-                gap = load[u] - load[v]
-                delta = abs(gap) >> 1
-                limit = x[e][u] if gap > 0 else x[e][v]
-                delta = min(delta, limit)
-                if delta > eps:
-                    if gap > 0:
-                        load[u] -= delta
-                        load[v] += delta
-                        x[e][u] -= delta
-                        x[e][v] += delta
-                    else:
-                        load[v] -= delta
-                        load[u] += delta
-                        x[e][v] -= delta
-                        x[e][u] += delta
+                f = signed_move(load[u] - load[v], 1, x[e][u], x[e][v])
+                if abs(f) > eps:
+                    load[u] -= f
+                    load[v] += f
+                    x[e][u] -= f
+                    x[e][v] += f
                     if trace is not None:
                         trace.append(max(load))
     for e, xe in x.items():

@@ -28,7 +28,7 @@ from typing import Dict, Sequence, Tuple
 
 import numpy as np
 
-from .moe_oracle import _remote_pool, colour_transfers, even_split, host_sets, split, split_transfers
+from .moe_oracle import _remote_pool, colour_transfers, even_split, host_sets, signed_move, split, split_transfers
 
 VARIANTS = ("relief", "no_reverse", "jacobi", "water_fill", "proportional", "hash", "libra_greedy")
 
@@ -97,15 +97,12 @@ def _pairwise(c, home, replica, G: int, E: int, passes: int, eps: int, reverse: 
                 gap = (snap[u] - snap[v]) if snapshot else (load[u] - load[v])
                 if gap <= 0 and not reverse:
                     continue
-                delta = abs(gap) >> (2 if snapshot else 1)
-                limit = x[e][u] if gap > 0 else x[e][v]
-                delta = min(delta, limit)
-                if delta > eps:
-                    a, b = (u, v) if gap > 0 else (v, u)
-                    load[a] -= delta
-                    load[b] += delta
-                    x[e][a] -= delta
-                    x[e][b] += delta
+                f = signed_move(gap, 2 if snapshot else 1, x[e][u], x[e][v])
+                if abs(f) > eps:
+                    load[u] -= f
+                    load[v] += f
+                    x[e][u] -= f
+                    x[e][v] += f
                     moved = True
         if not moved:
             break

@@ -195,3 +195,30 @@ def test_permute_invariants(seed, G, N):
         assert len(members) == expect                                  # sizes from counts and split
     x = O.gather_rows(np.arange(T)[:, None] * 10, perm, k)
     assert np.array_equal(x[:, 0], (perm // k) * 10)
+
+
+def test_static_loads_by_hand():
+    # no balancing: every pair of e is served by home(e).  Column sums of c are
+    # [6, 9, 10, 14]; homes [0, 0, 1, 2] give [6 + 9, 10, 14]; the scattered
+    # homes [2, 0, 2, 1] give [9, 14, 6 + 10].
+    c = np.array([[1, 2, 3, 4],
+                  [5, 6, 7, 8],
+                  [0, 1, 0, 2]], np.int64)
+    assert O.static_loads(c, np.array([0, 0, 1, 2]), 3, 4) == [15, 10, 14]
+    assert O.static_loads(c, np.array([2, 0, 2, 1]), 3, 4) == [9, 14, 16]
+    # the split with no replicas sends every pool home: the same loads
+    _, ld = O.split(c, np.array([2, 0, 2, 1]), None, 3, 4)
+    assert ld.tolist() == [9, 14, 16]
+
+
+def test_signed_move_closed_forms():
+    # half the gap rounded toward zero, toward the lighter side, capped by the
+    # giver's mass; shift 2 is the damped quarter-gap move
+    assert O.signed_move(7, 1, 10, 10) == 3
+    assert O.signed_move(-7, 1, 10, 10) == -3
+    assert O.signed_move(1, 1, 10, 10) == 0 and O.signed_move(-1, 1, 10, 10) == 0
+    assert O.signed_move(0, 1, 10, 10) == 0
+    assert O.signed_move(10, 1, 2, 10) == 2      # u gives, holds 2
+    assert O.signed_move(-10, 1, 10, 1) == -1    # v gives, holds 1
+    assert O.signed_move(-10, 1, 0, 10) == -5    # u's mass does not cap a move into u
+    assert O.signed_move(9, 2, 10, 10) == 2 and O.signed_move(-9, 2, 10, 10) == -2

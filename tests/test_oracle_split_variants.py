@@ -199,3 +199,64 @@ def test_stale_split_by_hand():
     # negative entries read as 0: 7 * (0, 1, 1) / 2 = (0, 3, 3) rem (0, 1, 1)
     prev[0] = [-4, 1, 1, 0]
     assert V.stale_split(c, home, rep, prev, G, E)[0][0].tolist() == [0, 4, 3, 0]
+
+
+def _two_pools_sharing_a_host():
+    """Three ranks, one expert each (home = rank).  Rank 0 replicates e1 and
+    e2, so e1's pool (its pairs owned by rank 2: 8) spreads over {0, 1} and
+    e2's pool (its pairs owned by rank 1: 8) over {0, 2}; both pools share
+    host 0.  Own tokens: rank 1 serves 10 of e1, rank 2 serves 10 of e2, rank
+    0 none.  Even split 4/4 and 4/4: loads [8, 14, 14]."""
+    G, E = 3, 3
+    home = np.array([0, 1, 2], np.int32)
+    rep = np.array([[1, 2], [-1, -1], [-1, -1]], np.int32)
+    c = np.array([[0, 0, 0],
+                  [0, 10, 8],
+                  [0, 8, 10]], np.int64)
+    return c, home, rep, G, E
+
+
+def test_water_fill_two_pools_by_hand_snapshot_not_sequential():
+    # Pass 1 reads the snapshot [8, 14, 14].  Levels (load less own mass):
+    # e1: host 0 at 4, host 1 at 10; filling R = 8 reaches z = 11 exactly
+    # ((11-4) + (11-10) = 8), so e1 -> {0: 7, 1: 1}; e2 the same over {0, 2}.
+    # Loads [14, 11, 11].  (Sequential filling would let e2 see e1's move:
+    # after e1, loads [11, 11, 14]; e2's levels 7 and 10 give z = 12 plus one
+    # token to host 0 -> {0: 6, 2: 2}, loads [13, 11, 12].)
+    c, home, rep, G, E = _two_pools_sharing_a_host()
+    hc, ld = V.split_variant(c, home, rep, G, E, "water_fill", passes=1)
+    assert ld.tolist() == [14, 11, 11]
+    assert hc[1].tolist() == [7, 1, 0] and hc[2].tolist() == [7, 0, 1]
+    # Pass 2 from [14, 11, 11]: levels 14-7 = 7 and 11-1 = 10; z = 12 takes
+    # 5 + 2 = 7, the token left goes to host 0 (level 7 <= 12, lowest rank):
+    # {0: 6, 1: 2}, e2 the same; loads [12, 12, 12].  Pass 3 reproduces it
+    # (levels 6 and 10, z = 12 takes exactly 8) and the loop stops.
+    hc, ld = V.split_variant(c, home, rep, G, E, "water_fill", passes=2)
+    assert ld.tolist() == [12, 12, 12]
+    assert hc[1].tolist() == [6, 2, 0] and hc[2].tolist() == [6, 0, 2]
+    hc12, ld12 = V.split_variant(c, home, rep, G, E, "water_fill", passes=12)
+    assert np.array_equal(hc12, hc) and np.array_equal(ld12, ld)
+
+
+def test_proportional_two_pools_by_hand():
+    # Pass 1, snapshot [8, 14, 14]: e1's levels 4 and 10 give weights 1/5 and
+    # 1/11, shares 8*11/16 = 5.5 and 8*5/16 = 2.5; floors 5 and 2, the tied
+    # remainder goes to the lower rank: {0: 6, 1: 2}; e2 the same.  Loads
+    # [12, 12, 12].  (Sequential: e1 first gives loads [10, 12, 14], then e2's
+    # levels 6 and 10 give 8*11/18 and 8*7/18 -> {0: 5, 2: 3}, loads
+    # [11, 12, 13].)
+    c, home, rep, G, E = _two_pools_sharing_a_host()
+    hc, ld = V.split_variant(c, home, rep, G, E, "proportional", passes=1)
+    assert ld.tolist() == [12, 12, 12]
+    assert hc[1].tolist() == [6, 2, 0] and hc[2].tolist() == [6, 0, 2]
+    # Pass 2 from [12, 12, 12]: levels 12-6 = 6 and 12-2 = 10, weights 1/7 and
+    # 1/11: 88/18 = 4.89 and 56/18 = 3.11 -> floors 4 and 3, the larger
+    # remainder (0.89) to host 0: {0: 5, 1: 3}; loads [10, 13, 13].
+    hc, ld = V.split_variant(c, home, rep, G, E, "proportional", passes=2)
+    assert ld.tolist() == [10, 13, 13]
+    assert hc[1].tolist() == [5, 3, 0] and hc[2].tolist() == [5, 0, 3]
+    # Pass 3 from [10, 13, 13]: levels 5 and 10, weights 1/6 and 1/11: 88/17 =
+    # 5.18 and 48/17 = 2.82 -> floors 5 and 2, the larger remainder (0.82) to
+    # host 1: {0: 5, 1: 3} again, so the loop stops there.
+    hc12, ld12 = V.split_variant(c, home, rep, G, E, "proportional", passes=12)
+    assert np.array_equal(hc12, hc) and np.array_equal(ld12, ld)
