@@ -16,7 +16,8 @@
  * (moelb_split_schedule, moelb_split_scheduled), split variants for
  * comparison (moelb_split_variant), an earlier step's split dealt again
  * (moelb_split_stale), FreeBalance's expert-swap planner (moelb_plan_swaps),
- * and the permutation in two phases (moelb_permute_local, moelb_permute_remote).
+ * the permutation in two phases (moelb_permute_local, moelb_permute_remote)
+ * and the FFN in stages (moelb_grouped_ffn_stages).
  *
  * Conventions for every entry point:
  *  - Plain C ABI.  Every pointer argument is DEVICE memory owned by the caller
@@ -338,18 +339,26 @@ int moelb_permute_remote(const void* h, const int32_t* idx, int T, int d, int k,
  *  states: pass moelb_permute's perm and the top-k).  Rows outside every
  *  computed group are not written.
  *  x          [rows_x,d]  dtype    rows (X_perm, or h when gather is given)
- *  group_off  [num_groups+1] int32 non-decreasing offsets, <= rows
+ *  group_off  [num_groups+1] int32 non-decreasing offsets in [0, rows]
  *  gather     [rows] int32 or NULL; gather_k >= 1
  *  w13        [E,2*inter,d] dtype  gate rows then up rows, K-contiguous
  *  w2         [E,d,inter]   dtype  K-contiguous
  *  ws         workspace of moelb_grouped_ffn_workspace_bytes(...) bytes
+ *             (schedule tables and the SwiGLU activations; no initial
+ *             contents needed)
  *  y          [rows,d]      dtype out
- *  events     NULL or 4 hipEvent_t recorded on `stream`: before the schedule
- *             kernel, before the gate/up GEMM, before the down GEMM, after it.
- *  Device offsets outside [0, rows] are clamped into it; gather entries
- *  outside [0, rows_x*gather_k) read row 0.
- * Requires rows >= 0, d % 8 == 0, inter % 8 == 0, E <= 256,
- * num_groups % E == 0 when rank >= 0, num_groups <= 32768.
+ *  Device offsets are clamped: group g covers [lo, hi) with lo =
+ *  clamp(group_off[g], 0, rows), hi = clamp(group_off[g+1], lo, rows).
+ *  Computed groups are taken expert by expert (e ascending, then g
+ *  ascending) and at most `rows` rows are computed in all; with offsets
+ *  that are not non-decreasing, groups can overlap (a row computed by
+ *  several groups gets one of their results) and rows past that total are
+ *  not computed.  Every row read or written stays inside the buffers either
+ *  way.  gather entries outside [0, rows_x*gather_k) read row 0.
+ * Requires rows >= 0, rows_x >= 1 when rows > 0, d % 8 == 0, inter % 8 == 0,
+ * E <= 256, num_groups % E == 0 when rank >= 0, num_groups <= 32768, and
+ * 32-bit byte offsets inside each operand (rows_x*d, rows*inter and
+ * 2*inter*d elements below 2^32 bytes).
  */
 size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, int E, int d, int inter,
                                          int dtype);
@@ -357,7 +366,29 @@ int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_
                       int num_groups, int E, int G, int rank,
                       const int32_t* gather, int gather_k,
                       int d, int inter, int dtype, const void* w13, const void* w2,
-                      void* ws, size_t ws_bytes, void* y, void* stream, void* const* events);
+                      void* ws, size_t ws_bytes, void* y, void* stream);
+
+/*
+ * The same FFN in stages, for callers that schedule or time them apart:
+ * MOELB_FFN_SCHEDULE (expert-major row order and tile tables, from group_off,
+ * rank and gather, into ws), MOELB_FFN_GATE_UP (x -> SwiGLU activations in
+ * ws), MOELB_FFN_DOWN (activations -> y).  `stages` is a bitwise OR of them;
+ * moelb_grouped_ffn runs MOELB_FFN_ALL.  A stage reads what the earlier
+ * stages left in ws, so the calls of one FFN take the same arguments and the
+ * same ws, in stage order on one stream.  Same requirements and errors as
+ * moelb_grouped_ffn; stages outside [1, MOELB_FFN_ALL] return MOELB_EINVAL.
+ */
+enum moelb_ffn_stage {
+  MOELB_FFN_SCHEDULE = 1,
+  MOELB_FFN_GATE_UP = 2,
+  MOELB_FFN_DOWN = 4,
+  MOELB_FFN_ALL = 7
+};
+int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, int rows,
+                             const int32_t* group_off, int num_groups, int E, int G, int rank,
+                             const int32_t* gather, int gather_k, int d, int inter, int dtype,
+                             const void* w13, const void* w2, void* ws, size_t ws_bytes,
+                             void* y, void* stream);
 
 /*
  * Top-k weighted combine (FreeBalance section 2.1: MoE(h) = sum_i W_i

@@ -51,7 +51,7 @@ constexpr int SCHED_MIN_BM = 64;
 
 struct FfnSched {
   int32_t* eoff;      // [E+1]   virtual row offset of each expert
-  int32_t* gvb;       // [num_groups] virtual row base of each group, -1 if not computed
+  int32_t* gvb;       // [num_groups] virtual row base of each group (capped at rows)
   int32_t* mt_e;      // [max_mtiles] expert of each M tile
   int32_t* mt_v0;     // [max_mtiles] first virtual row of each M tile
   int32_t* n_mtiles;  // [1]
@@ -97,20 +97,25 @@ inline size_t sched_layout(int rows, int num_groups, int E, int inter, int dtype
 // contiguous range inside e's range [eoff[e], eoff[e+1]); M tiles of BM rows
 // never straddle experts.  One workgroup; the group offsets are staged
 // through LDS in chunks (two passes: sizes per expert, then each group's
-// start), so no thread waits on a chain of global loads.
+// start), so no thread waits on a chain of global loads.  Group g covers the
+// clamped rows [lo, hi), lo = clamp(group_off[g], 0, rows), hi =
+// clamp(group_off[g+1], lo, rows); an unselected group counts as empty.  The
+// groups of one expert get consecutive ranges in group order, so gvb over
+// g = e, e+E, e+2E, ... is non-decreasing and the next group starts where
+// the previous one ends (the row map relies on this).
 constexpr int SCHED_CHUNK = 4096;
 
 __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ group_off, int num_groups, int E, int G,
                                                     int rank, int rows, int BM, FfnSched s) {
   __shared__ int goff[SCHED_CHUNK + 1];
-  __shared__ int ecount[MOELB_MAX_E];
   __shared__ int eoff[MOELB_MAX_E + 1];
   __shared__ int toff[MOELB_MAX_E + 1];
   const int tid = threadIdx.x;
   const int e = tid;
-  // walk the selected groups of expert e, chunk by chunk: add each group's
-  // size to run, and (write) record the group's start first
-  auto walk = [&](bool write, int& run) {
+  // walk the groups of expert e, chunk by chunk: add each selected group's
+  // size to run, and (write) record every group's start first, capped at rows
+  // (64-bit: offsets that overlap can add up past 2^31)
+  auto walk = [&](bool write, long long& run) {
     for (int base = 0; base < num_groups; base += SCHED_CHUNK) {
       const int cnt = min(SCHED_CHUNK, num_groups - base);
       __syncthreads();
@@ -121,13 +126,13 @@ __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ 
           const bool sel = rank < 0 || ((g / E) % G) == rank;
           const int lo = min(max(goff[g - base], 0), rows);
           const int hi = min(max(goff[g - base + 1], lo), rows);
-          if (write) s.gvb[g] = sel ? run : -1;
+          if (write) s.gvb[g] = (int)min(run, (long long)rows);
           if (sel) run += hi - lo;
         }
       }
     }
   };
-  int n = 0;
+  long long n = 0;
   walk(false, n);
   // expert offsets (clamped to rows) and M-tile offsets: two block scans
   // (Hillis-Steele over the 256 threads, one per expert)
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ 
     *s.n_mtiles = (int)tincl;
   }
   __syncthreads();
-  int start = e < E ? eoff[e] : 0;
+  long long start = e < E ? eoff[e] : 0;
   walk(true, start);
   if (e < E) {
     s.eoff[e] = eoff[e];
@@ -170,28 +175,36 @@ __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ 
   if (e == 0) s.eoff[E] = eoff[E];
 }
 
-// Virtual -> physical row map, and the row of x each virtual row reads (through
-// the gather, when the rows come straight from the unpermuted hidden states).
-// One thread per physical row q: its group by binary search over group_off.
+// Virtual -> physical row map, and the row of x each virtual row reads
+// (through the gather, when the rows come straight from the unpermuted hidden
+// states).  One thread per virtual row v < eoff[E]: its expert e is the last
+// one with eoff[e] <= v (offsets staged in LDS), its group the last group g
+// of e with gvb[g] <= v, and its physical row clamp(group_off[g]) + (v -
+// gvb[g]).  So every virtual row a GEMM tile can read is written, and with a
+// row in [0, rows) (by the schedule's construction, and clamped besides),
+// whatever the device offsets hold.
 __global__ __launch_bounds__(256) void rowmap_kernel(const int32_t* __restrict__ group_off, int num_groups, int E,
                                                      int rows, const int32_t* __restrict__ gather, int gather_k,
                                                      int rows_x, FfnSched s) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= rows) return;
-  // last group g with clamp(group_off[g]) <= q (clamped offsets are non-decreasing)
-  int lo = 0, hi = num_groups - 1;
+  __shared__ int eo[MOELB_MAX_E + 1];
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) eo[i] = s.eoff[i];
+  __syncthreads();
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= eo[E]) return;
+  int lo = 0, hi = E - 1;  // eo[0] = 0 <= v
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (min(max(group_off[mid], 0), rows) <= q) lo = mid; else hi = mid - 1;
+    if (eo[mid] <= v) lo = mid; else hi = mid - 1;
   }
-  const int g = lo;
-  const int glo = min(max(group_off[g], 0), rows);
-  const int ghi = min(max(group_off[g + 1], glo), rows);
-  if (q < glo || q >= ghi) return;  // in no group (or an empty one)
-  const int vb = s.gvb[g];
-  if (vb < 0) return;
-  const int v = vb + (q - glo);
-  if (v >= s.eoff[g % E + 1]) return;
+  const int e = lo;
+  int jl = 0, jh = (num_groups - 1 - e) / E;  // groups e, e+E, ... below num_groups
+  while (jl < jh) {
+    const int mid = (jl + jh + 1) >> 1;
+    if (s.gvb[e + mid * E] <= v) jl = mid; else jh = mid - 1;
+  }
+  const int g = e + jl * E;
+  const long long q64 = (long long)min(max(group_off[g], 0), rows) + (v - s.gvb[g]);
+  const int q = (int)min(max(q64, 0ll), (long long)rows - 1);
   s.rowmap[v] = q;
   const int src = gather ? gather[q] / gather_k : q;
   s.asrc[v] = (src >= 0 && src < rows_x) ? src : 0;
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_kernel(const uint16_t* __
     int v = v0 + r;
     v = v < vend ? v : v0;  // tiles always start with a valid row
     if (MODE == 0) {
-      aoff[i] = (uint32_t)s.asrc[v] * (uint32_t)d;
+      aoff[i] = (uint32_t)min(max(s.asrc[v], 0), rows_x - 1) * (uint32_t)d;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
       boff[i] = (uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d;
@@ -491,7 +504,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
     int v = v0 + r;
     v = v < vend ? v : v0;
     if (MODE == 0) {
-      aoff[j] = ((uint32_t)s.asrc[v] * (uint32_t)d + chunk * 8) * 2u;
+      aoff[j] = ((uint32_t)min(max(s.asrc[v], 0), rows_x - 1) * (uint32_t)d + chunk * 8) * 2u;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
       boff[j] = ((uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8) * 2u;
@@ -748,18 +761,19 @@ __device__ __forceinline__ int dl_out_row(const DlTile& c, const FfnSched& s, in
 }
 
 // Gate/up GEMM: the source rows of this lane's 8 DMA rows of tile c (rows
-// past the expert's end repeat its first row).
-__device__ __forceinline__ void dl_src_rows(const DlTile& c, const FfnSched& s, int wave, int lane, int (&src)[8]) {
+// past the expert's end repeat its first row), kept inside [0, rows_x).
+__device__ __forceinline__ void dl_src_rows(const DlTile& c, const FfnSched& s, int rows_x, int wave, int lane,
+                                            int (&src)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     int v = c.v0 + (wave * 8 + j) * 8 + (lane >> 3);
     v = v < c.vend ? v : c.v0;
-    src[j] = s.asrc[v];
+    src[j] = min(max(s.asrc[v], 0), rows_x - 1);
   }
 }
 
 template <int MODE>
-__global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16_t* __restrict__ x, int rows_x,
                                                                     const uint16_t* __restrict__ w, FfnSched s,
                                                                     int rows_y, int d, int inter, int ntn,
                                                                     uint16_t* __restrict__ y) {
@@ -811,9 +825,9 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
       }                                                                                                \
     }                                                                                                  \
   }
-  if (MODE == 0) dl_src_rows(cur, s, wave, lane, src);
+  if (MODE == 0) dl_src_rows(cur, s, rows_x, wave, lane, src);
   DL_OFFSETS(cur)
-  if (MODE == 0 && ntiles > 1) dl_src_rows(nxt, s, wave, lane, src);
+  if (MODE == 0 && ntiles > 1) dl_src_rows(nxt, s, rows_x, wave, lane, src);
   int out_row = MODE == 1 ? dl_out_row(cur, s, rows_y, wave, lane) : 0;
 
   f32x16_t acc[4][4];
@@ -1034,7 +1048,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
       }
     }
     // source rows of the tile after next (first used at its offsets switch)
-    if (MODE == 0 && has_nn) dl_src_rows(nn, s, wave, lane, src);
+    if (MODE == 0 && has_nn) dl_src_rows(nn, s, rows_x, wave, lane, src);
     cur = nxt;
     nxt = nn;
     out_row = next_out_row;
@@ -1088,10 +1102,7 @@ __global__ __launch_bounds__(256) void ffn_simt_kernel(const float* __restrict__
     const float* p = nullptr;
     if (v < vend) {
       if (MODE == 0) {
-        const int q = s.rowmap[v];
-        int src = gather ? gather[q] / gather_k : q;
-        src = (src >= 0 && src < rows_x) ? src : 0;
-        p = x + (size_t)src * d;
+        p = x + (size_t)min(max(s.asrc[v], 0), rows_x - 1) * d;
       } else {
         p = amid + (size_t)v * inter;
       }
@@ -1173,15 +1184,16 @@ extern "C" size_t moelb_grouped_ffn_workspace_bytes(int rows, int num_groups, in
   return sched_layout(rows, num_groups, E, inter, dtype, nullptr, nullptr);
 }
 
-extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_off, int num_groups, int E,
-                                 int G, int rank, const int32_t* gather, int gather_k, int d, int inter, int dtype,
-                                 const void* w13, const void* w2, void* ws, size_t ws_bytes, void* y, void* stream,
-                                 void* const* events) {
+extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, int rows, const int32_t* group_off,
+                                        int num_groups, int E, int G, int rank, const int32_t* gather, int gather_k,
+                                        int d, int inter, int dtype, const void* w13, const void* w2, void* ws,
+                                        size_t ws_bytes, void* y, void* stream) {
+  if (stages < 1 || stages > MOELB_FFN_ALL) return MOELB_EINVAL;
   if (rows < 0 || rows_x < 0 || num_groups < 1 || num_groups > 32768 || E < 1 || E > MOELB_MAX_E) return MOELB_EINVAL;
   if (d <= 0 || d % 8 != 0 || inter <= 0 || inter % 8 != 0 || !moelb_dtype_ok(dtype)) return MOELB_EINVAL;
   if (rank >= 0 && (G < 1 || rank >= G || num_groups % E != 0)) return MOELB_EINVAL;
   if (gather && gather_k < 1) return MOELB_EINVAL;
-  if (!group_off || !w13 || !w2 || (rows > 0 && (!x || !y))) return MOELB_EINVAL;
+  if (!group_off || !w13 || !w2 || (rows > 0 && (!x || !y || rows_x < 1))) return MOELB_EINVAL;
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w13) | reinterpret_cast<uintptr_t>(w2) |
        reinterpret_cast<uintptr_t>(y)) & 15)
     return MOELB_EINVAL;
@@ -1195,19 +1207,18 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
   FfnSched sc;
   sched_layout(rows, num_groups, E, inter, dtype, &sc, static_cast<char*>(ws));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto rec = [&](int i) {
-    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-  };
   const bool bf = dtype == MOELB_BF16;
   const int BM = bf ? MF_BM : SF_BM;
-  rec(0);
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows, BM,
-                     sc);
-  MOELB_CHECK_LAUNCH();
-  if (rows > 0)
-    hipLaunchKernelGGL(rowmap_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, group_off, num_groups, E, rows, gather,
-                       gather_k, rows_x, sc);
-  MOELB_CHECK_LAUNCH();
+  const bool run_up = stages & MOELB_FFN_GATE_UP, run_down = stages & MOELB_FFN_DOWN;
+  if (stages & MOELB_FFN_SCHEDULE) {
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows,
+                       BM, sc);
+    MOELB_CHECK_LAUNCH();
+    if (rows > 0)
+      hipLaunchKernelGGL(rowmap_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, group_off, num_groups, E, rows,
+                         gather, gather_k, rows_x, sc);
+    MOELB_CHECK_LAUNCH();
+  }
   const size_t mtiles = (size_t)(rows + BM - 1) / BM + E;
   if (bf) {
     if (!moelb_allow_lds(ffn_mfma_kernel<0>, MF_LDS_BYTES) || !moelb_allow_lds(ffn_mfma_kernel<1>, MF_LDS_BYTES))
@@ -1223,48 +1234,58 @@ extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int3
         (pers0 && !moelb_allow_lds(ffn_persistent_kernel<0>, DL_LDS_BYTES)) ||
         (pers1 && !moelb_allow_lds(ffn_persistent_kernel<1>, DL_LDS_BYTES)))
       return MOELB_ELAUNCH;
-    rec(1);
-    if (pers0)
-      hipLaunchKernelGGL(ffn_persistent_kernel<0>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13), sc, rows, d, inter, ntn0,
-                         static_cast<uint16_t*>(sc.amid));
-    else if (dma0)
-      hipLaunchKernelGGL(ffn_mfma_dma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13),
-                         sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
-    else
-      hipLaunchKernelGGL(ffn_mfma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(x), rows_x, gather, gather_k, static_cast<const uint16_t*>(w13),
-                         sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
-    MOELB_CHECK_LAUNCH();
-    rec(2);
-    if (pers1)
-      hipLaunchKernelGGL(ffn_persistent_kernel<1>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
-                         nullptr, static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1,
-                         static_cast<uint16_t*>(y));
-    else if (dma1)
-      hipLaunchKernelGGL(ffn_mfma_dma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
-                         d, inter, ntn1, static_cast<uint16_t*>(y));
-    else
-      hipLaunchKernelGGL(ffn_mfma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
-                         static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1, static_cast<const uint16_t*>(w2), sc,
-                         d, inter, ntn1, static_cast<uint16_t*>(y));
-    MOELB_CHECK_LAUNCH();
+    if (run_up) {
+      if (pers0)
+        hipLaunchKernelGGL(ffn_persistent_kernel<0>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(x), rows_x, static_cast<const uint16_t*>(w13), sc, rows, d,
+                           inter, ntn0, static_cast<uint16_t*>(sc.amid));
+      else if (dma0)
+        hipLaunchKernelGGL(ffn_mfma_dma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(x), rows_x, gather, gather_k,
+                           static_cast<const uint16_t*>(w13), sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
+      else
+        hipLaunchKernelGGL(ffn_mfma_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(x), rows_x, gather, gather_k,
+                           static_cast<const uint16_t*>(w13), sc, d, inter, ntn0, static_cast<uint16_t*>(sc.amid));
+      MOELB_CHECK_LAUNCH();
+    }
+    if (run_down) {
+      if (pers1)
+        hipLaunchKernelGGL(ffn_persistent_kernel<1>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                           nullptr, rows, static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1,
+                           static_cast<uint16_t*>(y));
+      else if (dma1)
+        hipLaunchKernelGGL(ffn_mfma_dma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), DL_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1,
+                           static_cast<const uint16_t*>(w2), sc, d, inter, ntn1, static_cast<uint16_t*>(y));
+      else
+        hipLaunchKernelGGL(ffn_mfma_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(MF_THREADS), MF_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(sc.amid), rows, nullptr, 1,
+                           static_cast<const uint16_t*>(w2), sc, d, inter, ntn1, static_cast<uint16_t*>(y));
+      MOELB_CHECK_LAUNCH();
+    }
   } else {
     const int ntn0 = (inter + 31) / 32;
     const int ntn1 = (d + 63) / 64;
-    rec(1);
-    hipLaunchKernelGGL(ffn_simt_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(256), 0, s, static_cast<const float*>(x),
-                       rows_x, gather, gather_k, static_cast<const float*>(w13), sc, d, inter, ntn0,
-                       static_cast<float*>(sc.amid));
-    MOELB_CHECK_LAUNCH();
-    rec(2);
-    hipLaunchKernelGGL(ffn_simt_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(256), 0, s,
-                       static_cast<const float*>(sc.amid), rows, nullptr, 1, static_cast<const float*>(w2), sc, d,
-                       inter, ntn1, static_cast<float*>(y));
-    MOELB_CHECK_LAUNCH();
+    if (run_up) {
+      hipLaunchKernelGGL(ffn_simt_kernel<0>, dim3(mtiles * ntn0 + 8), dim3(256), 0, s, static_cast<const float*>(x),
+                         rows_x, gather, gather_k, static_cast<const float*>(w13), sc, d, inter, ntn0,
+                         static_cast<float*>(sc.amid));
+      MOELB_CHECK_LAUNCH();
+    }
+    if (run_down) {
+      hipLaunchKernelGGL(ffn_simt_kernel<1>, dim3(mtiles * ntn1 + 8), dim3(256), 0, s,
+                         static_cast<const float*>(sc.amid), rows, nullptr, 1, static_cast<const float*>(w2), sc, d,
+                         inter, ntn1, static_cast<float*>(y));
+      MOELB_CHECK_LAUNCH();
+    }
   }
-  rec(3);
   return MOELB_OK;
+}
+
+extern "C" int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_off, int num_groups, int E,
+                                 int G, int rank, const int32_t* gather, int gather_k, int d, int inter, int dtype,
+                                 const void* w13, const void* w2, void* ws, size_t ws_bytes, void* y, void* stream) {
+  return moelb_grouped_ffn_stages(MOELB_FFN_ALL, x, rows_x, rows, group_off, num_groups, E, G, rank, gather, gather_k,
+                                  d, inter, dtype, w13, w2, ws, ws_bytes, y, stream);
 }

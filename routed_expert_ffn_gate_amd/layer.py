@@ -49,7 +49,8 @@ def to_host(t: torch.Tensor) -> np.ndarray:
 
 
 class HipEvents:
-    """hipEvent_t handles from libamdhip64 (the events the library records)."""
+    """hipEvent_t handles from libamdhip64, recorded on a stream between
+    entry-point calls (the step's stage marks)."""
 
     def __init__(self, n: int):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -57,9 +58,6 @@ class HipEvents:
         for e in self.ev:
             if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
-
-    def handles(self, i0: int, n: int):
-        return [self.ev[i].value for i in range(i0, i0 + n)]
 
     def record(self, i: int, stream) -> None:
         s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream)
@@ -165,6 +163,9 @@ class MoELayer:
         # the placement in force and for the next layer's
         self.sched_cur = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, **i32)
         self.sched_next = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, **i32)
+        # advance(): the next layer's plan becomes the one in force while the
+        # next step writes its own next plan into the other buffer
+        self.replica_spare = torch.empty((G, N), **i32)
         if balancer == "freebalance":
             self.home_next = torch.empty((E,), **i32)
             self.swaps_next = torch.empty((E // 2 + 1, 2), **i32)
@@ -208,6 +209,32 @@ class MoELayer:
             M.moelb_plan(self.counts_next, home, self.L, self.replica_next, self.plan_load_next, stream=self.side)
             M.moelb_split_schedule(home, self.replica_next, self.sched_next, self.G, stream=self.side)
 
+    def advance(self) -> torch.Tensor:
+        """Make the plan this step made for the next layer the one in force
+        (Libra "Key Ideas": the lookahead plan of layer i+1 is applied at
+        layer i+1): returns its replica table, to pass as ``replica_cur`` to
+        the next step, and the split schedule made beside it becomes the one
+        the split reads.  The buffers are swapped, not copied, so the next
+        step's own plan does not overwrite the placement in force."""
+        self.replica_next, self.replica_spare = self.replica_spare, self.replica_next
+        self.sched_cur, self.sched_next = self.sched_next, self.sched_cur
+        return self.replica_spare
+
+    def _ffn(self, h, w13, w2, mark=None, stream=None):
+        """The grouped FFN over every group; with ``mark``, its three stages
+        are launched apart and marks 8..11 recorded around them."""
+        x = h if self.gather_rows else self.x_perm
+        kw = dict(G=self.G, stream=stream)
+        if self.gather_rows:
+            kw.update(gather=self.perm, gather_k=self.k)
+        if mark is None:
+            M.moelb_grouped_ffn(x, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, **kw)
+            return
+        for i, stage in enumerate((M.MOELB_FFN_SCHEDULE, M.MOELB_FFN_GATE_UP, M.MOELB_FFN_DOWN)):
+            mark(8 + i)
+            M.moelb_grouped_ffn_stages(stage, x, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, **kw)
+        mark(11)
+
     def _out(self):
         return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
                        self.plan_load_next, self.host_count, self.load, self.group_off, self.perm, self.pos,
@@ -217,9 +244,9 @@ class MoELayer:
     def step(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None, shared_w2=None,
              stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
         """One layer step.  With ``events``, marks ev_base+0..7 bracket the
-        stages of STAGES on the step's stream, ev_base+8..11 are recorded
-        inside the grouped FFN (before its schedule, gate/up GEMM and down GEMM
-        kernels, and after), ev_base+12..13 bracket the side stream's work."""
+        stages of STAGES on the step's stream, ev_base+8..11 bracket the
+        grouped FFN's three stages (schedule, gate/up GEMM, down GEMM, each
+        launched on its own), ev_base+12..13 bracket the side stream's work."""
         ev = events
         s0 = stream if stream is not None else torch.cuda.current_stream()
 
@@ -248,13 +275,7 @@ class MoELayer:
                         self.ws_perm, self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None,
                         d=self.d, dtype=M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32, stream=s0)
         mark(4)
-        ffn_ev = ev.handles(ev_base + 8, 4) if ev is not None else None
-        if self.gather_rows:
-            M.moelb_grouped_ffn(h, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                gather=self.perm, gather_k=self.k, stream=s0, events=ffn_ev)
-        else:
-            M.moelb_grouped_ffn(self.x_perm, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                stream=s0, events=ffn_ev)
+        self._ffn(h, w13, w2, mark if ev is not None else None, stream=s0)
         if self.shared is not None:
             M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
                                 stream=s0)

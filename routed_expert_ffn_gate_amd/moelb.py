@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence
+from typing import Optional
 
 import torch
 
@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoelb.so")
 
 MOELB_OK, MOELB_EINVAL, MOELB_ELAUNCH, MOELB_EWORKSPACE = 0, 1, 2, 3
 MOELB_F32, MOELB_BF16 = 0, 1
+MOELB_FFN_SCHEDULE, MOELB_FFN_GATE_UP, MOELB_FFN_DOWN, MOELB_FFN_ALL = 1, 2, 4, 7
 
 # name -> (restype, argtypes)
 _P, _I, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -39,7 +40,9 @@ SIGNATURES = {
     "moelb_permute_local": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moelb_permute_remote": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moelb_grouped_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "moelb_grouped_ffn": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]),
+    "moelb_grouped_ffn": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, _P]),
+    "moelb_grouped_ffn_stages": (_I, [_I, _P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P,
+                                      _P]),
     "moelb_combine": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
 }
 
@@ -215,17 +218,24 @@ def moelb_grouped_ffn_workspace_bytes(rows, num_groups, E, d, inter, dtype) -> i
     return int(lib().moelb_grouped_ffn_workspace_bytes(rows, num_groups, E, d, inter, dtype))
 
 
-def moelb_grouped_ffn(x, rows, group_off, E, w13, w2, ws, y, G=1, rank=-1, gather=None, gather_k=1, stream=None,
-                      events: Optional[Sequence] = None):
+def moelb_grouped_ffn(x, rows, group_off, E, w13, w2, ws, y, G=1, rank=-1, gather=None, gather_k=1, stream=None):
     rows_x, d = x.shape
     inter = w2.shape[-1]
     num_groups = group_off.numel() - 1
-    ev = None
-    if events is not None:
-        ev = (ctypes.c_void_p * 4)(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
     _check(lib().moelb_grouped_ffn(_p(x), rows_x, rows, _p(group_off), num_groups, E, G, rank, _p(gather), gather_k,
                                    d, inter, dtype_code(x), _p(w13), _p(w2), _p(ws), ws.numel() * ws.element_size(),
-                                   _p(y), _stream(stream), ev), "moelb_grouped_ffn")
+                                   _p(y), _stream(stream)), "moelb_grouped_ffn")
+
+
+def moelb_grouped_ffn_stages(stages, x, rows, group_off, E, w13, w2, ws, y, G=1, rank=-1, gather=None, gather_k=1,
+                             stream=None):
+    rows_x, d = x.shape
+    inter = w2.shape[-1]
+    num_groups = group_off.numel() - 1
+    _check(lib().moelb_grouped_ffn_stages(stages, _p(x), rows_x, rows, _p(group_off), num_groups, E, G, rank,
+                                          _p(gather), gather_k, d, inter, dtype_code(x), _p(w13), _p(w2), _p(ws),
+                                          ws.numel() * ws.element_size(), _p(y), _stream(stream)),
+           "moelb_grouped_ffn_stages")
 
 
 def moelb_combine(y, pos, wts, out, shared=None, stream=None):

@@ -35,7 +35,7 @@ int main(void) {
   EXPECT(moelb_permute(NULL, P, 64, 8, 2, 8, 4, 1, MOELB_BF16, P, P, P, P, need - 1, P, P, P, NULL, NULL) ==
          MOELB_EWORKSPACE);
   /* grouped FFN: d not a multiple of 8; combine: k above the limit */
-  EXPECT(moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 12, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL, NULL) ==
+  EXPECT(moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 12, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
          MOELB_EINVAL);
   EXPECT(moelb_combine(P, 8, P, P, 4, 17, 8, MOELB_BF16, NULL, P, NULL) == MOELB_EINVAL);
   printf("%s\n", fails ? "failed" : "ok");

@@ -77,8 +77,14 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert need > 0
     assert lib.moelb_permute(N, P, 64, 8, 2, 8, 4, 1, 1, P, P, P, P, need - 1, P, P, P, N, N) == 3
     # grouped ffn: rank filter needs num_groups % E == 0; workspace too small
-    assert lib.moelb_grouped_ffn(P, 8, 8, P, 7, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P, N, N) == 1
-    assert lib.moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 16, P, N, N) == 3
+    assert lib.moelb_grouped_ffn(P, 8, 8, P, 7, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P, N) == 1
+    assert lib.moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 16, P, N) == 3
+    # rows > 0 with no source rows; stage masks outside [1, 7]
+    assert lib.moelb_grouped_ffn(P, 0, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P, N) == 1
+    for stages in (0, 8, -1):
+        assert lib.moelb_grouped_ffn_stages(stages, P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P,
+                                            N) == 1
+    assert lib.moelb_grouped_ffn_stages(2, P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 16, P, N) == 3
     # combine: k out of range; misaligned output
     assert lib.moelb_combine(P, 8, P, P, 4, 17, 8, 1, N, P, N) == 1
     assert lib.moelb_combine(P, 8, P, P, 4, 2, 8, 1, N, ctypes.c_void_p(18), N) == 1
