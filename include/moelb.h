@@ -299,6 +299,26 @@ int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E,
                   void* stream);
 
 /*
+ * moelb_permute without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc).  The workspace is a fixed array of
+ * MOELB_PERMUTE_NOALLOC_WS_BYTES in device memory, one per device the
+ * library runs on, held until the process ends; the call allocates and
+ * frees nothing.  Same arguments (less ws, ws_bytes), outputs and errors as
+ * moelb_permute, plus MOELB_EWORKSPACE (nothing launched) when
+ * moelb_permute_workspace_bytes(T, k, E, G) exceeds that size, and
+ * MOELB_ELAUNCH if the array's device address cannot be obtained.  Every
+ * call on a device shares that device's array: calls that overlap on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller.  No initial contents are needed.
+ */
+#define MOELB_PERMUTE_NOALLOC_WS_BYTES (32u << 20)
+int moelb_permute_noalloc(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                          int dtype, const int32_t* home, const int32_t* replica,
+                          const int32_t* host_count, int32_t* group_off, int32_t* perm, int32_t* pos,
+                          void* x_perm, void* stream);
+
+/*
  * The same permutation in two phases (Libra README "Key Ideas": MoE_local
  * starts right after gating; the token sharding of the remote pairs runs
  * beside it).  Calling moelb_permute_local and then moelb_permute_remote with

@@ -391,9 +391,10 @@ extern "C" size_t moelb_permute_workspace_bytes(int T, int k, int E, int G) {
   return ws_layout(T, k, E, G, nullptr, nullptr);
 }
 
-static int permute_check(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
-                         const int32_t* home, const int32_t* replica, void* ws, size_t ws_bytes,
-                         const int32_t* group_off, const int32_t* perm, const int32_t* pos, const void* x_perm) {
+// Arguments other than the workspace.
+static int permute_args(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
+                        const int32_t* home, const int32_t* replica, const int32_t* group_off, const int32_t* perm,
+                        const int32_t* pos, const void* x_perm) {
   if (T < 0 || d <= 0 || d % 8 != 0 || k < 1 || k > MOELB_MAX_K || E < 1 || E > MOELB_MAX_E || G < 1 ||
       G > MOELB_MAX_G || N < 0 || N > MOELB_MAX_N || T % G != 0 || !moelb_dtype_ok(dtype))
     return MOELB_EINVAL;
@@ -401,6 +402,14 @@ static int permute_check(const void* h, const int32_t* idx, int T, int d, int k,
   if (x_perm && !h) return MOELB_EINVAL;
   if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(x_perm)) & 15) return MOELB_EINVAL;
   if ((size_t)T * k > 0x7fffffffull) return MOELB_EINVAL;
+  return MOELB_OK;
+}
+
+static int permute_check(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N, int dtype,
+                         const int32_t* home, const int32_t* replica, void* ws, size_t ws_bytes,
+                         const int32_t* group_off, const int32_t* perm, const int32_t* pos, const void* x_perm) {
+  const int st = permute_args(h, idx, T, d, k, E, G, N, dtype, home, replica, group_off, perm, pos, x_perm);
+  if (st != MOELB_OK) return st;
   const size_t need = ws_layout(T, k, E, G, nullptr, nullptr);
   if (!ws || ws_bytes < need) return MOELB_EWORKSPACE;
   return MOELB_OK;
@@ -447,6 +456,46 @@ extern "C" int moelb_permute(const void* h, const int32_t* idx, int T, int d, in
                                x_perm);
   if (st != MOELB_OK) return st;
   if (!host_count) return MOELB_EINVAL;
+  return permute_launch(false, h, idx, T, d, k, E, G, N, dtype, home, replica, host_count, ws, group_off, perm, pos,
+                        x_perm, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- no-allocation form
+
+// Workspace of moelb_permute_noalloc: a fixed array in device memory (one per
+// device the library runs on, held until the process ends).  Its host-side
+// name is not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[MOELB_PERMUTE_NOALLOC_WS_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the first call made with that device current) and remembered; NULL if the
+// lookup fails.
+static void* scratch_address() {
+  static std::mutex mu;
+  static std::vector<std::pair<int, void*>> known;  // (device, address)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& x : known)
+    if (x.first == dev) return x.second;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  known.emplace_back(dev, p);
+  return p;
+}
+
+extern "C" int moelb_permute_noalloc(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,
+                                     int dtype, const int32_t* home, const int32_t* replica,
+                                     const int32_t* host_count, int32_t* group_off, int32_t* perm, int32_t* pos,
+                                     void* x_perm, void* stream) {
+  // arguments, then the workspace size, both before any device call
+  const int st = permute_args(h, idx, T, d, k, E, G, N, dtype, home, replica, group_off, perm, pos, x_perm);
+  if (st != MOELB_OK) return st;
+  if (!host_count) return MOELB_EINVAL;
+  if (ws_layout(T, k, E, G, nullptr, nullptr) > MOELB_PERMUTE_NOALLOC_WS_BYTES) return MOELB_EWORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MOELB_ELAUNCH;
   return permute_launch(false, h, idx, T, d, k, E, G, N, dtype, home, replica, host_count, ws, group_off, perm, pos,
                         x_perm, static_cast<hipStream_t>(stream));
 }
