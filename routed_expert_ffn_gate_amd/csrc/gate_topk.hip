@@ -16,8 +16,8 @@
 // step); router rows go straight from global/L2 into registers, since each
 // wave needs only its own columns.  The epilogue writes biased fp32 logits to
 // LDS (one token half at a time) and 4 lanes per token and direction select
-// the top-(k+1) with a register insertion list, merged across the 4 lanes with
-// two xor shuffles.
+// the top-(k+2) with a register insertion list, merged across the 4 lanes with
+// two xor shuffles; the selection is exact (see topk_epilogue).
 #include "common.h"
 
 namespace {
@@ -27,27 +27,52 @@ constexpr int GATE_BK = 64;        // K per pipeline step
 constexpr int GATE_THREADS = 512;  // 8 waves
 constexpr int A_STRIDE = GATE_BK + 8;  // bf16 elements per LDS row (16 B pad)
 
-// Selection key of logit v of expert id: the float's bits mapped to an
-// order-preserving unsigned integer, the low 8 bits replaced by 255 - id.  A
-// larger key is a larger logit, equal logits rank the lower id first; logits
-// that agree in their top 24 bits (within 2^-15 relative of each other, far
-// inside the near-tie band of a k/k+1 gap below 1e-3) are ranked by id.  The
-// selected ids then read back their exact logits.
-__device__ __forceinline__ uint32_t topk_key(float v, int id) {
-  uint32_t b = __float_as_uint(v);
-  b ^= (b & 0x80000000u) ? 0xffffffffu : 0x80000000u;
-  return (b & 0xffffff00u) | (uint32_t)(255 - id);
+// Selection keys of logit v of expert id: the float's bits mapped to an
+// order-preserving unsigned integer, followed by 255 - id, so a larger key is
+// a larger logit and equal logits rank the lower id first.  The fast key
+// keeps the top 24 bits of the logit (logits within 2^-15 relative of each
+// other share a bucket and rank by id); the exact key keeps all 32.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return b ^ ((b & 0x80000000u) ? 0xffffffffu : 0x80000000u);
 }
+__device__ __forceinline__ uint32_t topk_key(float v, int id) {
+  return (ordered_bits(v) & 0xffffff00u) | (uint32_t)(255 - id);
+}
+__device__ __forceinline__ uint64_t topk_key_exact(float v, int id) {
+  return ((uint64_t)ordered_bits(v) << 8) | (uint64_t)(255 - id);
+}
+__device__ __forceinline__ uint32_t make_key(float v, int id, uint32_t) { return topk_key(v, id); }
+__device__ __forceinline__ uint64_t make_key(float v, int id, uint64_t) { return topk_key_exact(v, id); }
 
 // Sorted (descending) insertion into a register list of KL keys: one max and
 // one min per list entry.
-template <int KL>
-__device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
+template <int KL, typename Key>
+__device__ __forceinline__ void list_insert(Key (&l)[KL], Key x) {
 #pragma unroll
   for (int i = 0; i < KL; ++i) {
-    const uint32_t hi = max(x, l[i]);
-    x = min(x, l[i]);
+    const Key hi = x > l[i] ? x : l[i];
+    x = x > l[i] ? l[i] : x;
     l[i] = hi;
+  }
+}
+
+// The KL largest keys of a token's E logits in `row`: each of the token's lpt
+// lanes (sub = 0..lpt-1) scans every lpt-th logit, then the partial lists are
+// merged across those lanes (xor shuffles), so every lane ends with the whole
+// list.  All lanes of the wave take part (inactive tokens scan nothing).
+template <int KL, typename Key>
+__device__ __forceinline__ void select_keys(const float* row, bool active, int E, int sub, int lpt, Key (&l)[KL]) {
+#pragma unroll
+  for (int i = 0; i < KL; ++i) l[i] = 0;  // below every real key
+  if (active)
+    for (int e = sub; e < E; e += lpt) list_insert<KL>(l, make_key(row[e], e, Key(0)));
+  for (int m = 1; m < lpt; m <<= 1) {
+    Key p[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) p[i] = __shfl_xor(l[i], m, MOELB_WAVE);
+#pragma unroll
+    for (int i = 0; i < KL; ++i) list_insert<KL>(l, p[i]);
   }
 }
 
@@ -56,6 +81,14 @@ __device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
 // The 512 threads split into directions (two if has_next), then tokens of
 // `lpt` adjacent lanes (a power of two, 2..8): direction = tid / per_dir,
 // token = (tid % per_dir) / lpt, sub = tid % lpt.
+//
+// Selection is exact: the k+2 largest fast keys are found first.  If entries
+// k and k+1 fall in different buckets, no logit outside the first k+1
+// entries shares entry k's bucket, so those entries are exactly the k+1
+// largest logits; entries inside one bucket are then re-ordered by their
+// exact logits where two adjacent ones share a bucket.  If entries k and k+1
+// share a bucket (rare), the token is selected again with exact keys (the
+// whole wave runs that pass, and only such tokens keep its result).
 template <int KL>
 __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int tok0, int T, int E, int k,
                               bool has_next, int32_t* __restrict__ idx, float* __restrict__ wts,
@@ -67,24 +100,49 @@ __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int
   const int sub = tid & (lpt - 1);
   const bool active = tl < ntok;
   const int t = tok0 + tl;
-  uint32_t l[KL];
-#pragma unroll
-  for (int i = 0; i < KL; ++i) l[i] = 0u;  // below every real key
   const float* row = z + tl * stride + dir * E;
-  if (active) {
-    for (int e = sub; e < E; e += lpt) list_insert<KL>(l, topk_key(row[e], e));
-  }
-  // merge the partial lists of the token's lanes (sub ^ 1, sub ^ 2, ...)
-  for (int m = 1; m < lpt; m <<= 1) {
-    uint32_t p[KL];
-#pragma unroll
-    for (int i = 0; i < KL; ++i) p[i] = __shfl_xor(l[i], m, MOELB_WAVE);
-#pragma unroll
-    for (int i = 0; i < KL; ++i) list_insert<KL>(l, p[i]);
-  }
+  uint32_t l[KL];
+  select_keys<KL>(row, active, E, sub, lpt, l);
   int li[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(l[i] & 0xffu), E - 1);  // unused entries stay in the row
+  // buckets of entries k and k+1 (k is a runtime value: no dynamic register indexing)
+  uint32_t bk = 0u, bk1 = 1u;
+  bool tie_run = false;  // two adjacent entries among 0..k share a bucket
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    if (j == k) bk = l[j] >> 8;
+    if (j == k + 1) bk1 = l[j] >> 8;
+    if (j + 1 < KL && j + 1 <= k && (l[j] >> 8) == (l[j + 1] >> 8)) tie_run = true;
+  }
+  const bool straddle = active && k + 2 <= E && bk == bk1;
+  if (__ballot(straddle) != 0ull) {
+    uint64_t lx[KL];
+    select_keys<KL>(row, active, E, sub, lpt, lx);
+    if (straddle) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(lx[i] & 0xffu), E - 1);
+    }
+  }
+  if (active && tie_run && !straddle) {
+    // order entries 0..k by exact logit (descending), equal logits by id
+    // (odd-even transposition: KL rounds sort up to KL entries)
+    float v[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) v[j] = row[li[j]];
+#pragma unroll
+    for (int r = 0; r < KL; ++r)
+#pragma unroll
+      for (int j = r & 1; j + 1 < KL; j += 2)
+        if (j + 1 <= k && (v[j + 1] > v[j] || (v[j + 1] == v[j] && li[j + 1] < li[j]))) {
+          const float tv = v[j];
+          v[j] = v[j + 1];
+          v[j + 1] = tv;
+          const int ti = li[j];
+          li[j] = li[j + 1];
+          li[j + 1] = ti;
+        }
+  }
   if (dir == 0) {
     // softmax denominator over all E logits of this token (no weights wanted:
     // a lookahead-only block of the split launch)
@@ -106,7 +164,7 @@ __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int
         float g = INFINITY;
 #pragma unroll
         for (int j = 1; j < KL; ++j)
-          if (j == k && k < E) g = fabsf(row[li[j - 1]] - row[li[j]]);
+          if (j == k && k < E) g = row[li[j - 1]] - row[li[j]];
         gap[t] = g;
       }
     }
@@ -631,18 +689,18 @@ extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dt
     const bool fused = dma_ok && N % 64 == 0 && NF <= nfmax;
     if (split || fused) {
       const int nf = split ? NFs : NF;
-      if (k <= 2) return launch_dma<3>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      if (k <= 4) return launch_dma<5>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      if (k <= 8) return launch_dma<9>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      return launch_dma<17>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 2) return launch_dma<4>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 4) return launch_dma<6>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 8) return launch_dma<10>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      return launch_dma<18>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
     }
-    if (k <= 2) return launch_bf16<3>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    if (k <= 4) return launch_bf16<5>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    if (k <= 8) return launch_bf16<9>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-    return launch_bf16<17>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    if (k <= 2) return launch_bf16<4>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    if (k <= 4) return launch_bf16<6>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    if (k <= 8) return launch_bf16<10>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+    return launch_bf16<18>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
   }
-  if (k <= 2) return launch_f32<3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-  if (k <= 4) return launch_f32<5>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-  if (k <= 8) return launch_f32<9>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
-  return launch_f32<17>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  if (k <= 2) return launch_f32<4>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  if (k <= 4) return launch_f32<6>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  if (k <= 8) return launch_f32<10>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
+  return launch_f32<18>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
 }

@@ -105,7 +105,6 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
 
 def check_gate(run: LayerRun) -> dict:
     cfg, li, g = run.cfg, run.li, run.out
-    tol = TOL[cfg.dtype]
     idx_o, w_o, gap_o, idxn_o, z = O.route(li.h, li.w_cur, li.b_cur, li.w_next, li.b_next, cfg.k, cfg.dtype)
     h64 = O.widen(li.h, cfg.dtype)
     zn = O.router_logits(h64, O.widen(li.w_next, cfg.dtype), li.b_next)
@@ -139,8 +138,11 @@ def check_gate(run: LayerRun) -> dict:
     res = dict(near_ties=int(near.sum()), near_ties_next=int(near_n.sum()), idx_mismatch=bad,
                order_mismatch=order_bad, idx_next_mismatch=bad_next, max_rel_w=worst_w, max_gap_err=gap_err)
     assert bad == 0 and bad_next == 0 and order_bad == 0, res
-    assert worst_w <= tol, res
-    assert gap_err <= 1e-3, res
+    # router weights and the gap are fp32 outputs (fp32 logits from fp32
+    # accumulation): the fp32 bar, relative for the weights, and in logit
+    # units for the gap (a difference of two O(1..10) logits)
+    assert worst_w <= TOL["f32"], res
+    assert gap_err <= 1e-4, res
     return res
 
 
