@@ -91,33 +91,65 @@ def routing_stats(cfg, layer, idx_pred, home):
             "spatial_split": round(sp(split), 4)}
 
 
-def cpu_baseline(cfg, li, w13, w2, shared, ntok):
-    """The oracle as it stands, on the first ``ntok`` tokens of the workload."""
-    import numpy as np
-    from oracle import moe_oracle as O
+def host_cpu():
+    """CPU model, the cores this process may run on, and the BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = 1
+    return model, cores, blas
+
+
+def cpu_baseline(cfg, li, w13, w2, shared, ntok):
+    """The oracle as it stands, on the first ``ntok`` tokens of the workload:
+    the whole layer step in fp64 (route with lookahead, prologue routing,
+    three histograms, both plans, split, permutation, grouped FFN and
+    combine), each stage timed."""
+    from oracle import moe_oracle as O
+    model, cores, blas = host_cpu()
     G, E, k = cfg.G, cfg.E, cfg.k
-    t0 = time.perf_counter()
+    st = {}
+    t_all = time.perf_counter()
+
+    def lap(name, t0):
+        st[name] = round(time.perf_counter() - t0, 3)
+        return time.perf_counter()
+
+    t = time.perf_counter()
     h = li.h[:ntok]
     idx, w, gap, idx_next, _ = O.route(h, li.w_cur, li.b_cur, li.w_next, li.b_next, k, cfg.dtype)
     pred = O.route(li.h_prev[:ntok], li.w_cur, li.b_cur, None, None, k, cfg.dtype)[0]
+    t = lap("gate_topk", t)
     c, cn, cp = O.histogram(idx, G, E), O.histogram(idx_next, G, E), O.histogram(pred, G, E)
+    t = lap("histogram", t)
     rep_cur = O.plan(cp, li.home, G, E, cfg.N, cfg.L)
     O.plan(cn, li.home, G, E, cfg.N, cfg.L)
+    t = lap("plan", t)
     hc, _ = O.split(c, li.home, rep_cur, G, E)
+    t = lap("split", t)
     off, perm, pos = O.permute(idx, li.home, rep_cur, hc, G, E)
+    t = lap("permute", t)
     h64 = O.widen(h, cfg.dtype)
     out, _ = O.moe_via_groups(h64, idx, w, lambda e: (O.widen(w13[e], cfg.dtype), O.widen(w2[e], cfg.dtype)),
                               off, perm, pos, E)
     if shared is not None:
         out += O.swiglu(h64, O.widen(shared[0], cfg.dtype), O.widen(shared[1], cfg.dtype))
-    dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, whole layer step (fp64), {dt:.1f} s"}
+    lap("grouped_ffn_combine", t)
+    dt = time.perf_counter() - t_all
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, whole layer step (fp64), {dt:.1f} s",
+            "cpu_model": model, "blas_threads": int(blas), "stage_s": st}
 
 
 def time_two_stage(layer, args, K, stream, T):
@@ -324,10 +356,97 @@ def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20):
     return out
 
 
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return 0.0 if n == 0 else (v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2]))
+
+
+def prepare_units(cfg, layer, dev):
+    """The layer steps a timed run cycles through, inputs resident in HBM: the
+    workload's one layer; or each of the drift workload's layers (its own
+    router and experts; layer 1's plan from the prologue's lookahead, layer
+    l+1's from layer l's lookahead, made by the step itself); or each decode
+    step (re-drawn inputs, fixed weights, plan from its own predicted
+    routing).  Each unit keeps its placement, split schedule and the routing
+    its plan was made from."""
+    import torch
+    from synth import workloads as W
+    from routed_expert_ffn_gate_amd.layer import to_device
+    up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
+    home = up(W.resident_home(cfg))
+    shared = W.shared_weights(cfg)
+    S13, S2 = (up(shared[0]), up(shared[1])) if shared is not None else (None, None)
+    units = []
+
+    def unit(name, li, W13, W2):
+        return {"name": name, "li": li, "h": up(li.h), "h_prev": up(li.h_prev), "wc": up(li.w_cur),
+                "bc": up(li.b_cur), "wn": up(li.w_next), "bn": up(li.b_next), "W13": W13, "W2": W2}
+
+    def prologue(u):
+        u["replica"] = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
+        layer.predict_plan(u["h_prev"], u["wc"], u["bc"], home, u["replica"])
+        u["sched"] = layer.sched_cur.clone()
+        u["idx_pred"] = layer.idx_next.clone()
+
+    if cfg.layers > 1:
+        hs = W.hidden_states(cfg, cfg.layers)
+        for l in range(1, cfg.layers + 1):
+            w13, w2 = W.expert_weights_stacked(cfg, l)
+            units.append(unit(f"layer{l}", W.layer_inputs(cfg, l, 0, hs=hs), up(w13), up(w2)))
+            del w13, w2
+        prologue(units[0])
+        for a, b in zip(units, units[1:]):
+            layer.step(a["h"], a["wc"], a["bc"], a["wn"], a["bn"], home, a["replica"], a["W13"], a["W2"], S13, S2,
+                       sched=a["sched"])
+            b["idx_pred"] = layer.idx_next.clone()
+            b["replica"] = layer.advance().clone()
+            b["sched"] = layer.sched_cur.clone()
+    else:
+        w13, w2 = W.expert_weights_stacked(cfg, 1)
+        W13, W2 = up(w13), up(w2)
+        del w13, w2
+        for st in range(cfg.steps):
+            u = unit(f"step{st}" if cfg.steps > 1 else "layer1", W.layer_inputs(cfg, 1, st), W13, W2)
+            prologue(u)
+            units.append(u)
+    torch.cuda.synchronize()
+    return units, home, S13, S2
+
+
+def run_unit(layer, u, home, S13, S2, **kw):
+    return layer.step(u["h"], u["wc"], u["bc"], u["wn"], u["bn"], home, u["replica"], u["W13"], u["W2"], S13, S2,
+                      sched=u["sched"], **kw)
+
+
+def rank_times(layer, u, home, S13, S2, stream, reps=5):
+    """One virtual rank's share of the grouped FFN (its local and remote
+    groups), timed alone for every rank on this step's permutation: t_r
+    (median of ``reps`` launches), the slowest, and the time-spatial balance
+    mean/max."""
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import HipEvents
+    run_unit(layer, u, home, S13, S2)
+    x = u["h"] if layer.gather_rows else layer.x_perm
+    kw = dict(gather=layer.perm, gather_k=layer.k) if layer.gather_rows else {}
+    ev = HipEvents(2 * reps)
+    t = []
+    for r in range(layer.G):
+        for i in range(reps):
+            ev.record(2 * i, stream)
+            M.moelb_grouped_ffn(x, layer.P, layer.group_off, layer.E, u["W13"], u["W2"], layer.ws_ffn, layer.y,
+                                G=layer.G, rank=r, stream=stream, **kw)
+            ev.record(2 * i + 1, stream)
+        t.append(_median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+    ev.close()
+    return t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed layer steps (default 20; 24 for workloads of 8 layers or decode steps)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
@@ -336,6 +455,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter_collection.csv files")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rank-times", action="store_true",
+                    help="skip the per-virtual-rank FFN timing (for counter runs)")
     ap.add_argument("--studies", action="store_true",
                     help="also measure the two-stage step, the split variants and FreeBalance's swaps "
                          "(reported beside the headline; their kernels then share the profile)")
@@ -350,10 +471,10 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from synth import workloads as W
-    from routed_expert_ffn_gate_amd.layer import EVENTS_PER_STEP, HipEvents, MoELayer, stage_times_ms, to_device
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import EVENTS_PER_STEP, HipEvents, MoELayer, stage_times_ms
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -361,80 +482,123 @@ def main():
     cfg = W.config(args.workload)
     dev = torch.device("cuda:0")
     t0 = time.time()
-    li = W.layer_inputs(cfg)
-    w13, w2 = W.expert_weights_stacked(cfg, 1)
-    shared = W.shared_weights(cfg)
-    log(f"inputs generated in {time.time() - t0:.1f} s")
-    up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
-    h, h_prev = up(li.h), up(li.h_prev)
-    wc, wn, bc, bn, home = up(li.w_cur), up(li.w_next), up(li.b_cur), up(li.b_next), up(li.home)
-    W13, W2 = up(w13), up(w2)
-    S13 = S2 = None
-    if shared is not None:
-        S13, S2 = up(shared[0]), up(shared[1])
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
                      shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True)
-    replica_cur = torch.empty((cfg.G, cfg.N), dtype=torch.int32, device=dev)
-    layer.predict_plan(h_prev, wc, bc, home, replica_cur)
-    idx_pred = layer.idx_next.clone()  # the lookahead routing this step's plan was made from
-    torch.cuda.synchronize()
-    log(f"uploaded; workspace {layer.ws_ffn.numel() / 2**30:.2f} GiB")
+    units, home, S13, S2 = prepare_units(cfg, layer, dev)
+    n_units = len(units)
+    u0 = units[0]
+    log(f"{n_units} layer step(s) prepared in {time.time() - t0:.1f} s; "
+        f"FFN workspace {layer.ws_ffn.numel() / 2**30:.2f} GiB")
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        layer.step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2)
+    K = args.steps if args.steps is not None else (20 if n_units == 1 else 3 * n_units)
+    for i in range(max(args.warmup, n_units)):
+        run_unit(layer, units[i % n_units], home, S13, S2)
     torch.cuda.synchronize()
 
-    K = args.steps
     EPS = EVENTS_PER_STEP
     ev = HipEvents(EPS * K + 2)
     torch.cuda.synchronize()
     ev.record(EPS * K, stream)
     for i in range(K):
-        layer.step(h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2, events=ev, ev_base=EPS * i)
+        run_unit(layer, units[i % n_units], home, S13, S2, events=ev, ev_base=EPS * i)
     ev.record(EPS * K + 1, stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(EPS * K, EPS * K + 1)
     ms = total_ms / K
-    stage = {}
-    for i in range(K):
-        for name, v in stage_times_ms(ev, EPS * i).items():
-            stage[name] = stage.get(name, 0.0) + v / K
-    sub = {n: stage.pop(n) for n in ("ffn_schedule", "ffn_gate_up_gemm", "ffn_down_gemm")}
+    per_step = [stage_times_ms(ev, EPS * i) for i in range(K)]
+    step_ms = [ev.elapsed_ms(EPS * i, EPS * i + 7) for i in range(K)]
+    ev.close()
+    names = list(per_step[0])
+    mean_st = {n: sum(p[n] for p in per_step) / K for n in names}
+    med_st = {n: _median([p[n] for p in per_step]) for n in names}
 
     # the row-materialising permutation, timed on its own (the step reads rows
     # of h straight through the permutation instead)
-    from routed_expert_ffn_gate_amd import moelb as M
+    run_unit(layer, u0, home, S13, S2)
     pe = HipEvents(2)
     pe.record(0, stream)
     reps = 5
     for _ in range(reps):
-        M.moelb_permute(h, layer.idx, cfg.G, home, replica_cur, layer.host_count, layer.ws_perm, layer.group_off,
-                        layer.perm, layer.pos, layer.x_perm)
+        M.moelb_permute(u0["h"], layer.idx, cfg.G, home, u0["replica"], layer.host_count, layer.ws_perm,
+                        layer.group_off, layer.perm, layer.pos, layer.x_perm)
     pe.record(1, stream)
     permute_rows_ms = pe.elapsed_ms(0, 1) / reps
+    # the split when the schedule does not match the placement (placement
+    # changed since the schedule was made): the kernel colours the transfers
+    pe.record(0, stream)
+    for _ in range(20):
+        M.moelb_split_scheduled(layer.counts, home, u0["replica"], None, layer.host_count, layer.load,
+                                passes=layer.passes, stream=stream)
+    pe.record(1, stream)
+    split_unscheduled_ms = pe.elapsed_ms(0, 1) / 20
+    pe.close()
 
-    balance = routing_stats(cfg, layer, idx_pred, home)
+    # per unit: routing quality, balance, stage medians, per-rank FFN times
+    f, by = algorithmic_work(cfg)
+    unit_rows = []
+    gu_bytes_time = [0.0, 0.0]
+    for j, u in enumerate(units):
+        run_unit(layer, u, home, S13, S2)
+        torch.cuda.synchronize()
+        r = routing_stats(cfg, layer, u["idx_pred"], home)
+        # the plan alone (even split of its pools) and the plan + split, against no balancing
+        M.moelb_split(layer.counts, home, u["replica"], layer.host_count, layer.load, passes=0, stream=stream)
+        ld = layer.load.double()
+        r["spatial_plan_even"] = round(float(ld.sum() / (cfg.G * ld.max().clamp(min=1))), 4)
+        r["improved"] = r["spatial_split"] > r["spatial_static"]
+        active = int((layer.counts.long().sum(0) > 0).sum().item())
+        idx_steps = [i for i in range(K) if i % n_units == j]
+        st = {n: round(_median([per_step[i][n] for i in idx_steps]), 4) for n in names}
+        gu = [per_step[i]["ffn_gate_up_gemm"] for i in idx_steps]
+        _, _, _, _, gbytes = gate_up_roofline(cfg, active, 1.0)
+        gu_bytes_time[0] += gbytes * len(gu)
+        gu_bytes_time[1] += sum(gu)
+        row = {"name": u["name"], "ms_median": round(_median([step_ms[i] for i in idx_steps]), 4),
+               "stages_ms": st, "active_experts": active, **r}
+        if not args.no_rank_times:
+            t_r = rank_times(layer, u, home, S13, S2, stream)
+            t_max = max(t_r)
+            t_split = st["split"]
+            t_plan = st["side_histogram_plan"]
+            row["rank_ffn_ms"] = [round(x, 4) for x in t_r]
+            row["rank_ffn_max_ms"] = round(t_max, 4)
+            row["time_spatial"] = round(sum(t_r) / (len(t_r) * t_max), 4)
+            # Relief "Effective Utilization Metric": spatial / (1 + T_solve / T_moe),
+            # T_moe = the slowest rank's FFN, T_solve = the per-step split
+            # (and, second form, the plan made beside the previous step as well)
+            row["u_eff"] = round(r["spatial_split"] / (1.0 + t_split / t_max), 4)
+            row["u_eff_with_plan"] = round(r["spatial_split"] / (1.0 + (t_split + t_plan) / t_max), 4)
+        unit_rows.append(row)
+    torch.cuda.synchronize()
+
     studies = {}
     if args.studies:
-        studies["two_stage"] = time_two_stage(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K,
-                                              stream, cfg.T)
-        studies["split_variants"] = time_split_variants(layer, home, replica_cur, stream)
-        studies["freebalance"] = time_freebalance(cfg, (h, h_prev, wc, bc, wn, bn, home, W13, W2, S13, S2), K,
+        tensors = (u0["h"], u0["wc"], u0["bc"], u0["wn"], u0["bn"], home, u0["replica"], u0["W13"], u0["W2"], S13,
+                   S2)
+        layer.sched_cur.copy_(u0["sched"])
+        studies["two_stage"] = time_two_stage(layer, tensors, K, stream, cfg.T)
+        run_unit(layer, u0, home, S13, S2)
+        studies["split_variants"] = time_split_variants(layer, home, u0["replica"], stream)
+        studies["freebalance"] = time_freebalance(cfg, (u0["h"], u0["h_prev"], u0["wc"], u0["bc"], u0["wn"],
+                                                        u0["bn"], home, u0["W13"], u0["W2"], S13, S2), K,
                                                   args.warmup, stream, gather_rows=args.rows == "gather")
         studies["stale_split"] = time_stale_split(cfg, dev, stream)
-        studies["graph"] = time_graph(layer, (h, wc, bc, wn, bn, home, replica_cur, W13, W2, S13, S2), K,
-                                      args.warmup, stream)
-    f, by = algorithmic_work(cfg)
+        studies["graph"] = time_graph(layer, tensors, K, args.warmup, stream)
+
     total_flop = f["gate_flop"] + f["ffn_gate_up_flop"] + f["ffn_down_flop"] + f["shared_flop"]
     tokens_per_s = cfg.T / (ms * 1e-3)
-    gu_ms = sub["ffn_gate_up_gemm"]
-    active = int((layer.counts.long().sum(0) > 0).sum().item())
-    gu_hbm_bound, achieved, peak, unit, gu_bytes = gate_up_roofline(cfg, active, gu_ms)
+    gu_ms = mean_st["ffn_gate_up_gemm"]
+    gu_hbm_bound, _, peak, unit, _ = gate_up_roofline(cfg, unit_rows[0]["active_experts"], gu_ms)
+    gu_bytes = gu_bytes_time[0] / K
+    if gu_hbm_bound:
+        achieved = gu_bytes_time[0] / (gu_bytes_time[1] * 1e-3) / 1e9
+    else:
+        achieved = f["ffn_gate_up_flop"] / (gu_ms * 1e-3) / 1e12
     hbm = {
-        "gate_topk": by["gate_topk"] / (stage["gate_topk"] * 1e-3) / 1e9,
+        "gate_topk": by["gate_topk"] / (med_st["gate_topk"] * 1e-3) / 1e9,
         "permute_rows": by["permute_rows"] / (permute_rows_ms * 1e-3) / 1e9,
-        "combine": by["combine"] / (stage["combine"] * 1e-3) / 1e9,
+        "combine": by["combine"] / (med_st["combine"] * 1e-3) / 1e9,
     }
     traffic = None
     if os.path.exists(TRAFFIC_JSON):
@@ -459,7 +623,8 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "inter": cfg.inter, "shared_inter": cfg.shared_inter, "virtual_ranks": cfg.G,
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
-                   "ffn_rows": args.rows},
+                   "layer_steps_cycled": n_units, "ffn_rows": args.rows},
+        "ms_per_step_median": round(_median(step_ms), 4),
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
         "roofline": {"bound": "hbm" if gu_hbm_bound else "mfma",
                      "kernel": (GATE_UP_KERNEL if cfg.dtype == "bf16" else "ffn_simt_kernel<0>") +
@@ -468,14 +633,26 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "flop_per_launch": f["ffn_gate_up_flop"], "bytes_per_launch": gu_bytes,
                      "avg_launch_ms": round(gu_ms, 4)},
-        "stages_ms": {k_: round(v, 4) for k_, v in {**stage, **sub, "permute_rows": permute_rows_ms}.items()},
+        "stages_ms": {k_: round(v, 4) for k_, v in {**med_st, "permute_rows": permute_rows_ms,
+                                                       "split_unscheduled": split_unscheduled_ms}.items()},
+        "stages_ms_mean": {k_: round(v, 4) for k_, v in mean_st.items()},
         "hbm_frac": {k_: round(v / PEAK_HBM_GBS, 4) for k_, v in hbm.items()},
-        "routing": balance,
-        **studies,
         "ffn_mfma_frac": round((f["ffn_gate_up_flop"] + f["ffn_down_flop"]) /
-                               ((sub["ffn_gate_up_gemm"] + sub["ffn_down_gemm"]) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-                               4),
+                               ((med_st["ffn_gate_up_gemm"] + med_st["ffn_down_gemm"]) * 1e-3) /
+                               (PEAK_BF16_TFLOPS * 1e12), 4),
+        "routing": {k_: v for k_, v in unit_rows[0].items()
+                    if k_ in ("lookahead_hit", "spatial_static", "spatial_plan_even", "spatial_split")},
+        "balance": {k_: v for k_, v in unit_rows[0].items()
+                    if k_ in ("rank_ffn_ms", "rank_ffn_max_ms", "time_spatial", "u_eff", "u_eff_with_plan")},
+        **studies,
     }
+    if n_units > 1:
+        result["units"] = unit_rows
+        result["units_mean"] = {
+            key: round(sum(float(r_[key]) for r_ in unit_rows) / n_units, 4)
+            for key in ("ms_median", "lookahead_hit", "spatial_static", "spatial_plan_even", "spatial_split",
+                        "u_eff", "time_spatial") if key in unit_rows[0]}
+        result["units_mean"]["improved_share"] = round(sum(r_["improved"] for r_ in unit_rows) / n_units, 4)
     if args.copy_bytes > 0:
         # plain copy of known size: the counters' calibration in a PMC run
         n = args.copy_bytes // 4
@@ -488,7 +665,8 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(cfg, li, w13, w2, shared, args.cpu_tokens)
+        w13, w2 = W.expert_weights_stacked(cfg, u0["li"].layer)
+        result["cpu_baseline"] = cpu_baseline(cfg, u0["li"], w13, w2, W.shared_weights(cfg), args.cpu_tokens)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

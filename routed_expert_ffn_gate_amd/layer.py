@@ -242,11 +242,13 @@ class MoELayer:
                        self.home_next if self.balancer == "freebalance" else None)
 
     def step(self, h, w_cur, b_cur, w_next, b_next, home, replica_cur, w13, w2, shared_w13=None, shared_w2=None,
-             stream=None, events: Optional[HipEvents] = None, ev_base: int = 0) -> StepOut:
+             stream=None, events: Optional[HipEvents] = None, ev_base: int = 0, sched=None) -> StepOut:
         """One layer step.  With ``events``, marks ev_base+0..7 bracket the
         stages of STAGES on the step's stream, ev_base+8..11 bracket the
         grouped FFN's three stages (schedule, gate/up GEMM, down GEMM, each
-        launched on its own), ev_base+12..13 bracket the side stream's work."""
+        launched on its own), ev_base+12..13 bracket the side stream's work.
+        ``sched``: the split's round schedule for ``replica_cur`` (default: the
+        one ``predict_plan`` or ``advance`` left in force)."""
         ev = events
         s0 = stream if stream is not None else torch.cuda.current_stream()
 
@@ -267,8 +269,8 @@ class MoELayer:
         mark(1)
         M.moelb_histogram(self.idx, self.G, self.counts, stream=s0)
         mark(2)
-        M.moelb_split_scheduled(self.counts, home, replica_cur, self.sched_cur, self.host_count, self.load,
-                                passes=self.passes, stream=s0)
+        M.moelb_split_scheduled(self.counts, home, replica_cur, self.sched_cur if sched is None else sched,
+                                self.host_count, self.load, passes=self.passes, stream=s0)
         mark(3)
         copy_rows = not self.gather_rows  # the gather GEMM reads h through perm instead
         M.moelb_permute(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
