@@ -9,10 +9,11 @@ the timed region.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-Traffic counters: run under ``rocprofv3 --pmc FETCH_SIZE`` and then
-``--pmc WRITE_SIZE`` with ``--copy-bytes`` (a plain device copy of that many
-bytes follows the timed region and calibrates the counters), then
-``python bench.py --summarize-pmc FETCH_CSV WRITE_CSV`` writes
+Counters: one kernel-trace run and three counter runs (FETCH_SIZE;
+WRITE_SIZE; MFMA operations and busy cycles) of the same command with
+``--copy-bytes`` (a plain device copy of that many bytes follows the timed
+region and calibrates the traffic counters), then ``python bench.py
+--summarize-profile DIR KT_JSON`` writes profiles/kernels_<workload>.md and
 profiles/ffn_gate_up_gemm_traffic.json, which later runs report as
 ``roofline.traffic`` while the kernel source is unchanged.
 """
@@ -452,8 +453,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, one plain device-to-device copy of this many bytes")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic summary from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("PROF_DIR", "BENCH_JSON"),
+                    help="write profiles/kernels_<workload>.md from a kernel-trace run and three counter runs "
+                         "(PROF_DIR/kt, pmc_f, pmc_w, pmc_m) and the bench line of the kernel-trace run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-times", action="store_true",
                     help="skip the per-virtual-rank FFN timing (for counter runs)")
@@ -463,8 +465,8 @@ def main():
     ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
                     help="gate/up GEMM reads h rows through the permutation, or a copied x_perm")
     args = ap.parse_args()
-    if args.summarize_pmc:
-        summarize_pmc(args.workload, *args.summarize_pmc)
+    if args.summarize_profile:
+        summarize_profile(args.workload, *args.summarize_profile)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
@@ -548,6 +550,7 @@ def main():
         r["spatial_plan_even"] = round(float(ld.sum() / (cfg.G * ld.max().clamp(min=1))), 4)
         r["improved"] = r["spatial_split"] > r["spatial_static"]
         active = int((layer.counts.long().sum(0) > 0).sum().item())
+        r["active_experts"] = active
         idx_steps = [i for i in range(K) if i % n_units == j]
         st = {n: round(_median([per_step[i][n] for i in idx_steps]), 4) for n in names}
         gu = [per_step[i]["ffn_gate_up_gemm"] for i in idx_steps]
@@ -555,7 +558,7 @@ def main():
         gu_bytes_time[0] += gbytes * len(gu)
         gu_bytes_time[1] += sum(gu)
         row = {"name": u["name"], "ms_median": round(_median([step_ms[i] for i in idx_steps]), 4),
-               "stages_ms": st, "active_experts": active, **r}
+               "stages_ms": st, **r}
         if not args.no_rank_times:
             t_r = rank_times(layer, u, home, S13, S2, stream)
             t_max = max(t_r)
@@ -641,7 +644,8 @@ def main():
                                ((med_st["ffn_gate_up_gemm"] + med_st["ffn_down_gemm"]) * 1e-3) /
                                (PEAK_BF16_TFLOPS * 1e12), 4),
         "routing": {k_: v for k_, v in unit_rows[0].items()
-                    if k_ in ("lookahead_hit", "spatial_static", "spatial_plan_even", "spatial_split")},
+                    if k_ in ("lookahead_hit", "spatial_static", "spatial_plan_even", "spatial_split",
+                              "active_experts")},
         "balance": {k_: v for k_, v in unit_rows[0].items()
                     if k_ in ("rank_ffn_ms", "rank_ffn_max_ms", "time_spatial", "u_eff", "u_eff_with_plan")},
         **studies,
@@ -672,42 +676,167 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _read_pmc(path, counter):
+def _short_kernel(name):
+    """Kernel name without 'void', the anonymous namespace and the argument list."""
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def _dispatches(path, counter=None):
+    """Per-dispatch rows of a rocprofv3 CSV (kernel trace or counter
+    collection): (kernel, duration s, counter value or None)."""
     import csv
-    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-    return rows
+    out = []
+    for r in csv.DictReader(open(path)):
+        if counter is not None and r.get("Counter_Name") != counter:
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        out.append((_short_kernel(r["Kernel_Name"]), dur, float(r["Counter_Value"]) if counter else None))
+    return out
 
 
-def summarize_pmc(workload, fetch_csv, write_csv):
-    """Per-dispatch HBM-side bytes of the gate/up GEMM from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the same
-    counter on the largest plain copy dispatch to the bytes it must move."""
-    out = {"workload": workload, "kernel": GATE_UP_KERNEL, "kernel_source_sha": _kernel_sha()}
-    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        rows = _read_pmc(path, counter)
-        gu = [float(r["Counter_Value"]) for r in rows if GATE_UP_KERNEL in r["Kernel_Name"]]
-        cp = [r for r in rows if "copy" in r["Kernel_Name"].lower()]
-        if not gu or not cp:
-            raise SystemExit(f"{path}: no gate/up or copy dispatch with {counter}")
-        big = max(cp, key=lambda r: float(r["Counter_Value"]))
-        out[f"{key}_kib_per_dispatch"] = sum(gu) / len(gu)
-        out[f"{key}_dispatches"] = len(gu)
-        out[f"{key}_copy_kib"] = float(big["Counter_Value"])
-        out[f"{key}_copy_kernel"] = big["Kernel_Name"]
-    out["note"] = ("copy of copy_bytes moves copy_bytes read + copy_bytes written; factor = copy_bytes / "
-                   "(counter KiB x 1024) per counter")
-    cb = int(os.environ.get("COPY_BYTES", "0"))
-    if cb <= 0:
-        raise SystemExit("set COPY_BYTES to the --copy-bytes of the PMC runs")
-    out["copy_bytes"] = cb
-    f_fetch = cb / (out["fetch_copy_kib"] * 1024.0)
-    f_write = cb / (out["write_copy_kib"] * 1024.0)
-    out["fetch_factor"], out["write_factor"] = f_fetch, f_write
-    out["bytes_per_launch"] = (out["fetch_kib_per_dispatch"] * 1024.0 * f_fetch +
-                               out["write_kib_per_dispatch"] * 1024.0 * f_write)
-    with open(TRAFFIC_JSON, "w") as fh:
-        json.dump(out, fh, indent=1)
-    print(json.dumps(out, indent=1))
+# the row-copying permutation is the same kernel as the index-only one; a
+# launch that copies rows runs far longer
+ROWS_SPLIT_S = 100e-6
+
+
+def _kernel_key(name, dur):
+    if name.startswith("rank_scatter_kernel"):
+        return name + (" (rows)" if dur > ROWS_SPLIT_S else " (indices)")
+    return name
+
+
+def kernel_work(cfg, active):
+    """Algorithmic work per launch of the step's kernels: (bound, amount, unit)
+    with bytes for HBM-bound kernels and FLOP for MFMA-bound ones."""
+    T, d, E, k, I, G = cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G
+    b = cfg.elem_bytes
+    P = T * k
+    f, by = algorithmic_work(cfg)
+    return {
+        "gate_topk_dma_kernel": ("hbm", by["gate_topk"], "B"),
+        "histogram_kernel": ("hbm", 4.0 * P + 4.0 * G * E, "B"),
+        "count_kernel": ("hbm", 4.0 * P, "B"),
+        "rank_scatter_kernel (indices)": ("hbm", 12.0 * P, "B"),
+        "rank_scatter_kernel (rows)": ("hbm", by["permute_rows"], "B"),
+        "ffn_persistent_kernel<0>": ("mfma", f["ffn_gate_up_flop"], "FLOP"),
+        "ffn_persistent_kernel<1>": ("mfma", f["ffn_down_flop"], "FLOP"),
+        "combine_kernel": ("hbm", by["combine"], "B"),
+        "_ffn_bytes": (active * 2.0 * I * d * b + T * d * b + P * I * b, P * I * b + active * d * I * b + P * d * b),
+    }
+
+
+def summarize_profile(workload, prof_dir, bench_json):
+    """Per-kernel table from one kernel-trace run and three counter runs of
+    the same command (FETCH_SIZE, WRITE_SIZE, and the MFMA/clock counters),
+    each in ``prof_dir`` (kt/, pmc_f/, pmc_w/, pmc_m/).  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are scaled by the factor that maps the same
+    counter on the largest plain copy dispatch (copy_bytes each way) to its
+    known bytes.  Writes profiles/kernels_<workload>.md and, for the gate/up
+    GEMM, the traffic record bench.py reports as roofline.traffic."""
+    import collections
+    from synth import workloads as W
+    cfg = W.config(workload)
+    res = json.load(open(bench_json))
+    active = res["routing"]["active_experts"]
+    cb = int(res["copy_bytes"])
+    kt = _dispatches(os.path.join(prof_dir, "kt", "kt_kernel_trace.csv"))
+    pf = os.path.join(prof_dir, "pmc_f", "p_counter_collection.csv")
+    pw = os.path.join(prof_dir, "pmc_w", "p_counter_collection.csv")
+    pm = os.path.join(prof_dir, "pmc_m", "p_counter_collection.csv")
+    fetch, write = _dispatches(pf, "FETCH_SIZE"), _dispatches(pw, "WRITE_SIZE")
+    mops, grbm = _dispatches(pm, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), _dispatches(pm, "GRBM_GUI_ACTIVE")
+    copy_f = max(v for n, _, v in fetch if "copyBuffer" in n)
+    copy_w = max(v for n, _, v in write if "copyBuffer" in n)
+    ff, fw = cb / (copy_f * 1024.0), cb / (copy_w * 1024.0)
+
+    def per_kernel(rows):
+        agg = collections.defaultdict(list)
+        for n, dur, v in rows:
+            agg[_kernel_key(n, dur)].append((dur, v))
+        return agg
+
+    KT, F, Wr, MO, GR = (per_kernel(x) for x in (kt, fetch, write, mops, grbm))
+    work = kernel_work(cfg, active)
+    ffn_bytes = work.pop("_ffn_bytes")
+    lines = [f"# Kernels of one layer step, {workload}, one MI355X", "",
+             "Durations: rocprofv3 kernel trace (average per launch). Traffic: FETCH_SIZE and WRITE_SIZE per "
+             f"launch, each scaled by the factor that maps the counter on a plain {cb >> 20} MiB device copy to "
+             f"the bytes it moves (FETCH x{ff:.4f}, WRITE x{fw:.4f}). MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 "
+             "FLOP (executed, padding included) per launch, over the launch's duration in the counter run. "
+             "Clock: GRBM_GUI_ACTIVE per launch / duration / 8 XCDs, for launches of 200 µs or more (counter "
+             "run; the profiler slows long kernels by a few %).", "",
+             "| kernel | launches | avg µs | bound | algorithmic work / launch | achieved | of peak | "
+             "fetched GB | written GB | traffic / algorithmic bytes | executed MFMA TFLOP/s | clock GHz |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    gu_row = None
+    for name in sorted(KT, key=lambda n: -sum(d for d, _ in KT[n])):
+        if name.startswith(("at::native", "__amd")):
+            continue
+        durs = [d for d, _ in KT[name]]
+        avg = sum(durs) / len(durs)
+        fb = sum(v for _, v in F.get(name, [])) / max(1, len(F.get(name, []))) * 1024 * ff
+        wb = sum(v for _, v in Wr.get(name, [])) / max(1, len(Wr.get(name, []))) * 1024 * fw
+        mo = MO.get(name, [])
+        mf = sum(v * 512 / d for d, v in mo) / max(1, len(mo)) / 1e12
+        gr = GR.get(name, [])
+        gr = [(d, v) for d, v in gr if d >= 200e-6]  # short launches: the counter is not a clock
+        clk = sum(v / d for d, v in gr) / len(gr) / 8e9 if gr else None
+        base, _, tail = name.partition(" (")
+        key = next((w for w in work if base.startswith(w.partition(" (")[0]) and
+                    (not tail or w.endswith("(" + tail))), None)
+        bound, amt, unit = work[key] if key else ("latency", None, "")
+        if bound == "hbm":
+            ach, peak, txt = amt / avg / 1e9, PEAK_HBM_GBS, f"{amt / 1e6:.1f} MB"
+            alg_bytes = amt
+            ach_s = f"{ach:.0f} GB/s"
+        elif bound == "mfma":
+            ach, peak, txt = amt / avg / 1e12, PEAK_BF16_TFLOPS, f"{amt / 1e12:.3f} TFLOP"
+            alg_bytes = ffn_bytes[0] if name.endswith("<0>") else ffn_bytes[1]
+            ach_s = f"{ach:.0f} TFLOP/s"
+        else:
+            ach = peak = alg_bytes = None
+            txt, ach_s = "-", "-"
+        frac = f"{ach / peak:.3f}" if ach is not None else "-"
+        ratio = f"{(fb + wb) / alg_bytes:.2f}" if alg_bytes else "-"
+        lines.append(f"| `{name}` | {len(durs)} | {avg * 1e6:.1f} | {bound} | {txt} | {ach_s} | {frac} | "
+                     f"{fb / 1e9:.3f} | {wb / 1e9:.3f} | {ratio} | {mf:.0f} | "
+                     f"{'-' if clk is None else f'{clk:.2f}'} |")
+        if name == GATE_UP_KERNEL:
+            gu_row = (fb, wb)
+    lines += ["", "Commands (repository root; each counter set in a run of its own):", "", "```",
+              "export TMPDIR=/tmp",
+              "B='python -u bench.py --workload %s --steps 2 --warmup 0 --no-cpu-baseline --no-rank-times "
+              "--copy-bytes %d'" % (workload, cb),
+              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/kt -o kt -- $B > "
+              "gpurun_out/prof/kt.json",
+              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/pmc_f -o p -- $B",
+              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/pmc_w -o p -- $B",
+              "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+              "GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/prof/pmc_m -o p -- $B",
+              f"python bench.py --workload {workload} --summarize-profile gpurun_out/prof gpurun_out/prof/kt.json",
+              "```", ""]
+    out = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+    if gu_row is not None:
+        tr = {"workload": workload, "kernel": GATE_UP_KERNEL, "kernel_source_sha": _kernel_sha(),
+              "fetch_bytes_per_launch": gu_row[0], "write_bytes_per_launch": gu_row[1],
+              "fetch_factor": ff, "write_factor": fw, "copy_bytes": cb,
+              "bytes_per_launch": gu_row[0] + gu_row[1],
+              "note": "FETCH_SIZE and WRITE_SIZE per launch, scaled by copy_bytes / (counter KiB x 1024) "
+                      "of a plain device copy of copy_bytes"}
+        with open(TRAFFIC_JSON, "w") as fh:
+            json.dump(tr, fh, indent=1)
 
 
 def _kernel_sha():

@@ -8,7 +8,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/moelb.h"
+#include "moelb.h"
 
 #define MOELB_WAVE 64
 

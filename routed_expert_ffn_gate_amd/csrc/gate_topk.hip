@@ -85,14 +85,17 @@ __device__ __forceinline__ void select_keys(const float* row, bool active, int E
 // Selection is exact: the k+2 largest fast keys are found first.  If entries
 // k and k+1 fall in different buckets, no logit outside the first k+1
 // entries shares entry k's bucket, so those entries are exactly the k+1
-// largest logits; entries inside one bucket are then re-ordered by their
-// exact logits where two adjacent ones share a bucket.  If entries k and k+1
-// share a bucket (rare), the token is selected again with exact keys (the
-// whole wave runs that pass, and only such tokens keep its result).
+// largest logits, in exact order unless two adjacent ones share a bucket.
+// A token where either fails (rare: a few in ten thousand here) is selected
+// again by the whole wave, by exact keys: each lane holds a few of the
+// token's logits and k+1 wave-wide maxima give the order.  One workgroup per
+// CU means the slowest wave sets the kernel's time, so this path is kept
+// short rather than merely rare.
 template <int KL>
-__device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int tok0, int T, int E, int k,
-                              bool has_next, int32_t* __restrict__ idx, float* __restrict__ wts,
-                              float* __restrict__ gap, int32_t* __restrict__ idx_next) {
+__device__ __forceinline__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int tok0, int T, int E,
+                                              int k, bool has_next, int32_t* __restrict__ idx,
+                                              float* __restrict__ wts, float* __restrict__ gap,
+                                              int32_t* __restrict__ idx_next) {
   const int tid = threadIdx.x;
   const int per_dir = has_next ? GATE_THREADS / 2 : GATE_THREADS;
   const int dir = tid / per_dir;
@@ -106,42 +109,50 @@ __device__ void topk_epilogue(const float* z, int stride, int ntok, int lpt, int
   int li[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(l[i] & 0xffu), E - 1);  // unused entries stay in the row
-  // buckets of entries k and k+1 (k is a runtime value: no dynamic register indexing)
+  // buckets of entries k and k+1, and adjacent equal buckets among 0..k (k is
+  // a runtime value: no dynamic register indexing)
   uint32_t bk = 0u, bk1 = 1u;
-  bool tie_run = false;  // two adjacent entries among 0..k share a bucket
+  bool tie_run = false;
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
     if (j == k) bk = l[j] >> 8;
     if (j == k + 1) bk1 = l[j] >> 8;
     if (j + 1 < KL && j + 1 <= k && (l[j] >> 8) == (l[j + 1] >> 8)) tie_run = true;
   }
-  const bool straddle = active && k + 2 <= E && bk == bk1;
-  if (__ballot(straddle) != 0ull) {
-    uint64_t lx[KL];
-    select_keys<KL>(row, active, E, sub, lpt, lx);
-    if (straddle) {
+  const bool redo = active && ((k + 2 <= E && bk == bk1) || tie_run);
+  uint64_t todo = __ballot(redo);
+  while (todo != 0ull) {
+    // one such token per round, all 64 lanes on it (E <= 256: four logits per lane)
+    const int src = __ffsll(static_cast<long long>(todo)) - 1;
+    const int first = src & ~(lpt - 1);
+    todo &= ~(((lpt == 64 ? 0ull : (1ull << lpt)) - 1ull) << first);
+    const int off = __shfl(static_cast<int>(row - z), src, MOELB_WAVE);
+    const int lane = threadIdx.x & (MOELB_WAVE - 1);
+    uint64_t mine[4];
 #pragma unroll
-      for (int i = 0; i < KL; ++i) li[i] = min(255 - (int)(lx[i] & 0xffu), E - 1);
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      mine[q] = e < E ? topk_key_exact(z[off + e], e) : 0ull;
     }
-  }
-  if (active && tie_run && !straddle) {
-    // order entries 0..k by exact logit (descending), equal logits by id
-    // (odd-even transposition: KL rounds sort up to KL entries)
-    float v[KL];
+    int ids[KL];
 #pragma unroll
-    for (int j = 0; j < KL; ++j) v[j] = row[li[j]];
+    for (int r = 0; r < KL; ++r) {
+      uint64_t b = mine[0];
 #pragma unroll
-    for (int r = 0; r < KL; ++r)
+      for (int q = 1; q < 4; ++q) b = mine[q] > b ? mine[q] : b;
 #pragma unroll
-      for (int j = r & 1; j + 1 < KL; j += 2)
-        if (j + 1 <= k && (v[j + 1] > v[j] || (v[j + 1] == v[j] && li[j + 1] < li[j]))) {
-          const float tv = v[j];
-          v[j] = v[j + 1];
-          v[j + 1] = tv;
-          const int ti = li[j];
-          li[j] = li[j + 1];
-          li[j + 1] = ti;
-        }
+      for (int m = 1; m < MOELB_WAVE; m <<= 1) {
+        const uint64_t o = __shfl_xor(b, m, MOELB_WAVE);
+        b = o > b ? o : b;
+      }
+      ids[r] = min(255 - (int)(b & 0xffu), E - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine[q] = mine[q] == b ? 0ull : mine[q];
+    }
+    if (lane >= first && lane < first + lpt) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i) li[i] = ids[i];
+    }
   }
   if (dir == 0) {
     // softmax denominator over all E logits of this token (no weights wanted:
