@@ -498,18 +498,29 @@ def main():
         run_unit(layer, units[i % n_units], home, S13, S2)
     torch.cuda.synchronize()
 
-    EPS = EVENTS_PER_STEP
-    ev = HipEvents(EPS * K + 2)
+    # the timed region: K layer steps, one event between consecutive steps
+    tev = HipEvents(K + 1)
     torch.cuda.synchronize()
-    ev.record(EPS * K, stream)
+    for i in range(K):
+        tev.record(i, stream)
+        run_unit(layer, units[i % n_units], home, S13, S2)
+    tev.record(K, stream)
+    torch.cuda.synchronize()
+    total_ms = tev.elapsed_ms(0, K)
+    ms = total_ms / K
+    step_ms = [tev.elapsed_ms(i, i + 1) for i in range(K)]
+    tev.close()
+    # the stage breakdown: the same K steps again, with a mark around every
+    # stage (the marks cost a few microseconds each, so they stay out of the
+    # timed region)
+    EPS = EVENTS_PER_STEP
+    ev = HipEvents(EPS * K)
+    torch.cuda.synchronize()
     for i in range(K):
         run_unit(layer, units[i % n_units], home, S13, S2, events=ev, ev_base=EPS * i)
-    ev.record(EPS * K + 1, stream)
     torch.cuda.synchronize()
-    total_ms = ev.elapsed_ms(EPS * K, EPS * K + 1)
-    ms = total_ms / K
     per_step = [stage_times_ms(ev, EPS * i) for i in range(K)]
-    step_ms = [ev.elapsed_ms(EPS * i, EPS * i + 7) for i in range(K)]
+    marked_ms = [ev.elapsed_ms(EPS * i, EPS * i + 7) for i in range(K)]
     ev.close()
     names = list(per_step[0])
     mean_st = {n: sum(p[n] for p in per_step) / K for n in names}
@@ -558,6 +569,7 @@ def main():
         gu_bytes_time[0] += gbytes * len(gu)
         gu_bytes_time[1] += sum(gu)
         row = {"name": u["name"], "ms_median": round(_median([step_ms[i] for i in idx_steps]), 4),
+               "ms_median_marked": round(_median([marked_ms[i] for i in idx_steps]), 4),
                "stages_ms": st, **r}
         if not args.no_rank_times:
             t_r = rank_times(layer, u, home, S13, S2, stream)
@@ -628,6 +640,7 @@ def main():
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
                    "layer_steps_cycled": n_units, "ffn_rows": args.rows},
         "ms_per_step_median": round(_median(step_ms), 4),
+        "ms_per_step_marked_median": round(_median(marked_ms), 4),
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
         "roofline": {"bound": "hbm" if gu_hbm_bound else "mfma",
                      "kernel": (GATE_UP_KERNEL if cfg.dtype == "bf16" else "ffn_simt_kernel<0>") +

@@ -1077,6 +1077,172 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
 #undef DL_NBO
 }
 
+// ---------------------------------------------------------------- bf16 MFMA GEMM, 64-row tiles
+
+// For few rows per expert (decode batches: tens of rows per expert), where
+// the GEMMs stream expert weights and a 256-row tile would be mostly
+// repeated rows: M tiles of 64 rows, the same 256 B rows per tile (gate/up:
+// 128 gate rows and the matching 128 up rows; down: 256 output columns).
+// One workgroup per tile, 4 waves; wave w takes all 64 A rows and B rows
+// [32w, 32w+32) and [128+32w, ...) (gate/up: the gate and up rows of the same
+// 32 columns, so the SwiGLU stays in the wave) or [64w, 64w+64) (down), as
+// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  A (8 KiB) and B (32 KiB) of each
+// 64-wide K step stream global -> LDS with global_load_lds_dwordx4 into a
+// ring of three stages, two steps ahead of the one computed; one barrier per
+// step.  Each lane stores its four adjacent output columns straight from the
+// accumulators (8 bytes).  (A persistent form with a four-stage ring that
+// streams across tile boundaries measured slower on the decode shape.)
+constexpr int SK_BM = 64;
+constexpr int SK_BN = 256;
+constexpr int SK_STAGE = (SK_BM + SK_BN) * DL_BK;  // elements per stage
+constexpr int SK_STAGES = 3;
+constexpr size_t SK_LDS_BYTES = (size_t)SK_STAGES * SK_STAGE * sizeof(uint16_t);
+constexpr int SK_VPS = 10;  // DMA instructions per wave and stage: 2 of A, 8 of B
+
+template <int MODE>
+__global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* __restrict__ x, int rows_x,
+                                                                const uint16_t* __restrict__ w, FfnSched s,
+                                                                int rows_y, int d, int inter, int ntn,
+                                                                uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) char smem[];
+  const int n_mtiles = *s.n_mtiles;
+  const int tile = xcd_tile(n_mtiles * ntn);
+  if (tile < 0) return;
+  int mt, nt;
+  grouped_tile(tile, n_mtiles, ntn, mt, nt);
+  const int e = s.mt_e[mt];
+  const int v0 = s.mt_v0[mt];
+  const int vend = s.eoff[e + 1];
+  const int K = MODE == 0 ? d : inter;
+  const int KT = K / DL_BK;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+
+  // DMA rows of this lane: A block (wave*2 + j) of 8 rows, B block (wave*8 + j)
+  // of 8 rows; row (lane >> 3) in the block, slot (lane & 7) <- global chunk
+  // dl_slot(row, slot); byte offsets from the operand bases
+  const uint16_t* abase = MODE == 0 ? x : static_cast<const uint16_t*>(s.amid);
+  const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
+  uint32_t aoff[2], boff[8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 8 + (lane >> 3);
+    int v = v0 + r;
+    v = v < vend ? v : v0;  // rows past the expert's end repeat its first row
+    const uint32_t src = MODE == 0 ? (uint32_t)min(max(s.asrc[v], 0), rows_x - 1) : (uint32_t)v;
+    aoff[j] = (src * (uint32_t)K + dl_slot(r, lane & 7) * 8) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wave * 8 + j) * 8 + (lane >> 3);
+    uint32_t brow;
+    if (MODE == 0) {
+      int c = nt * 128 + (r & 127);
+      c = c < inter ? c : 0;
+      brow = (uint32_t)((r < 128) ? c : inter + c);
+    } else {
+      const int c = nt * 256 + r;
+      brow = (uint32_t)(c < d ? c : 0);
+    }
+    boff[j] = (brow * (uint32_t)K + dl_slot(r, lane & 7) * 8) * 2u;
+  }
+  // issue K step KTI into its ring stage (SK_VPS instructions per wave)
+  auto issue = [&](int kti) {
+    const uint32_t st = lds_u32 + (uint32_t)((kti % SK_STAGES) * SK_STAGE) * 2u;
+    const size_t ko = (size_t)kti * DL_BK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dl_copy16(aoff[j], abase + ko, st + (uint32_t)((wave_s * 2 + j) * 8 * DL_BK) * 2u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dl_copy16(boff[j], bbase + ko, st + (uint32_t)((SK_BM + (wave_s * 8 + j) * 8) * DL_BK) * 2u);
+  };
+
+  // fragment rows: A blocks mi = 0, 1 (rows 32 mi + lane % 32); B blocks ni:
+  // gate/up rows 32 wave + ni * 128, down rows 64 wave + 32 ni
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  int arow[2], brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    arow[i] = i * 32 + fr;
+    brow[i] = SK_BM + (MODE == 0 ? wave * 32 + i * 128 : wave * 64 + i * 32) + fr;
+  }
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  // the epilogue's output rows, fetched now so their latency hides behind the K loop
+  int orow[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int v = v0 + mi * 32 + fr;
+    orow[mi] = v < vend ? (MODE == 0 ? v : min(max(s.rowmap[v], 0), rows_y - 1)) : -1;
+  }
+  asm volatile("" ::"v"(orow[0]), "v"(orow[1]), "s"(y));
+  issue(0);
+  if (KT > 1) issue(1);
+  for (int kt = 0; kt < KT; ++kt) {
+    // step kt landed (only step kt+1 may still be in flight), and every wave
+    // has finished step kt-1, whose stage the refill below takes
+    if (kt + 1 < KT)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SK_VPS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < KT) issue(kt + 2);
+    const uint16_t* st = lds + (kt % SK_STAGES) * SK_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(st + arow[i] * DL_BK + dl_slot(arow[i], ks * 2 + fh) * 8);
+        fb[i] = *reinterpret_cast<const bf16x8_t*>(st + brow[i] * DL_BK + dl_slot(brow[i], ks * 2 + fh) * 8);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+    }
+  }
+  // acc[mi][ni] holds its block transposed: lane -> row (lane % 32) of block
+  // mi, element j -> column (j / 4) * 8 + (lane / 32) * 4 + j % 4 of block ni
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (orow[mi] < 0) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (MODE == 0) {
+        const int col = nt * 128 + wave * 32 + q * 8 + fh * 4;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = silu_f32(acc[mi][0][q * 4 + i]) * acc[mi][1][q * 4 + i];
+        if (col < inter)
+          *reinterpret_cast<uint2*>(y + (size_t)orow[mi] * inter + col) =
+              make_uint2(bf16x2_pack(o[0], o[1]), bf16x2_pack(o[2], o[3]));
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = nt * 256 + wave * 64 + ni * 32 + q * 8 + fh * 4;
+          const f32x16_t& a4 = acc[mi][ni];
+          if (col < d)
+            *reinterpret_cast<uint2*>(y + (size_t)orow[mi] * d + col) =
+                make_uint2(bf16x2_pack(a4[q * 4], a4[q * 4 + 1]), bf16x2_pack(a4[q * 4 + 2], a4[q * 4 + 3]));
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
 template <int MODE>
@@ -1172,6 +1338,13 @@ __global__ __launch_bounds__(256) void ffn_simt_kernel(const float* __restrict__
 
 }  // namespace
 
+// Few rows per expert: the 64-row tile kernels (a host-side rule on the
+// shapes, so every stage of one FFN call takes the same tile height).
+static bool skinny_rows(int rows, int num_groups, int E) {
+  (void)num_groups;
+  return (size_t)rows < (size_t)128 * E;
+}
+
 // One workgroup per compute unit (a multiple of the 8 XCDs).
 static int persistent_grid() {
   const int cus = moelb_compute_units();
@@ -1208,7 +1381,8 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
   sched_layout(rows, num_groups, E, inter, dtype, &sc, static_cast<char*>(ws));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == MOELB_BF16;
-  const int BM = bf ? MF_BM : SF_BM;
+  const bool skinny_tiles = bf && skinny_rows(rows, num_groups, E) && d % DL_BK == 0 && inter % DL_BK == 0;
+  const int BM = bf ? (skinny_tiles ? SK_BM : MF_BM) : SF_BM;
   const bool run_up = stages & MOELB_FFN_GATE_UP, run_down = stages & MOELB_FFN_DOWN;
   if (stages & MOELB_FFN_SCHEDULE) {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows,
@@ -1229,13 +1403,24 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
     const bool dma0 = d % DL_BK == 0, dma1 = inter % DL_BK == 0;  // else the register-staged kernel
     const bool pers0 = dma0 && d / DL_BK >= 3;                      // persistent kernels
     const bool pers1 = dma1 && inter / DL_BK >= 3;
+    // 64-row tiles where experts average fewer than 128 rows (each 256-row
+    // tile would be mostly repeated rows) and both K are whole 64-wide steps
+    const bool skinny = skinny_rows(rows, num_groups, E) && dma0 && dma1;
+    const size_t mtiles_sk = (size_t)(rows + SK_BM - 1) / SK_BM + E;
+    if (skinny && (!moelb_allow_lds(ffn_skinny_kernel<0>, SK_LDS_BYTES) ||
+                   !moelb_allow_lds(ffn_skinny_kernel<1>, SK_LDS_BYTES)))
+      return MOELB_ELAUNCH;
     if ((dma0 && !moelb_allow_lds(ffn_mfma_dma_kernel<0>, DL_LDS_BYTES)) ||
         (dma1 && !moelb_allow_lds(ffn_mfma_dma_kernel<1>, DL_LDS_BYTES)) ||
         (pers0 && !moelb_allow_lds(ffn_persistent_kernel<0>, DL_LDS_BYTES)) ||
         (pers1 && !moelb_allow_lds(ffn_persistent_kernel<1>, DL_LDS_BYTES)))
       return MOELB_ELAUNCH;
     if (run_up) {
-      if (pers0)
+      if (skinny)
+        hipLaunchKernelGGL(ffn_skinny_kernel<0>, dim3(mtiles_sk * ntn0 + 8), dim3(MF_THREADS), SK_LDS_BYTES, s,
+                           static_cast<const uint16_t*>(x), rows_x, static_cast<const uint16_t*>(w13), sc, rows, d,
+                           inter, ntn0, static_cast<uint16_t*>(sc.amid));
+      else if (pers0)
         hipLaunchKernelGGL(ffn_persistent_kernel<0>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
                            static_cast<const uint16_t*>(x), rows_x, static_cast<const uint16_t*>(w13), sc, rows, d,
                            inter, ntn0, static_cast<uint16_t*>(sc.amid));
@@ -1250,7 +1435,11 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
       MOELB_CHECK_LAUNCH();
     }
     if (run_down) {
-      if (pers1)
+      if (skinny)
+        hipLaunchKernelGGL(ffn_skinny_kernel<1>, dim3(mtiles_sk * ntn1 + 8), dim3(MF_THREADS), SK_LDS_BYTES, s,
+                           nullptr, rows, static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1,
+                           static_cast<uint16_t*>(y));
+      else if (pers1)
         hipLaunchKernelGGL(ffn_persistent_kernel<1>, dim3(persistent_grid()), dim3(MF_THREADS), DL_LDS_BYTES, s,
                            nullptr, rows, static_cast<const uint16_t*>(w2), sc, rows, d, inter, ntn1,
                            static_cast<uint16_t*>(y));

@@ -101,6 +101,16 @@ def test_persistent_gemms_short_k_several_tiles_per_workgroup(moelb, d, inter):
     _full_check(cfg, tokens=sample_tokens(cfg.T, 64))
 
 
+@pytest.mark.parametrize("T,d,E,k,inter", [(512, 320, 64, 6, 192), (256, 64, 32, 4, 64), (1024, 2048, 128, 8, 768)])
+def test_decode_tiles_64_rows(moelb, T, d, E, k, inter):
+    # fewer than 128 rows per expert: the 64-row tile GEMMs, with column
+    # tails (gate/up 192 = 1.5 x 128, down 320 = 1.25 x 256), one and three
+    # 64-wide K steps, and a decode batch twice C2's
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=T, d=d, E=E, k=k, inter=inter, G=8, N=2, L=1)
+    assert T * k < 128 * E
+    _full_check(cfg)
+
+
 @pytest.mark.parametrize("name,changes", [
     ("c2_qwen3_30b_decode", dict(steps=1, **RAGGED)),
     ("c2_qwen3_30b_decode", dict(steps=1)),
