@@ -38,6 +38,31 @@ int main(void) {
   EXPECT(moelb_grouped_ffn(P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 12, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
          MOELB_EINVAL);
   EXPECT(moelb_combine(P, 8, P, P, 4, 17, 8, MOELB_BF16, NULL, P, NULL) == MOELB_EINVAL);
+  /* every status string, including unknown codes */
+  for (int st = -2; st < 6; ++st) EXPECT(moelb_status_string(st) != NULL);
+  /* workspace sizes: zero for invalid shapes, growing with the batch, no
+     overflow at the largest shapes the entry points accept */
+  EXPECT(moelb_permute_workspace_bytes(64, 2, 8, 0) == 0);
+  EXPECT(moelb_permute_workspace_bytes(1 << 20, 16, 256, 64) > moelb_permute_workspace_bytes(1 << 10, 16, 256, 64));
+  EXPECT(moelb_grouped_ffn_workspace_bytes(-1, 8, 8, 64, 64, MOELB_BF16) == 0);
+  EXPECT(moelb_grouped_ffn_workspace_bytes(1 << 24, 32768, 256, 8192, 8192, MOELB_F32) >
+         (size_t)(1 << 24) * 8192 * 4);
+  /* FFN stages outside [1, MOELB_FFN_ALL]; rows without source rows */
+  EXPECT(moelb_grouped_ffn_stages(0, P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 8, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
+         MOELB_EINVAL);
+  EXPECT(moelb_grouped_ffn_stages(8, P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 8, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
+         MOELB_EINVAL);
+  EXPECT(moelb_grouped_ffn(P, 0, 8, P, 8, 2, 2, 0, NULL, 1, 8, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
+         MOELB_EINVAL);
+  /* operands whose byte offsets would not fit 32 bits */
+  EXPECT(moelb_grouped_ffn(P, 1 << 20, 8, P, 8, 2, 2, 0, NULL, 1, 4096, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
+         MOELB_EINVAL);
+  /* the no-allocation permutation: a workspace beyond its fixed array */
+  EXPECT(moelb_permute_noalloc(NULL, P, 1 << 22, 64, 8, 256, 64, 1, MOELB_BF16, P, P, P, P, P, P, NULL, NULL) ==
+         MOELB_EWORKSPACE);
+  /* split schedule and scheduled split: bad sizes */
+  EXPECT(moelb_split_schedule(P, P, 65, 8, 1, P, NULL) == MOELB_EINVAL);
+  EXPECT(moelb_split_scheduled(P, P, P, NULL, 4, 8, 9, 12, 0, 0, P, P, NULL) == MOELB_EINVAL);
   printf("%s\n", fails ? "failed" : "ok");
   return fails != 0;
 }
