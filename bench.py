@@ -742,6 +742,8 @@ def kernel_work(cfg, active):
         "rank_scatter_kernel (rows)": ("hbm", by["permute_rows"], "B"),
         "ffn_persistent_kernel<0>": ("mfma", f["ffn_gate_up_flop"], "FLOP"),
         "ffn_persistent_kernel<1>": ("mfma", f["ffn_down_flop"], "FLOP"),
+        "ffn_skinny_kernel<0>": ("mfma", f["ffn_gate_up_flop"], "FLOP"),
+        "ffn_skinny_kernel<1>": ("mfma", f["ffn_down_flop"], "FLOP"),
         "combine_kernel": ("hbm", by["combine"], "B"),
         "_ffn_bytes": (active * 2.0 * I * d * b + T * d * b + P * I * b, P * I * b + active * d * I * b + P * d * b),
     }
@@ -780,6 +782,7 @@ def summarize_profile(workload, prof_dir, bench_json):
     KT, F, Wr, MO, GR = (per_kernel(x) for x in (kt, fetch, write, mops, grbm))
     work = kernel_work(cfg, active)
     ffn_bytes = work.pop("_ffn_bytes")
+    f, _ = algorithmic_work(cfg)
     lines = [f"# Kernels of one layer step, {workload}, one MI355X", "",
              "Durations: rocprofv3 kernel trace (average per launch). Traffic: FETCH_SIZE and WRITE_SIZE per "
              f"launch, each scaled by the factor that maps the counter on a plain {cb >> 20} MiB device copy to "
@@ -807,17 +810,27 @@ def summarize_profile(workload, prof_dir, bench_json):
         key = next((w for w in work if base.startswith(w.partition(" (")[0]) and
                     (not tail or w.endswith("(" + tail))), None)
         bound, amt, unit = work[key] if key else ("latency", None, "")
+        if bound == "mfma":
+            # the FFN GEMMs: HBM-bound below the ridge (decode batches stream weights)
+            fb_alg = ffn_bytes[0] if name.endswith("<0>") else ffn_bytes[1]
+            if amt / fb_alg < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9):
+                bound, amt, unit = "hbm", fb_alg, "B"
+        if bound == "hbm" and amt / (PEAK_HBM_GBS * 1e9) < 2e-6:
+            bound = "latency"  # under 2 us of traffic at the HBM peak: launch and latency bound
         if bound == "hbm":
             ach, peak, txt = amt / avg / 1e9, PEAK_HBM_GBS, f"{amt / 1e6:.1f} MB"
             alg_bytes = amt
+            if name.startswith(("ffn_persistent_kernel", "ffn_skinny_kernel")):
+                txt += f" ({(f['ffn_gate_up_flop'] if name.endswith('<0>') else f['ffn_down_flop']) / 1e9:.0f} GFLOP)"
             ach_s = f"{ach:.0f} GB/s"
         elif bound == "mfma":
             ach, peak, txt = amt / avg / 1e12, PEAK_BF16_TFLOPS, f"{amt / 1e12:.3f} TFLOP"
             alg_bytes = ffn_bytes[0] if name.endswith("<0>") else ffn_bytes[1]
             ach_s = f"{ach:.0f} TFLOP/s"
         else:
-            ach = peak = alg_bytes = None
-            txt, ach_s = "-", "-"
+            ach = peak = None
+            alg_bytes = amt if unit == "B" else None
+            txt, ach_s = (f"{amt / 1e6:.2f} MB" if alg_bytes else "-"), "-"
         frac = f"{ach / peak:.3f}" if ach is not None else "-"
         ratio = f"{(fb + wb) / alg_bytes:.2f}" if alg_bytes else "-"
         lines.append(f"| `{name}` | {len(durs)} | {avg * 1e6:.1f} | {bound} | {txt} | {ach_s} | {frac} | "
