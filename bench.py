@@ -456,6 +456,8 @@ def main():
     ap.add_argument("--summarize-profile", nargs=2, metavar=("PROF_DIR", "BENCH_JSON"),
                     help="write profiles/kernels_<workload>.md from a kernel-trace run and three counter runs "
                          "(PROF_DIR/kt, pmc_f, pmc_w, pmc_m) and the bench line of the kernel-trace run")
+    ap.add_argument("--summarize-runs", nargs="+", metavar="ARG",
+                    help="OUT_NAME COMMAND JSON...: write profiles/OUT_NAME.md from bench result lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-times", action="store_true",
                     help="skip the per-virtual-rank FFN timing (for counter runs)")
@@ -467,6 +469,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args.workload, *args.summarize_profile)
+        return
+    if args.summarize_runs:
+        summarize_runs(args.summarize_runs[2:], args.summarize_runs[0], args.summarize_runs[1])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the expert-parallel ranks are simulated on a single MI355X; "
@@ -863,6 +868,54 @@ def summarize_profile(workload, prof_dir, bench_json):
                       "of a plain device copy of copy_bytes"}
         with open(TRAFFIC_JSON, "w") as fh:
             json.dump(tr, fh, indent=1)
+
+
+def summarize_runs(paths, out_name, command):
+    """A markdown summary of bench.py result lines (one JSON file each):
+    step time, throughput and fractions per workload, the stage medians, the
+    balance figures, per-layer or per-step rows, the CPU baseline and any
+    side studies.  Written to profiles/<out_name>.md."""
+    rows = [json.load(open(p_)) for p_ in paths]
+    L = [f"# bench.py results, one MI355X", "", "Command (repository root):", "", "```", command, "```", "",
+         "| workload | ms/step (mean / median) | tokens/s | layer MFMA frac | gate/up roofline | FFN MFMA frac "
+         "| lookahead hit | spatial static / plan / split | max t_r ms | time-spatial | U_eff |",
+         "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        c, ro, rt, b = r["config"], r["roofline"], r.get("routing", {}), r.get("balance", {})
+        L.append(f"| {c['workload']} | {r['ms_per_step']:.4f} / {r.get('ms_per_step_median', 0):.4f} | "
+                 f"{r['value']:.0f} | {r['mfma_frac_layer']:.3f} | {ro['frac']:.3f} of {ro['bound']} "
+                 f"({ro['achieved']} {ro['unit']}) | {r['ffn_mfma_frac']:.3f} | {rt.get('lookahead_hit', '-')} | "
+                 f"{rt.get('spatial_static', '-')} / {rt.get('spatial_plan_even', '-')} / "
+                 f"{rt.get('spatial_split', '-')} | {b.get('rank_ffn_max_ms', '-')} | "
+                 f"{b.get('time_spatial', '-')} | {b.get('u_eff', '-')} |")
+    for r in rows:
+        c = r["config"]
+        L += ["", f"## {c['workload']}", "", "Stage medians (ms, marked pass): " +
+              ", ".join(f"{k} {v}" for k, v in r["stages_ms"].items())]
+        if r.get("hbm_frac"):
+            L.append("")
+            L.append("HBM fractions: " + ", ".join(f"{k} {v}" for k, v in r["hbm_frac"].items()))
+        if r.get("units"):
+            L += ["", "| unit | ms median | gate/up ms | plan ms (side) | split ms | permute ms | lookahead hit | "
+                  "spatial static / plan / split | improved | U_eff |", "|---|---|---|---|---|---|---|---|---|---|"]
+            for u in r["units"]:
+                st = u["stages_ms"]
+                L.append(f"| {u['name']} | {u['ms_median']} | {st['ffn_gate_up_gemm']} | "
+                         f"{st['side_histogram_plan']} | {st['split']} | {st['permute']} | {u['lookahead_hit']} | "
+                         f"{u['spatial_static']} / {u['spatial_plan_even']} / {u['spatial_split']} | "
+                         f"{u['improved']} | {u.get('u_eff', '-')} |")
+            L += ["", "Means: " + ", ".join(f"{k} {v}" for k, v in r["units_mean"].items())]
+        if r.get("cpu_baseline"):
+            cb = r["cpu_baseline"]
+            L += ["", f"CPU oracle: {cb['value']:.0f} {cb['unit']} on {cb['cores']} cores ({cb.get('cpu_model')}, "
+                  f"BLAS threads {cb.get('blas_threads')}); {cb['sample']}; stage seconds {cb.get('stage_s')}"]
+        for key in ("two_stage", "split_variants", "freebalance", "stale_split", "graph"):
+            if r.get(key):
+                L += ["", f"{key}: `{json.dumps(r[key])}`"]
+    out = os.path.join(ROOT, "profiles", out_name + ".md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L))
 
 
 def _kernel_sha():

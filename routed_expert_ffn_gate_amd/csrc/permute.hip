@@ -77,14 +77,23 @@ inline size_t ws_layout(int T, int k, int E, int G, PermuteWs* w, char* base) {
   return off;
 }
 
-__device__ __forceinline__ uint64_t host_mask(const int32_t* home, const int32_t* replica, int G, int N, int e) {
-  int h = home[e];
-  h = (h >= 0 && h < G) ? h : 0;
-  uint64_t m = 1ull << h;
-  for (int r = 0; r < G; ++r)
-    for (int j = 0; j < N; ++j)
-      if (replica[r * N + j] == e) m |= 1ull << r;
-  return m;
+// Host masks of experts [0, E) into LDS, by the whole workgroup: each expert's
+// home bit, then one replica entry per thread ORed in (no thread walks the
+// replica table).  Entries outside [0, E) are ignored.
+__device__ __forceinline__ void block_host_masks(const int32_t* __restrict__ home,
+                                                 const int32_t* __restrict__ replica, int G, int N, int E,
+                                                 uint64_t* hmask) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int h = home[e];
+    h = (h >= 0 && h < G) ? h : 0;
+    hmask[e] = 1ull << h;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < G * N; q += blockDim.x) {
+    const int e = replica[q];
+    if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&hmask[e]), 1ull << (q / N));
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int T, int k, int E, int G,
@@ -109,28 +118,37 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 // Expert e's remote pool (R pairs, in pair-id order) over its hosts in
 // ascending rank: host i serves places [host_lo, host_hi) -- host_count[e,h]
 // pairs each (negative read as 0), the highest host also the rest; the sizes
-// of the remote groups follow.
-__device__ void remote_ranges(int e, uint64_t mask, int R, const int32_t* __restrict__ host_count, int E, int G,
-                              PermuteWs ws) {
-  const int m = __popcll(mask);
-  int cum = 0, i = 0;
-  for (int h = 0; h < G; ++h) {
-    int size = 0;
-    if ((mask >> h) & 1ull) {
-      const int hc = max(host_count[(size_t)e * G + h], 0);
-      const int lo = min(cum, R);
-      cum = (cum > R - hc) ? R + 1 : cum + hc;  // saturating: stays > R once past it
-      int hi = min(cum, R);
-      if (i == m - 1) hi = R;                    // the highest host takes the rest
-      size = hi - lo;
-      ws.host_rank[(size_t)e * G + i] = h;
-      ws.host_lo[(size_t)e * G + i] = lo;
-      ws.host_hi[(size_t)e * G + i] = hi;
-      ++i;
-    }
-    ws.gsize[(size_t)(1 * G + h) * E + e] = size;
+// of the remote groups follow.  One wave, lane h for rank h (G <= 64): the
+// host's place is a wave prefix sum of the hosts' shares, capped at R + 1
+// (capped sums of non-negative shares stay associative).
+__device__ void remote_ranges_wave(int e, uint64_t mask, int R, const int32_t* __restrict__ host_count, int E,
+                                   int G, PermuteWs ws) {
+  const int h = threadIdx.x & (MOELB_WAVE - 1);
+  const bool host = h < G && ((mask >> h) & 1ull);
+  const int hc = host ? max(host_count[(size_t)e * G + h], 0) : 0;
+  const long long cap = (long long)R + 1;
+  long long incl = min((long long)hc, cap);
+#pragma unroll
+  for (int o = 1; o < MOELB_WAVE; o <<= 1) {
+    const long long v = __shfl_up(incl, o, MOELB_WAVE);
+    if (h >= o) incl = min(incl + v, cap);
   }
-  for (; i < G; ++i) ws.host_rank[(size_t)e * G + i] = -1;
+  const long long up = __shfl_up(incl, 1, MOELB_WAVE);
+  const int excl = h == 0 ? 0 : (int)min(up, (long long)R);
+  const int m = __popcll(mask);
+  const int i = __popcll(mask & lanemask_lt());  // this host's index among e's hosts
+  const int hi_all = i == m - 1 ? R : (int)min(incl, (long long)R);  // the highest host takes the rest
+  if (host) {
+    const int lo = excl;
+    const int hi = hi_all;
+    ws.host_rank[(size_t)e * G + i] = h;
+    ws.host_lo[(size_t)e * G + i] = lo;
+    ws.host_hi[(size_t)e * G + i] = hi;
+  }
+  if (h < G) {
+    ws.gsize[(size_t)(1 * G + h) * E + e] = host ? hi_all - excl : 0;
+    if (h >= m) ws.host_rank[(size_t)e * G + h] = -1;
+  }
 }
 
 // One workgroup per expert: a block scan over the chunks (token order) of the
@@ -148,7 +166,14 @@ __global__ __launch_bounds__(ESCAN_THREADS) void expert_scan_kernel(const int32_
   __shared__ uint64_t s_mask;
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
-  if (tid == 0) s_mask = host_mask(home, replica, G, N, e);
+  if (tid == 0) {
+    int h = home[e];
+    h = (h >= 0 && h < G) ? h : 0;
+    s_mask = 1ull << h;
+  }
+  __syncthreads();
+  for (int q = tid; q < G * N; q += ESCAN_THREADS)
+    if (replica[q] == e) atomicOr(reinterpret_cast<unsigned long long*>(&s_mask), 1ull << (q / N));
   __syncthreads();
   const uint64_t mask = s_mask;
   const int nch = G * nchr;
@@ -204,20 +229,20 @@ __global__ __launch_bounds__(ESCAN_THREADS) void expert_scan_kernel(const int32_
     }
     ws.gsize[(size_t)(0 * G + s) * E + e] = size;
   }
-  if (tid == 0) {
-    ws.remote_total[e] = R;
-    if (host_count) remote_ranges(e, mask, R, host_count, E, G, ws);
-  }
+  if (tid == 0) ws.remote_total[e] = R;
+  if (host_count && tid < MOELB_WAVE) remote_ranges_wave(e, mask, R, host_count, E, G, ws);
 }
 
-// Remote phase: host ranges of every expert (thread e).
+// Remote phase: host ranges of every expert (one wave per expert).
 __global__ __launch_bounds__(256) void remote_ranges_kernel(const int32_t* __restrict__ home,
                                                             const int32_t* __restrict__ replica,
                                                             const int32_t* __restrict__ host_count, int E, int G,
                                                             int N, PermuteWs ws) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ uint64_t hmask[MOELB_MAX_E];
+  block_host_masks(home, replica, G, N, E, hmask);
+  const int e = blockIdx.x * (blockDim.x / MOELB_WAVE) + threadIdx.x / MOELB_WAVE;
   if (e >= E) return;
-  remote_ranges(e, host_mask(home, replica, G, N, e), ws.remote_total[e], host_count, E, G, ws);
+  remote_ranges_wave(e, hmask[e], ws.remote_total[e], host_count, E, G, ws);
 }
 
 // Exclusive scan of the 2GE group sizes into group_off (one workgroup).
@@ -249,6 +274,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void group_scan_kernel(const int32_t*
   if (tid == SCAN_THREADS - 1) group_off[ngroups] = b + part[tid];
 }
 
+constexpr int RS_STAGE_EG = 4096;  // 48 KiB of LDS host ranges
+
 // LOCAL_ONLY (local phase of the two-phase form): remote pairs get pos -1 and
 // their place rho in ws.rho (every other pair -1 there); no perm entry or row
 // copy for them yet.
@@ -264,6 +291,19 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
   __shared__ int cnt[MOELB_MAX_E];
   __shared__ uint64_t hmask[MOELB_MAX_E];
   __shared__ int qpos[MAX_CHUNK * MOELB_MAX_K];
+  // host ranges of every expert in LDS when they fit (E*G <= RS_STAGE_EG):
+  // a remote pair's host search then reads LDS, not a chain of global loads
+  extern __shared__ int hr_lds[];  // [3][E*G]: host rank, first place, end place
+  const bool staged = !LOCAL_ONLY && E * G <= RS_STAGE_EG;
+  const int32_t* h_rank = staged ? hr_lds : ws.host_rank;
+  const int32_t* h_lo = staged ? hr_lds + E * G : ws.host_lo;
+  const int32_t* h_hi = staged ? hr_lds + 2 * E * G : ws.host_hi;
+  if (staged)
+    for (int i = threadIdx.x; i < E * G; i += blockDim.x) {
+      hr_lds[i] = ws.host_rank[i];
+      hr_lds[E * G + i] = ws.host_lo[i];
+      hr_lds[2 * E * G + i] = ws.host_hi[i];
+    }
   const int c = blockIdx.x;
   const int s = c / nchr, ci = c % nchr;
   const int per = Ttok / G;
@@ -271,11 +311,8 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
   const int t1 = min(t0 + chunk, (s + 1) * per);
   const int ntok = max(0, t1 - t0);
   const int np = ntok * k;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    cnt[e] = 0;
-    hmask[e] = host_mask(home, replica, G, N, e);
-  }
-  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  block_host_masks(home, replica, G, N, E, hmask);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const uint64_t below = lanemask_lt();
@@ -309,9 +346,9 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
         } else {
           // rank is rho, this pair's place in e's remote pool
           int i = 0;
-          while (i + 1 < G && ws.host_rank[(size_t)e * G + i + 1] >= 0 && rank >= ws.host_hi[(size_t)e * G + i]) ++i;
-          const int hst = ws.host_rank[(size_t)e * G + i];
-          rank -= ws.host_lo[(size_t)e * G + i];
+          while (i + 1 < G && h_rank[e * G + i + 1] >= 0 && rank >= h_hi[e * G + i]) ++i;
+          const int hst = h_rank[e * G + i];
+          rank -= h_lo[e * G + i];
           key = (1 * G + hst) * E + e;
         }
         if (key >= 0) {
@@ -435,8 +472,9 @@ static int permute_launch(bool local_only, const void* h, const int32_t* idx, in
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, w.gsize, (local_only ? 1 : 2) * G * E,
                      nullptr, group_off);
   MOELB_CHECK_LAUNCH();
+  const size_t rs_lds = (!local_only && E * G <= RS_STAGE_EG) ? (size_t)3 * E * G * sizeof(int) : 0;
 #define PERMUTE_SCATTER(TY, LO)                                                                                  \
-  hipLaunchKernelGGL((rank_scatter_kernel<TY, LO>), dim3(nchunks), dim3(256), 0, s, static_cast<const TY*>(h), \
+  hipLaunchKernelGGL((rank_scatter_kernel<TY, LO>), dim3(nchunks), dim3(256), rs_lds, s, static_cast<const TY*>(h), \
                      idx, T, d, k, E, G, N, chunk, nchr, home, rep, w, group_off, perm, pos, static_cast<TY*>(x_perm))
   if (dtype == MOELB_BF16) {
     if (local_only) PERMUTE_SCATTER(uint16_t, true); else PERMUTE_SCATTER(uint16_t, false);
@@ -523,7 +561,7 @@ extern "C" int moelb_permute_remote(const void* h, const int32_t* idx, int T, in
   ws_layout(T, k, E, G, &w, static_cast<char*>(ws));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t* rep = N > 0 ? replica : home;
-  hipLaunchKernelGGL(remote_ranges_kernel, dim3((E + 255) / 256), dim3(256), 0, s, home, rep, host_count, E, G, N, w);
+  hipLaunchKernelGGL(remote_ranges_kernel, dim3((E + 3) / 4), dim3(256), 0, s, home, rep, host_count, E, G, N, w);
   MOELB_CHECK_LAUNCH();
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, w.gsize + (size_t)G * E, G * E,
                      group_off + (size_t)G * E, group_off + (size_t)G * E);
