@@ -290,6 +290,8 @@ int moelb_split_stale(const int32_t* counts, const int32_t* home, const int32_t*
  *  perm, pos  [T*k]     int32 out
  *  x_perm     [T*k,d]   dtype out or NULL: x_perm[q] = h[perm[q] div k]
  * Requires T % G == 0, k <= 16, E <= 256, G <= 64, N <= 8, d % 8 == 0.
+ * With x_perm NULL, T*k <= 8192 and E*G <= 2048 the call is one launch of one
+ * workgroup (the same outputs; the workspace is then not touched), else four.
  */
 size_t moelb_permute_workspace_bytes(int T, int k, int E, int G);
 int moelb_permute(const void* h, const int32_t* idx, int T, int d, int k, int E, int G, int N,

@@ -20,6 +20,10 @@
 //      pos/perm; then all waves copy each token's row once into its k
 //      destinations (read once, written k times).
 //
+// Batches of at most 8192 pairs with no rows to copy run the same sort in one
+// workgroup instead (permute_one_wg_kernel below): at decode sizes the four
+// launches cost more than their work.
+//
 // Two-phase form (the two stages run apart, so MoE_local can start before
 // the split exists): the local phase does all of the above except what
 // depends on host_count -- it places the local pairs and keeps each remote
@@ -421,6 +425,210 @@ __global__ __launch_bounds__(RS_THREADS) void remote_scatter_kernel(const T* __r
   }
 }
 
+// ---------------------------------------------------------------- one-workgroup form
+//
+// Small batches (decode) spend the four-launch sort on launch latency.  Up to
+// OW_MAX_PAIRS pairs with E*G <= OW_MAX_EG, and no rows to copy, the same
+// result comes from one workgroup, everything but the inputs and outputs in
+// LDS:
+//   1. each wave takes segments of pairs (a rank's tokens cut into J pieces,
+//      so there are at least as many segments as waves) and ranks every pair
+//      among the pairs of its expert in its segment: the lanes holding expert
+//      e OR their bits into a per-wave LDS word for e, read it back, and take
+//      ranks from the popcount below the lane; the lowest such lane adds the
+//      count to the segment's counter of e and clears the word;
+//   2. one thread per expert walks the segments in token order, turning each
+//      segment's count into its base (inside the rank's local group when the
+//      rank hosts e, inside e's remote pool otherwise), and deals the remote
+//      pool over the hosts (host ranges and remote group sizes);
+//   3. a block scan of the 2GE group sizes gives group_off;
+//   4. the waves walk their segments again and place every pair.
+// Pair ranks are stable (pair-id order), so the result is the four-launch
+// form's, bit for bit.
+constexpr int OW_THREADS = 1024;
+constexpr int OW_WAVES = OW_THREADS / MOELB_WAVE;
+constexpr int OW_MAX_PAIRS = 8192;  // ranks inside a segment fit 16 bits
+constexpr int OW_MAX_EG = 2048;
+
+// Token pieces per rank: enough segments to give every wave one.
+__host__ __device__ inline int ow_pieces(int G) { return G >= OW_WAVES ? 1 : (OW_WAVES + G - 1) / G; }
+
+struct OwLds {
+  size_t hmask, wmask, segcnt, lrank, goff, hrank, hlo, hhi, part, total;
+};
+
+__host__ __device__ inline OwLds ow_lds(int E, int G, int P) {
+  const int nseg = G * ow_pieces(G);
+  OwLds L;
+  size_t off = 0;
+  auto take = [&](size_t* field, size_t bytes) {
+    *field = off;
+    off += (bytes + 15) & ~static_cast<size_t>(15);
+  };
+  take(&L.hmask, (size_t)E * 8);
+  take(&L.wmask, (size_t)OW_WAVES * E * 8);
+  take(&L.segcnt, (size_t)nseg * E * 4);
+  take(&L.lrank, (size_t)P * 2);
+  take(&L.goff, ((size_t)2 * G * E + 1) * 4);
+  take(&L.hrank, (size_t)E * G * 4);
+  take(&L.hlo, (size_t)E * G * 4);
+  take(&L.hhi, (size_t)E * G * 4);
+  take(&L.part, (size_t)(OW_WAVES + 1) * 4);
+  L.total = off;
+  return L;
+}
+
+__global__ __launch_bounds__(OW_THREADS) void permute_one_wg_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int G, int N, const int32_t* __restrict__ home,
+    const int32_t* __restrict__ replica, const int32_t* __restrict__ host_count, int32_t* __restrict__ group_off,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  extern __shared__ __align__(16) char ow_smem[];
+  const int per = T / G;
+  const int J = ow_pieces(G);
+  const int nseg = G * J;
+  const OwLds L = ow_lds(E, G, T * k);
+  uint64_t* hmask = reinterpret_cast<uint64_t*>(ow_smem + L.hmask);
+  int* segcnt = reinterpret_cast<int*>(ow_smem + L.segcnt);
+  uint16_t* lrank = reinterpret_cast<uint16_t*>(ow_smem + L.lrank);
+  int* goff = reinterpret_cast<int*>(ow_smem + L.goff);
+  int* hrank = reinterpret_cast<int*>(ow_smem + L.hrank);
+  int* hlo = reinterpret_cast<int*>(ow_smem + L.hlo);
+  int* hhi = reinterpret_cast<int*>(ow_smem + L.hhi);
+  int* part = reinterpret_cast<int*>(ow_smem + L.part);
+  const int tid = threadIdx.x, lane = tid & (MOELB_WAVE - 1), w = tid / MOELB_WAVE;
+  uint64_t* wm = reinterpret_cast<uint64_t*>(ow_smem + L.wmask) + (size_t)w * E;
+  for (int i = tid; i < nseg * E; i += OW_THREADS) segcnt[i] = 0;
+  for (int i = lane; i < E; i += MOELB_WAVE) wm[i] = 0ull;
+  block_host_masks(home, replica, G, N, E, hmask);  // its barriers also cover the clearing above
+
+  // 1. ranks inside (segment, expert); one wave's LDS traffic is in order, so
+  //    the OR, the reads and the leader's update need no barrier
+  const uint64_t below = lanemask_lt();
+  for (int seg = w; seg < nseg; seg += OW_WAVES) {
+    const int s = seg / J, j = seg % J;
+    const int p1 = (s * per + ((j + 1) * per) / J) * k;
+    int* cnt = segcnt + (size_t)seg * E;
+    for (int pb = (s * per + (j * per) / J) * k; pb < p1; pb += MOELB_WAVE) {
+      const int p = pb + lane;
+      const int e = p < p1 ? idx[p] : -1;
+      const bool valid = e >= 0 && e < E;
+      if (valid) atomicOr(reinterpret_cast<unsigned long long*>(&wm[e]), 1ull << lane);
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t m = valid ? wm[e] : 0ull;
+      const int base = valid ? cnt[e] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (m & below) == 0ull) {
+        cnt[e] = base + __popcll(m);
+        wm[e] = 0ull;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (valid) lrank[p] = static_cast<uint16_t>(base + __popcll(m & below));
+    }
+  }
+  __syncthreads();
+
+  // 2. segment bases, local group sizes, host ranges and remote group sizes
+  if (tid < E) {
+    const int e = tid;
+    const uint64_t mask = hmask[e];
+    int loc = 0, rem = 0;
+    for (int seg = 0; seg < nseg; ++seg) {
+      const int s = seg / J;
+      const int c = segcnt[seg * E + e];
+      if ((mask >> s) & 1ull) {
+        if (seg % J == 0) loc = 0;
+        segcnt[seg * E + e] = loc;
+        loc += c;
+      } else {
+        segcnt[seg * E + e] = rem;
+        rem += c;
+      }
+      if (seg % J == J - 1) goff[s * E + e] = ((mask >> s) & 1ull) ? loc : 0;
+    }
+    // remote pool [0, rem) over the hosts in ascending rank: host_count[e,h]
+    // places each (negative read as 0), capped at the pool, the highest host
+    // also the rest
+    const int m = __popcll(mask);
+    int i = 0, run = 0;
+    for (int hst = 0; hst < G; ++hst) {
+      int size = 0;
+      if ((mask >> hst) & 1ull) {
+        const long long hc = max(host_count[(size_t)e * G + hst], 0);
+        const int hi = i == m - 1 ? rem : (int)min((long long)run + hc, (long long)rem);
+        hrank[e * G + i] = hst;
+        hlo[e * G + i] = run;
+        hhi[e * G + i] = hi;
+        size = hi - run;
+        run = hi;
+        ++i;
+      }
+      goff[(G + hst) * E + e] = size;
+    }
+    for (; i < G; ++i) hrank[e * G + i] = -1;
+  }
+  __syncthreads();
+
+  // 3. group sizes -> exclusive offsets (each thread a contiguous run)
+  const int ng = 2 * G * E;
+  const int run_len = (ng + OW_THREADS - 1) / OW_THREADS;
+  const int g0 = min(tid * run_len, ng), g1 = min(g0 + run_len, ng);
+  int sum = 0;
+  for (int g = g0; g < g1; ++g) sum += goff[g];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < MOELB_WAVE; o <<= 1) {
+    const int v = __shfl_up(incl, o, MOELB_WAVE);
+    if (lane >= o) incl += v;
+  }
+  if (lane == MOELB_WAVE - 1) part[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int v = lane < OW_WAVES ? part[lane] : 0;
+    int wi = v;
+#pragma unroll
+    for (int o = 1; o < OW_WAVES; o <<= 1) {
+      const int u = __shfl_up(wi, o, MOELB_WAVE);
+      if (lane >= o) wi += u;
+    }
+    if (lane < OW_WAVES) part[lane] = wi - v;
+    if (lane == OW_WAVES - 1) part[OW_WAVES] = wi;
+  }
+  __syncthreads();
+  int acc = part[w] + incl - sum;
+  for (int g = g0; g < g1; ++g) {
+    const int size = goff[g];
+    goff[g] = acc;
+    acc += size;
+  }
+  if (tid == 0) goff[ng] = part[OW_WAVES];
+  __syncthreads();
+  for (int g = tid; g <= ng; g += OW_THREADS) group_off[g] = goff[g];
+
+  // 4. place every pair
+  for (int seg = w; seg < nseg; seg += OW_WAVES) {
+    const int s = seg / J, j = seg % J;
+    const int p1 = (s * per + ((j + 1) * per) / J) * k;
+    const int* base = segcnt + (size_t)seg * E;
+    for (int p = (s * per + (j * per) / J) * k + lane; p < p1; p += MOELB_WAVE) {
+      const int e = idx[p];
+      int q = -1;
+      if (e >= 0 && e < E) {
+        const int r = base[e] + lrank[p];
+        if ((hmask[e] >> s) & 1ull) {
+          q = goff[s * E + e] + r;
+        } else {
+          // r is rho, the pair's place in e's remote pool
+          int i = 0;
+          while (i + 1 < G && hrank[e * G + i + 1] >= 0 && r >= hhi[e * G + i]) ++i;
+          q = goff[(G + hrank[e * G + i]) * E + e] + r - hlo[e * G + i];
+        }
+        perm[q] = p;
+      }
+      pos[p] = q;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" size_t moelb_permute_workspace_bytes(int T, int k, int E, int G) {
@@ -464,6 +672,14 @@ static int permute_launch(bool local_only, const void* h, const int32_t* idx, in
   const int nchr = per > 0 ? (per + chunk - 1) / chunk : 1;
   const int nchunks = G * nchr;
   const int32_t* rep = N > 0 ? replica : home;
+  if (!local_only && !x_perm && (long long)T * k <= OW_MAX_PAIRS && E * G <= OW_MAX_EG) {
+    const size_t lds = ow_lds(E, G, T * k).total;
+    if (!moelb_allow_lds(permute_one_wg_kernel, lds)) return MOELB_ELAUNCH;
+    hipLaunchKernelGGL(permute_one_wg_kernel, dim3(1), dim3(OW_THREADS), lds, s, idx, T, k, E, G, N, home, rep,
+                       host_count, group_off, perm, pos);
+    MOELB_CHECK_LAUNCH();
+    return MOELB_OK;
+  }
   hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(256), 0, s, idx, T, k, E, G, chunk, nchr, w.chunk_counts);
   MOELB_CHECK_LAUNCH();
   hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(ESCAN_THREADS), 0, s, home, rep,

@@ -255,6 +255,70 @@ def test_permute_two_phases_equal_one_call(moelb):
             assert torch.equal(a, b), trial
 
 
+@pytest.mark.parametrize("T,k,E,G,N", [
+    (512, 8, 128, 8, 2),     # decode shape, 4096 pairs
+    (1024, 8, 256, 8, 8),    # 8192 pairs and E*G = 2048: the one-workgroup limits
+    (1032, 8, 256, 8, 8),    # 8256 pairs: past the limit
+    (128, 16, 32, 64, 8),    # 64 ranks, one segment each
+    (96, 3, 48, 3, 1),       # 3 ranks cut into 6 pieces each, ragged pieces
+    (2048, 4, 64, 16, 3),    # 16 ranks, one segment per wave
+    (60, 16, 256, 4, 8),
+    (7, 5, 13, 1, 0),        # one rank, no replicas
+    (0, 4, 16, 4, 1),        # empty batch
+])
+def test_permute_one_workgroup_form(moelb, T, k, E, G, N):
+    """moelb_permute without rows to copy runs batches of at most 8192 pairs
+    with E*G <= 2048 in one workgroup; with rows it always takes the four-launch
+    sort.  Both must give the oracle's outputs bit for bit: pairs left out,
+    replica slots out of range, shares from the split and arbitrary shares
+    (negative, short of or past the pool)."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(T * 131 + E * 7 + G)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    for trial in range(3):
+        pop = 1.0 / (1 + rng.permutation(E)) ** 1.2
+        idx = rng.choice(E, size=(T, k), p=pop / pop.sum()).astype(np.int32)
+        if T:
+            idx[rng.random((T, k)) < 0.02] = -1
+            idx[rng.random((T, k)) < 0.01] = E + 3
+        home = (np.arange(E) * G // E).astype(np.int32)
+        rep = rng.integers(-2, E + 2, (G, max(N, 1))).astype(np.int32)[:, :N]
+        idx_t, home_t, rep_t = t(idx), t(home), t(rep.reshape(G, N))
+        if trial == 0:
+            hc = rng.integers(-3, 40, (E, G)).astype(np.int32)
+            hc_t = t(hc)
+        else:
+            counts = torch.empty((G, E), dtype=torch.int32, device=dev)
+            M.moelb_histogram(idx_t, G, counts)
+            hc_t = torch.empty((E, G), dtype=torch.int32, device=dev)
+            ld = torch.empty(G, dtype=torch.int32, device=dev)
+            rep_s = rep_t if N else torch.full((G, 1), -1, dtype=torch.int32, device=dev)
+            M.moelb_split(counts, home_t, rep_s, hc_t, ld, passes=12 * (trial - 1))
+            torch.cuda.synchronize()
+            hc = hc_t.cpu().numpy()
+        ws = torch.empty(M.moelb_permute_workspace_bytes(T, k, E, G), dtype=torch.uint8, device=dev)
+        d = 64
+        h = torch.randn((T, d), device=dev).to(torch.bfloat16)
+        outs = []
+        for rows in (False, True):
+            off = torch.full((2 * G * E + 1,), -9, dtype=torch.int32, device=dev)
+            perm = torch.full((T * k,), -9, dtype=torch.int32, device=dev)
+            pos = torch.full((T * k,), -9, dtype=torch.int32, device=dev)
+            xp = torch.zeros((T * k, d), dtype=torch.bfloat16, device=dev) if rows else None
+            M.moelb_permute(h if rows else None, idx_t, G, home_t, rep_t, hc_t, ws, off, perm, pos, xp,
+                            d=d, dtype=M.MOELB_BF16)
+            torch.cuda.synchronize()
+            outs.append([off.cpu().numpy(), perm.cpu().numpy(), pos.cpu().numpy()])
+        ref = O.permute(idx, home, rep if N else None, hc, G, E)
+        nvalid = int(ref[0][-1])
+        for got in outs:
+            np.testing.assert_array_equal(got[0], ref[0], err_msg=f"group_off trial {trial}")
+            np.testing.assert_array_equal(got[1][:nvalid], ref[1], err_msg=f"perm trial {trial}")
+            np.testing.assert_array_equal(got[2], ref[2], err_msg=f"pos trial {trial}")
+
+
 def test_zero_router_single_hot_set(moelb):
     # W = 0: every token picks the same k experts (by bias), so a few groups
     # hold every pair -- the most skewed case the method has.
