@@ -40,6 +40,17 @@ __device__ __forceinline__ uint32_t bf16x2_pack(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// 16-byte non-temporal store and load: for streams much larger than the
+// caches that are written or read exactly once (the hint keeps them from
+// evicting reusable lines).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 // Element access for the two storage types.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -1013,7 +1013,9 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
           const int v = cur.v0 + (rl >> 6) * 128 + rd * 64 + (rl & 63);
           const int col = n0 + ch * 8;
           const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 128 + ((ch ^ (rl & 15)) * 8));
-          if (v < cur.vend && col < inter) *reinterpret_cast<uint4*>(y + (size_t)v * inter + col) = val;
+          // non-temporal: the activations (P x I) far exceed the caches and
+          // are read once, by the down GEMM
+          if (v < cur.vend && col < inter) store_nt16(y + (size_t)v * inter + col, val);
         }
         __syncthreads();
       }
@@ -1042,7 +1044,8 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
           const int col = n0 + ch * 8;
           const int orow = __shfl(out_row, rd * 16 + (lane >> 5) * 8 + i, 64);
           const uint4 val = *reinterpret_cast<const uint4*>(Cs + rl * 256 + ((ch ^ (rl & 15)) * 8));
-          if (v < cur.vend && col < d) *reinterpret_cast<uint4*>(y + (size_t)orow * d + col) = val;
+          // non-temporal: Y (P x d) is read once, by the combine
+          if (v < cur.vend && col < d) store_nt16(y + (size_t)orow * d + col, val);
         }
         __syncthreads();
       }
@@ -1090,8 +1093,13 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
 // 64-wide K step stream global -> LDS with global_load_lds_dwordx4 into a
 // ring of three stages, two steps ahead of the one computed; one barrier per
 // step.  Each lane stores its four adjacent output columns straight from the
-// accumulators (8 bytes).  (A persistent form with a four-stage ring that
-// streams across tile boundaries measured slower on the decode shape.)
+// accumulators (8 bytes).  Measured on the decode shape (T = 512, d = 2048,
+// E = 128, k = 8, I = 768) and dropped: a persistent form with a four-stage
+// ring streaming across tile boundaries (slower); 128-column tiles with a
+// five-stage ring, twice the tiles for a smaller last round (gate/up 0.135
+// against 0.125 ms); a four-stage ring (the same); a two-stage ring with two
+// workgroups per CU (the same).  The depth of the stream is not what bounds
+// these GEMMs at about 4.2 TB/s.
 constexpr int SK_BM = 64;
 constexpr int SK_BN = 256;
 constexpr int SK_STAGE = (SK_BM + SK_BN) * DL_BK;  // elements per stage

@@ -369,15 +369,33 @@ __global__ __launch_bounds__(256) void rank_scatter_kernel(const T* __restrict__
   }
   __syncthreads();
   if (x_perm == nullptr) return;
-  // copy each token's row to its k destinations: 16-byte chunks
+  // copy each token's row to its k destinations in 16-byte chunks: each
+  // thread loads U chunks before it stores any (U loads in flight), and the
+  // stores are non-temporal -- x_perm is written once and not read here, and
+  // keeping it out of the caches raised the copy from 4.4 to 4.9 TB/s
   const int nvec = d * (int)sizeof(T) / 16;
-  for (int tl = 0; tl < ntok; ++tl) {
-    const uint4* src = reinterpret_cast<const uint4*>(h + (size_t)(t0 + tl) * d);
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-      const uint4 val = src[v];
-      for (int j = 0; j < k; ++j) {
-        const int q = qpos[tl * k + j];
-        if (q >= 0) reinterpret_cast<uint4*>(x_perm + (size_t)q * d)[v] = val;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int U = 8;
+  const int items = ntok * nvec;
+  for (int i0 = threadIdx.x; i0 < items; i0 += U * 256) {
+    u32x4 val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 256;
+      if (i < items) {
+        const int tl = i / nvec;
+        val[u] = reinterpret_cast<const u32x4*>(h + (size_t)(t0 + tl) * d)[i - tl * nvec];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 256;
+      if (i < items) {
+        const int tl = i / nvec, v = i - tl * nvec;
+        for (int j = 0; j < k; ++j) {
+          const int q = qpos[tl * k + j];
+          if (q >= 0) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(x_perm + (size_t)q * d) + v);
+        }
       }
     }
   }
@@ -419,9 +437,10 @@ __global__ __launch_bounds__(RS_THREADS) void remote_scatter_kernel(const T* __r
     const int qi = qs[i];
     if (qi < 0) continue;
     const int p = blockIdx.x * RS_THREADS + i;
-    const uint4* src = reinterpret_cast<const uint4*>(h + (size_t)(p / k) * d);
-    uint4* dst = reinterpret_cast<uint4*>(x_perm + (size_t)qi * d);
-    for (int v = threadIdx.x; v < nvec; v += RS_THREADS) dst[v] = src[v];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)(p / k) * d);
+    u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (size_t)qi * d);
+    for (int v = threadIdx.x; v < nvec; v += RS_THREADS) __builtin_nontemporal_store(src[v], dst + v);
   }
 }
 
