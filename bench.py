@@ -721,14 +721,22 @@ def _dispatches(path, counter=None):
     return out
 
 
-# the row-copying permutation is the same kernel as the index-only one; a
-# launch that copies rows runs far longer
-ROWS_SPLIT_S = 100e-6
+# the row-copying permutation is the same kernel as the index-only one: a
+# launch is a row copy if it writes more than ROWS_WRITE_FACTOR times the
+# index bytes (12 per pair) in the WRITE_SIZE run, whose launches come in the
+# same order as in every other run of the same command
+ROWS_WRITE_FACTOR = 4.0
 
 
-def _kernel_key(name, dur):
+def _rows_launches(write_rows, fw, pairs):
+    """For each rank_scatter_kernel launch in order: does it copy rows?"""
+    return [v * 1024 * fw > ROWS_WRITE_FACTOR * 12.0 * pairs
+            for n, _, v in write_rows if n.startswith("rank_scatter_kernel")]
+
+
+def _kernel_key(name, rows_flag):
     if name.startswith("rank_scatter_kernel"):
-        return name + (" (rows)" if dur > ROWS_SPLIT_S else " (indices)")
+        return name + (" (rows)" if rows_flag else " (indices)")
     return name
 
 
@@ -778,10 +786,17 @@ def summarize_profile(workload, prof_dir, bench_json):
     copy_w = max(v for n, _, v in write if "copyBuffer" in n)
     ff, fw = cb / (copy_f * 1024.0), cb / (copy_w * 1024.0)
 
+    is_rows = _rows_launches(write, fw, cfg.T * cfg.k)
+
     def per_kernel(rows):
         agg = collections.defaultdict(list)
+        i = 0
         for n, dur, v in rows:
-            agg[_kernel_key(n, dur)].append((dur, v))
+            flag = False
+            if n.startswith("rank_scatter_kernel"):
+                flag = is_rows[i] if i < len(is_rows) else False
+                i += 1
+            agg[_kernel_key(n, flag)].append((dur, v))
         return agg
 
     KT, F, Wr, MO, GR = (per_kernel(x) for x in (kt, fetch, write, mops, grbm))
@@ -909,13 +924,50 @@ def summarize_runs(paths, out_name, command):
             cb = r["cpu_baseline"]
             L += ["", f"CPU oracle: {cb['value']:.0f} {cb['unit']} on {cb['cores']} cores ({cb.get('cpu_model')}, "
                   f"BLAS threads {cb.get('blas_threads')}); {cb['sample']}; stage seconds {cb.get('stage_s')}"]
-        for key in ("two_stage", "split_variants", "freebalance", "stale_split", "graph"):
-            if r.get(key):
-                L += ["", f"{key}: `{json.dumps(r[key])}`"]
+        L += _study_sections(r)
     out = os.path.join(ROOT, "profiles", out_name + ".md")
     with open(out, "w") as fh:
         fh.write("\n".join(L) + "\n")
     print("\n".join(L))
+
+
+def _study_sections(r):
+    """Markdown tables for the side studies of one result line (if present)."""
+    L = []
+    ts = r.get("two_stage")
+    if ts:
+        L += ["", "### Two-stage step (MoE_local beside the split and the remote permutation)", "",
+              f"Step {ts['ms_per_step']} ms against {r['ms_per_step']:.4f} ms in one stage.", "",
+              "| stage | ms |", "|---|---|"]
+        L += [f"| {k} | {v} |" for k, v in ts["stages_ms"].items()]
+        L += [f"| split + remote permutation (split stream) | {ts['side_work_ms']} |",
+              f"| exposed wait on the step's stream | {ts['exposed_ms']} |",
+              f"| hidden under MoE_local | {ts['hidden_ms']} |"]
+    sv = r.get("split_variants")
+    if sv:
+        L += ["", "### Split variants on the step's counts and placement", "",
+              "| variant | kernel µs | spatial balance |", "|---|---|---|"]
+        L += [f"| {k} | {v['us']} | {v['spatial']} |" for k, v in sv.items()]
+    fb = r.get("freebalance")
+    if fb:
+        L += ["", "### FreeBalance's swaps instead of replicas", "", "| quantity | value |", "|---|---|",
+              f"| step ms | {fb['ms_per_step']} |", f"| tokens/s | {fb['tokens_per_s']:.0f} |",
+              f"| spatial balance | {fb['spatial']} |", f"| swaps | {fb['swaps']} |",
+              f"| planner kernel µs | {fb['plan_us']} |", f"| gamma | {fb['gamma'][0]}/{fb['gamma'][1]} |",
+              f"| swap budget per rank | {fb['swaps_per_rank_budget']} |"]
+    st = r.get("stale_split")
+    if st:
+        L += ["", f"### Decision frequency over {st['steps']} step transitions", "",
+              "| split | mean spatial balance |", "|---|---|",
+              f"| fresh (Relief, every step) | {st['fresh']} |", f"| even | {st['even']} |",
+              f"| stale (previous step's shares) | {st['stale']} |", f"| no balancing | {st['static']} |", "",
+              f"Stale gives up {st['loss_vs_even']}x the fresh split's gain over the even split; Relief "
+              f"{st['relief_us']} µs per call, stale dealing {st['stale_us']} µs."]
+    g = r.get("graph")
+    if g:
+        L += ["", "### The step replayed from a HIP graph", "",
+              f"Eager {r['ms_per_step']:.4f} ms, replayed {g['ms_per_step']} ms ({g['tokens_per_s']:.0f} tokens/s)."]
+    return L
 
 
 def _kernel_sha():
