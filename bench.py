@@ -782,6 +782,8 @@ def summarize_profile(workload, prof_dir, bench_json):
     pm = os.path.join(prof_dir, "pmc_m", "p_counter_collection.csv")
     fetch, write = _dispatches(pf, "FETCH_SIZE"), _dispatches(pw, "WRITE_SIZE")
     mops, grbm = _dispatches(pm, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), _dispatches(pm, "GRBM_GUI_ACTIVE")
+    mbusy = _dispatches(pm, "SQ_VALU_MFMA_BUSY_CYCLES")
+    simds = 4 * int(res.get("compute_units", 256))
     copy_f = max(v for n, _, v in fetch if "copyBuffer" in n)
     copy_w = max(v for n, _, v in write if "copyBuffer" in n)
     ff, fw = cb / (copy_f * 1024.0), cb / (copy_w * 1024.0)
@@ -799,7 +801,7 @@ def summarize_profile(workload, prof_dir, bench_json):
             agg[_kernel_key(n, flag)].append((dur, v))
         return agg
 
-    KT, F, Wr, MO, GR = (per_kernel(x) for x in (kt, fetch, write, mops, grbm))
+    KT, F, Wr, MO, GR, MB = (per_kernel(x) for x in (kt, fetch, write, mops, grbm, mbusy))
     work = kernel_work(cfg, active)
     ffn_bytes = work.pop("_ffn_bytes")
     f, _ = algorithmic_work(cfg)
@@ -808,11 +810,14 @@ def summarize_profile(workload, prof_dir, bench_json):
              f"launch, each scaled by the factor that maps the counter on a plain {cb >> 20} MiB device copy to "
              f"the bytes it moves (FETCH x{ff:.4f}, WRITE x{fw:.4f}). MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 "
              "FLOP (executed, padding included) per launch, over the launch's duration in the counter run. "
+             "MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES per launch over the launch's SIMD cycles (GRBM_GUI_ACTIVE / 8 "
+             f"XCDs x {simds} SIMDs). "
              "Clock: GRBM_GUI_ACTIVE per launch / duration / 8 XCDs, for launches of 200 µs or more (counter "
-             "run; the profiler slows long kernels by a few %).", "",
+             "run; the profiler slows long kernels by a few %). Latency-bound kernels (under 2 µs of traffic "
+             "at the HBM peak, or no streamed operand) show their achieved rate for reference.", "",
              "| kernel | launches | avg µs | bound | algorithmic work / launch | achieved | of peak | "
-             "fetched GB | written GB | traffic / algorithmic bytes | executed MFMA TFLOP/s | clock GHz |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "fetched GB | written GB | traffic / algorithmic bytes | executed MFMA TFLOP/s | MFMA busy | clock GHz |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     gu_row = None
     for name in sorted(KT, key=lambda n: -sum(d for d, _ in KT[n])):
         if name.startswith(("at::native", "__amd")):
@@ -823,9 +828,13 @@ def summarize_profile(workload, prof_dir, bench_json):
         wb = sum(v for _, v in Wr.get(name, [])) / max(1, len(Wr.get(name, []))) * 1024 * fw
         mo = MO.get(name, [])
         mf = sum(v * 512 / d for d, v in mo) / max(1, len(mo)) / 1e12
-        gr = GR.get(name, [])
-        gr = [(d, v) for d, v in gr if d >= 200e-6]  # short launches: the counter is not a clock
+        gr_all = GR.get(name, [])
+        gr = [(d, v) for d, v in gr_all if d >= 200e-6]  # short launches: the counter is not a clock
         clk = sum(v / d for d, v in gr) / len(gr) / 8e9 if gr else None
+        mb = MB.get(name, [])
+        busy = None
+        if mb and len(mb) == len(gr_all) and any(v for _, v in gr_all):
+            busy = sum(b for _, b in mb) / (sum(v for _, v in gr_all) / 8.0 * simds)
         base, _, tail = name.partition(" (")
         key = next((w for w in work if base.startswith(w.partition(" (")[0]) and
                     (not tail or w.endswith("(" + tail))), None)
@@ -851,11 +860,16 @@ def summarize_profile(workload, prof_dir, bench_json):
             ach = peak = None
             alg_bytes = amt if unit == "B" else None
             txt, ach_s = (f"{amt / 1e6:.2f} MB" if alg_bytes else "-"), "-"
+            if alg_bytes:
+                ach, peak = alg_bytes / avg / 1e9, PEAK_HBM_GBS
+                ach_s = f"({ach:.0f} GB/s)"
         frac = f"{ach / peak:.3f}" if ach is not None else "-"
+        if bound == "latency" and ach is not None:
+            frac = f"({frac})"
         ratio = f"{(fb + wb) / alg_bytes:.2f}" if alg_bytes else "-"
         lines.append(f"| `{name}` | {len(durs)} | {avg * 1e6:.1f} | {bound} | {txt} | {ach_s} | {frac} | "
                      f"{fb / 1e9:.3f} | {wb / 1e9:.3f} | {ratio} | {mf:.0f} | "
-                     f"{'-' if clk is None else f'{clk:.2f}'} |")
+                     f"{'-' if not busy else f'{busy:.2f}'} | {'-' if clk is None else f'{clk:.2f}'} |")
         if name == GATE_UP_KERNEL:
             gu_row = (fb, wb)
     lines += ["", "Commands (repository root; each counter set in a run of its own):", "", "```",
