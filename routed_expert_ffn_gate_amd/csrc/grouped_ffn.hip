@@ -175,6 +175,115 @@ __global__ __launch_bounds__(256) void sched_kernel(const int32_t* __restrict__ 
   if (e == 0) s.eoff[E] = eoff[E];
 }
 
+// Inclusive prefix of v over the 256 threads of a workgroup (4 waves):
+// shuffles inside each wave, then the totals of the waves below.  part4 holds
+// 4 values; every thread of the workgroup must call it.
+__device__ __forceinline__ long long block_incl_scan_256(long long v, long long* part4) {
+  const int lane = threadIdx.x & (MOELB_WAVE - 1), w = threadIdx.x / MOELB_WAVE;
+#pragma unroll
+  for (int o = 1; o < MOELB_WAVE; o <<= 1) {
+    const long long y = __shfl_up(v, o, MOELB_WAVE);
+    if (lane >= o) v += y;
+  }
+  if (lane == MOELB_WAVE - 1) part4[w] = v;
+  __syncthreads();
+  long long add = 0;
+  for (int i = 0; i < w; ++i) add += part4[i];
+  __syncthreads();  // part4 is reused by the next call
+  return v + add;
+}
+
+// The schedule and the row map in one launch, for up to SCHED_FUSED_GROUPS
+// groups: every workgroup stages group_off in LDS and derives the expert
+// offsets and the groups' virtual bases itself (the same walk as
+// sched_kernel, from LDS), then maps its 256 virtual rows as rowmap_kernel
+// does; workgroup 0 also writes the tables the GEMMs read (expert offsets,
+// virtual bases, M tiles, one thread per tile).  The second launch and the
+// single workgroup's serial tile writes were most of the schedule's time.
+constexpr int SCHED_FUSED_GROUPS = 4096;
+
+__global__ __launch_bounds__(256) void sched_rowmap_kernel(const int32_t* __restrict__ group_off, int num_groups,
+                                                           int E, int G, int rank, int rows, int BM,
+                                                           const int32_t* __restrict__ gather, int gather_k,
+                                                           int rows_x, FfnSched s) {
+  __shared__ int goff[SCHED_FUSED_GROUPS + 1];
+  __shared__ int gvb[SCHED_FUSED_GROUPS];
+  __shared__ int eoff[MOELB_MAX_E + 1];
+  __shared__ int toff[MOELB_MAX_E + 1];
+  __shared__ long long part4[4];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  for (int i = tid; i <= num_groups; i += blockDim.x) goff[i] = group_off[i];
+  __syncthreads();
+  // rows of expert e's selected groups (clamped as in sched_kernel)
+  long long n = 0;
+  if (e < E)
+    for (int g = e; g < num_groups; g += E) {
+      const bool sel = rank < 0 || ((g / E) % G) == rank;
+      const int lo = min(max(goff[g], 0), rows);
+      const int hi = min(max(goff[g + 1], lo), rows);
+      if (sel) n += hi - lo;
+    }
+  const long long incl = block_incl_scan_256(e < E ? n : 0, part4);
+  const int lo_row = (int)min(incl - (e < E ? n : 0), (long long)rows);
+  const int hi_row = (int)min(incl, (long long)rows);
+  const int ntile = e < E ? (hi_row - lo_row + BM - 1) / BM : 0;
+  const long long tincl = block_incl_scan_256(ntile, part4);
+  if (e < E) {
+    eoff[e] = lo_row;
+    toff[e] = (int)(tincl - ntile);
+    // virtual bases of e's groups, in group order from e's first row
+    long long run = lo_row;
+    for (int g = e; g < num_groups; g += E) {
+      const bool sel = rank < 0 || ((g / E) % G) == rank;
+      const int lo = min(max(goff[g], 0), rows);
+      const int hi = min(max(goff[g + 1], lo), rows);
+      gvb[g] = (int)min(run, (long long)rows);
+      if (sel) run += hi - lo;
+    }
+  }
+  if (e == E - 1) {
+    eoff[E] = hi_row;
+    toff[E] = (int)tincl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= E; i += blockDim.x) s.eoff[i] = eoff[i];
+    for (int g = tid; g < num_groups; g += blockDim.x) s.gvb[g] = gvb[g];
+    if (tid == 0) *s.n_mtiles = toff[E];
+    // tile i belongs to the last expert with toff <= i (experts without
+    // tiles share their successor's offset and are skipped that way)
+    for (int i = tid; i < toff[E]; i += blockDim.x) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (toff[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      s.mt_e[i] = lo;
+      s.mt_v0[i] = eoff[lo] + (i - toff[lo]) * BM;
+    }
+  }
+  const int v = blockIdx.x * blockDim.x + tid;
+  if (v >= eoff[E]) return;
+  int lo = 0, hi = E - 1;  // eoff[0] = 0 <= v
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (eoff[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  const int ev = lo;
+  int jl = 0, jh = (num_groups - 1 - ev) / E;  // groups ev, ev+E, ... below num_groups
+  while (jl < jh) {
+    const int mid = (jl + jh + 1) >> 1;
+    if (gvb[ev + mid * E] <= v) jl = mid; else jh = mid - 1;
+  }
+  const int g = ev + jl * E;
+  const long long q64 = (long long)min(max(goff[g], 0), rows) + (v - gvb[g]);
+  const int q = (int)min(max(q64, 0ll), (long long)rows - 1);
+  s.rowmap[v] = q;
+  const int src = gather ? gather[q] / gather_k : q;
+  s.asrc[v] = (src >= 0 && src < rows_x) ? src : 0;
+}
+
 // Virtual -> physical row map, and the row of x each virtual row reads
 // (through the gather, when the rows come straight from the unpermuted hidden
 // states).  One thread per virtual row v < eoff[E]: its expert e is the last
@@ -1393,13 +1502,19 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
   const int BM = bf ? (skinny_tiles ? SK_BM : MF_BM) : SF_BM;
   const bool run_up = stages & MOELB_FFN_GATE_UP, run_down = stages & MOELB_FFN_DOWN;
   if (stages & MOELB_FFN_SCHEDULE) {
-    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank, rows,
-                       BM, sc);
-    MOELB_CHECK_LAUNCH();
-    if (rows > 0)
-      hipLaunchKernelGGL(rowmap_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, group_off, num_groups, E, rows,
-                         gather, gather_k, rows_x, sc);
-    MOELB_CHECK_LAUNCH();
+    if (num_groups <= SCHED_FUSED_GROUPS) {
+      hipLaunchKernelGGL(sched_rowmap_kernel, dim3(rows > 0 ? (rows + 255) / 256 : 1), dim3(256), 0, s, group_off,
+                         num_groups, E, G < 1 ? 1 : G, rank, rows, BM, gather, gather_k, rows_x, sc);
+      MOELB_CHECK_LAUNCH();
+    } else {
+      hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(256), 0, s, group_off, num_groups, E, G < 1 ? 1 : G, rank,
+                         rows, BM, sc);
+      MOELB_CHECK_LAUNCH();
+      if (rows > 0)
+        hipLaunchKernelGGL(rowmap_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, group_off, num_groups, E, rows,
+                           gather, gather_k, rows_x, sc);
+      MOELB_CHECK_LAUNCH();
+    }
   }
   const size_t mtiles = (size_t)(rows + BM - 1) / BM + E;
   if (bf) {

@@ -92,3 +92,44 @@ def test_ffn_rows_on_any_offsets(moelb, case):
         worst = max(worst, min(errs))
     log(f"  max rel err {worst:.3g}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ng", [4096, 4100])
+@pytest.mark.parametrize("rank", [-1, 3])
+def test_schedule_tables_many_groups(moelb, ng, rank):
+    """Up to 4096 groups the schedule and the row map run as one launch (each
+    workgroup derives the tables from group_off in LDS); past that as two.
+    Both give the model's tables, on offsets that mostly increase, with
+    some that decrease or leave [0, rows]."""
+    from routed_expert_ffn_gate_amd import moelb as M
+    e_, g_, rows = 4, 8, 3000
+    rng = np.random.default_rng(ng + rank)
+    steps = rng.integers(0, 2, ng + 1)
+    group_off = np.minimum(np.cumsum(steps) - steps[0], rows)
+    bad = rng.random(ng + 1) < 0.02
+    group_off[bad] += rng.integers(-40, 40, int(bad.sum()))  # local decreases and overlaps
+    group_off[-1] = rows + 25  # past the rows
+    group_off = group_off.astype(np.int32).tolist()
+    log(f"[ffn schedule] {ng} groups rank={rank}")
+    dev = torch.device("cuda")
+    x = torch.zeros((rows, D), dtype=torch.bfloat16, device=dev)
+    w13 = torch.zeros((e_, 2 * INTER, D), dtype=torch.bfloat16, device=dev)
+    w2 = torch.zeros((e_, D, INTER), dtype=torch.bfloat16, device=dev)
+    off = torch.tensor(group_off, dtype=torch.int32, device=dev)
+    nbytes = M.moelb_grouped_ffn_workspace_bytes(rows, ng, e_, D, INTER, M.MOELB_BF16)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=dev)
+    y = torch.zeros((rows, D), dtype=torch.bfloat16, device=dev)
+    M.moelb_grouped_ffn_stages(M.MOELB_FFN_SCHEDULE, x, rows, off, e_, w13, w2, ws, y, G=g_, rank=rank)
+    torch.cuda.synchronize()
+    eoff, gvb, tiles = F.schedule(np.array(group_off), ng, e_, g_, rank, rows, 256)
+    rm, src = F.rowmap(np.array(group_off), ng, e_, rows, eoff, gvb)
+    o = F.workspace_offsets(rows, ng, e_, INTER, 2)
+    w = ws.cpu().numpy()
+    i32 = lambda name, n: w[o[name]:o[name] + 4 * n].view(np.int32)  # noqa: E731
+    assert i32("eoff", e_ + 1).tolist() == eoff
+    assert i32("gvb", ng).tolist() == gvb
+    nt = int(i32("n_mtiles", 1)[0])
+    assert nt == len(tiles)
+    assert list(zip(i32("mt_e", nt).tolist(), i32("mt_v0", nt).tolist())) == tiles
+    assert np.array_equal(i32("rowmap", eoff[e_]), rm)
+    assert np.array_equal(i32("asrc", eoff[e_]), src)
