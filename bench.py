@@ -311,7 +311,7 @@ def time_stale_split(cfg, dev, stream, reps=20):
     return out
 
 
-def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20):
+def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20, packed=False):
     """The same step with FreeBalance's expert swaps in place of replication
     (budget: the N replica slots as swaps per rank; gamma = 1 / mean rank
     load): step time, the balance its placement leaves, the swap count and
@@ -323,7 +323,7 @@ def time_freebalance(cfg, tensors, K, W, stream, gather_rows=True, reps=20):
     dev = h.device
     fl = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
                   shared_inter=cfg.shared_inter, gather_rows=gather_rows, materialize_x=not gather_rows,
-                  balancer="freebalance", fb_budget=cfg.N)
+                  balancer="freebalance", fb_budget=cfg.N, packed_weights=packed)
     home_cur = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
     no_rep = torch.empty((cfg.G, 0), dtype=torch.int32, device=dev)
     fl.predict_placement(h_prev, wc, bc, home, home_cur)
@@ -374,10 +374,25 @@ def prepare_units(cfg, layer, dev):
     import torch
     from synth import workloads as W
     from routed_expert_ffn_gate_amd.layer import to_device
+    from routed_expert_ffn_gate_amd import moelb as M
     up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
+
+    def upw(a):
+        """Expert weights to the device, packed once for the FFN's weight
+        streams when the layer takes them so (model-load work, outside every
+        timed region)."""
+        t = up(a)
+        if not layer.ffn_opt:
+            return t
+        p = torch.empty_like(t)
+        M.moelb_pack_weights(t, p)
+        torch.cuda.synchronize()
+        del t
+        return p
+
     home = up(W.resident_home(cfg))
     shared = W.shared_weights(cfg)
-    S13, S2 = (up(shared[0]), up(shared[1])) if shared is not None else (None, None)
+    S13, S2 = (upw(shared[0]), upw(shared[1])) if shared is not None else (None, None)
     units = []
 
     def unit(name, li, W13, W2):
@@ -394,7 +409,7 @@ def prepare_units(cfg, layer, dev):
         hs = W.hidden_states(cfg, cfg.layers)
         for l in range(1, cfg.layers + 1):
             w13, w2 = W.expert_weights_stacked(cfg, l)
-            units.append(unit(f"layer{l}", W.layer_inputs(cfg, l, 0, hs=hs), up(w13), up(w2)))
+            units.append(unit(f"layer{l}", W.layer_inputs(cfg, l, 0, hs=hs), upw(w13), upw(w2)))
             del w13, w2
         prologue(units[0])
         for a, b in zip(units, units[1:]):
@@ -405,7 +420,7 @@ def prepare_units(cfg, layer, dev):
             b["sched"] = layer.sched_cur.clone()
     else:
         w13, w2 = W.expert_weights_stacked(cfg, 1)
-        W13, W2 = up(w13), up(w2)
+        W13, W2 = upw(w13), upw(w2)
         del w13, w2
         for st in range(cfg.steps):
             u = unit(f"step{st}" if cfg.steps > 1 else "layer1", W.layer_inputs(cfg, 1, st), W13, W2)
@@ -413,6 +428,12 @@ def prepare_units(cfg, layer, dev):
             units.append(u)
     torch.cuda.synchronize()
     return units, home, S13, S2
+
+
+def weights_packable(cfg):
+    """moelb_pack_weights' and the packed FFN's shape rules."""
+    return (cfg.dtype == "bf16" and cfg.d % 64 == 0 and cfg.inter % 64 == 0 and
+            (not cfg.shared_inter or cfg.shared_inter % 64 == 0))
 
 
 def run_unit(layer, u, home, S13, S2, **kw):
@@ -435,8 +456,9 @@ def rank_times(layer, u, home, S13, S2, stream, reps=5):
     for r in range(layer.G):
         for i in range(reps):
             ev.record(2 * i, stream)
-            M.moelb_grouped_ffn(x, layer.P, layer.group_off, layer.E, u["W13"], u["W2"], layer.ws_ffn, layer.y,
-                                G=layer.G, rank=r, stream=stream, **kw)
+            M.moelb_grouped_ffn_stages(M.MOELB_FFN_ALL | layer.ffn_opt, x, layer.P, layer.group_off, layer.E,
+                                       u["W13"], u["W2"], layer.ws_ffn, layer.y, G=layer.G, rank=r, stream=stream,
+                                       **kw)
             ev.record(2 * i + 1, stream)
         t.append(_median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
     ev.close()
@@ -464,6 +486,8 @@ def main():
     ap.add_argument("--studies", action="store_true",
                     help="also measure the two-stage step, the split variants and FreeBalance's swaps "
                          "(reported beside the headline; their kernels then share the profile)")
+    ap.add_argument("--weights", choices=["packed", "row-major"], default="packed",
+                    help="expert weights packed once by moelb_pack_weights (where the shape allows), or row-major")
     ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
                     help="gate/up GEMM reads h rows through the permutation, or a copied x_perm")
     args = ap.parse_args()
@@ -489,8 +513,10 @@ def main():
     cfg = W.config(args.workload)
     dev = torch.device("cuda:0")
     t0 = time.time()
+    packed = args.weights == "packed" and weights_packable(cfg)
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
-                     shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True)
+                     shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True,
+                     packed_weights=packed)
     units, home, S13, S2 = prepare_units(cfg, layer, dev)
     n_units = len(units)
     u0 = units[0]
@@ -602,7 +628,8 @@ def main():
         studies["split_variants"] = time_split_variants(layer, home, u0["replica"], stream)
         studies["freebalance"] = time_freebalance(cfg, (u0["h"], u0["h_prev"], u0["wc"], u0["bc"], u0["wn"],
                                                         u0["bn"], home, u0["W13"], u0["W2"], S13, S2), K,
-                                                  args.warmup, stream, gather_rows=args.rows == "gather")
+                                                  args.warmup, stream, gather_rows=args.rows == "gather",
+                                                  packed=packed)
         studies["stale_split"] = time_stale_split(cfg, dev, stream)
         studies["graph"] = time_graph(layer, tensors, K, args.warmup, stream)
 
@@ -624,7 +651,8 @@ def main():
     if os.path.exists(TRAFFIC_JSON):
         with open(TRAFFIC_JSON) as fh:
             tr = json.load(fh)
-        if tr.get("workload") == cfg.name and tr.get("kernel_source_sha") == _kernel_sha():
+        if (tr.get("workload") == cfg.name and tr.get("kernel_source_sha") == _kernel_sha() and
+                tr.get("ffn_weights", "row-major") == ("packed" if packed else "row-major")):
             traffic = tr.get("bytes_per_launch")
 
     result = {
@@ -643,7 +671,8 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "inter": cfg.inter, "shared_inter": cfg.shared_inter, "virtual_ranks": cfg.G,
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
-                   "layer_steps_cycled": n_units, "ffn_rows": args.rows},
+                   "layer_steps_cycled": n_units, "ffn_rows": args.rows,
+                   "ffn_weights": "packed" if packed else "row-major"},
         "ms_per_step_median": round(_median(step_ms), 4),
         "ms_per_step_marked_median": round(_median(marked_ms), 4),
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
@@ -890,6 +919,7 @@ def summarize_profile(workload, prof_dir, bench_json):
     print("\n".join(lines))
     if gu_row is not None:
         tr = {"workload": workload, "kernel": GATE_UP_KERNEL, "kernel_source_sha": _kernel_sha(),
+              "ffn_weights": res["config"].get("ffn_weights", "row-major"),
               "fetch_bytes_per_launch": gu_row[0], "write_bytes_per_launch": gu_row[1],
               "fetch_factor": ff, "write_factor": fw, "copy_bytes": cb,
               "bytes_per_launch": gu_row[0] + gu_row[1],

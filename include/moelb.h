@@ -16,8 +16,9 @@
  * (moelb_split_schedule, moelb_split_scheduled), split variants for
  * comparison (moelb_split_variant), an earlier step's split dealt again
  * (moelb_split_stale), FreeBalance's expert-swap planner (moelb_plan_swaps),
- * the permutation in two phases (moelb_permute_local, moelb_permute_remote)
- * and the FFN in stages (moelb_grouped_ffn_stages).
+ * the permutation in two phases (moelb_permute_local, moelb_permute_remote),
+ * the FFN in stages (moelb_grouped_ffn_stages) and expert weights packed once
+ * for the FFN's weight streams (moelb_pack_weights).
  *
  * Conventions for every entry point:
  *  - Plain C ABI.  Every pointer argument is DEVICE memory owned by the caller
@@ -398,19 +399,41 @@ int moelb_grouped_ffn(const void* x, int rows_x, int rows, const int32_t* group_
  * moelb_grouped_ffn runs MOELB_FFN_ALL.  A stage reads what the earlier
  * stages left in ws, so the calls of one FFN take the same arguments and the
  * same ws, in stage order on one stream.  Same requirements and errors as
- * moelb_grouped_ffn; stages outside [1, MOELB_FFN_ALL] return MOELB_EINVAL.
+ * moelb_grouped_ffn; stages outside [1, MOELB_FFN_ALL] (after removing the
+ * MOELB_FFN_PACKED_WEIGHTS option) return MOELB_EINVAL.
  */
 enum moelb_ffn_stage {
   MOELB_FFN_SCHEDULE = 1,
   MOELB_FFN_GATE_UP = 2,
   MOELB_FFN_DOWN = 4,
-  MOELB_FFN_ALL = 7
+  MOELB_FFN_ALL = 7,
+  /* option, ORed with the stages: w13 and w2 are in the packed layout of
+   * moelb_pack_weights (w13 packed with rows = 2*inter, K = d; w2 with rows =
+   * d, K = inter).  Requires bf16, d % 64 == 0, inter % 64 == 0; outputs are
+   * identical to the row-major call's. */
+  MOELB_FFN_PACKED_WEIGHTS = 8
 };
 int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, int rows,
                              const int32_t* group_off, int num_groups, int E, int G, int rank,
                              const int32_t* gather, int gather_k, int d, int inter, int dtype,
                              const void* w13, const void* w2, void* ws, size_t ws_bytes,
                              void* y, void* stream);
+
+/*
+ * Expert weights in the packed layout the grouped FFN reads with
+ * MOELB_FFN_PACKED_WEIGHTS (a layout of this library, not of the pages): the
+ * 8 rows of a row block and one 64-wide K step are one contiguous KiB, so
+ * each 64-lane DMA instruction of the GEMMs reads one KiB of DRAM instead of
+ * 128-byte pieces of 8 rows.  For callers that load expert weights once and
+ * run many steps (weights streamed by decode batches gain most).
+ *  w       [E][rows][K] bf16, row-major
+ *  packed  [E][rows/8][K/64][8][64] bf16 out: element (e, r, k) at
+ *          ((e*rows/8 + r/8)*(K/64) + k/64)*512 + (r%8)*64 + k%64
+ * w and packed are device buffers of E*rows*K elements, 16-byte aligned,
+ * not overlapping.  Requires bf16, rows % 8 == 0, K % 64 == 0; otherwise
+ * MOELB_EINVAL before any launch.
+ */
+int moelb_pack_weights(const void* w, int E, int rows, int K, int dtype, void* packed, void* stream);
 
 /*
  * Top-k weighted combine (FreeBalance section 2.1: MoE(h) = sum_i W_i

@@ -58,6 +58,7 @@ struct FfnSched {
   int32_t* rowmap;    // [rows] physical row of each virtual row
   int32_t* asrc;      // [rows] row of x the gate/up GEMM reads for each virtual row
   void* amid;         // [rows][inter] SwiGLU activations, virtual row order
+  int wpacked;        // W13 and W2 in the packed layout (moelb_pack_weights)
 };
 
 inline size_t max_mtiles(int rows, int E) { return (size_t)(rows + SCHED_MIN_BM - 1) / SCHED_MIN_BM + E; }
@@ -565,6 +566,18 @@ constexpr size_t DL_LDS_BYTES = DL_LDS_MAIN > DL_LDS_EPI ? DL_LDS_MAIN : DL_LDS_
 // conflict-free fragment reads whether the LDS serves 8 or 16 lanes per pass.
 __device__ __forceinline__ int dl_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row << 2)) & 7); }
 
+// Weight addressing.  Byte offset of 16-byte chunk `chunk` (0..7) of the
+// first 64-wide K step of an expert's weight row `row` (K elements per row),
+// in the row-major layout or the packed one ([row/8][K/64][8][64]: the 8 rows
+// of a block and one K step are one contiguous KiB, so a DMA instruction that
+// loads 8 rows x 128 bytes reads one KiB of DRAM instead of 8 pieces 4 KiB
+// or more apart).  One K step moves every row's data by w_step elements.
+__device__ __forceinline__ uint32_t w_off(int row, int K, int chunk, bool packed) {
+  return packed ? ((uint32_t)(row >> 3) * (uint32_t)K * 8u + (uint32_t)(row & 7) * 64u + (uint32_t)chunk * 8u) * 2u
+                : ((uint32_t)row * (uint32_t)K + (uint32_t)chunk * 8u) * 2u;
+}
+__device__ __forceinline__ int w_step(bool packed) { return packed ? 512 : DL_BK; }
+
 // 16 bytes per lane, global -> LDS: byte offset voff from the wave-uniform
 // base sbase; lane i lands at LDS byte address m0 + 16 i.
 // M0 is a reserved register, so the compiler warns that it does not preserve
@@ -605,6 +618,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
   // slot (lane & 7) <- global chunk dl_slot(row, slot); byte offsets
   const uint16_t* abase = MODE == 0 ? x : static_cast<const uint16_t*>(s.amid);
   const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
+  const int wstep = w_step(s.wpacked);  // elements one K step moves a weight row
   uint32_t aoff[8], boff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -616,12 +630,12 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
       aoff[j] = ((uint32_t)min(max(s.asrc[v], 0), rows_x - 1) * (uint32_t)d + chunk * 8) * 2u;
       int c = nt * 128 + (r & 127);
       c = c < inter ? c : 0;
-      boff[j] = ((uint32_t)((r < 128) ? c : inter + c) * (uint32_t)d + chunk * 8) * 2u;
+      boff[j] = w_off((r < 128) ? c : inter + c, d, chunk, s.wpacked);
     } else {
       aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;
       int c = nt * 256 + r;
       c = c < d ? c : 0;
-      boff[j] = ((uint32_t)c * (uint32_t)inter + chunk * 8) * 2u;
+      boff[j] = w_off(c, inter, chunk, s.wpacked);
     }
   }
 
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_mfma_dma_kernel(const uint16_t
 #define DL_COPY(J, JJ)                                                                                 \
   {                                                                                                    \
     const int j_ = (J);                                                                                \
-    const uint16_t* base_ = ((j_ & 1) ? bbase : abase) + (size_t)(j_ >> 1) * DL_BK;                    \
+    const uint16_t* base_ = ((j_ & 1) ? bbase : abase) + (size_t)(j_ >> 1) * ((j_ & 1) ? wstep : DL_BK); \
     dl_copy16((j_ & 1) ? boff[JJ] : aoff[JJ], base_,                                                   \
               lds_u32 + (uint32_t)(((j_ % DL_SLOTS) * DL_HALF + (wave_s * 8 + (JJ)) * 8 * DL_BK) * 2)); \
   }
@@ -912,6 +926,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
   DlTile nxt = ntiles > 1 ? dl_tile<MODE>(dl_tile_id(1, total), n_mtiles, ntn, s) : cur;
   int src[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* bbase;
+  const int wstep = w_step(s.wpacked);  // elements one K step moves a weight row
   uint32_t aoff[8], boff[8];
 #define DL_OFFSETS(C)                                                                                  \
   {                                                                                                    \
@@ -923,14 +938,14 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
         aoff[j] = ((uint32_t)src[j] * (uint32_t)d + chunk * 8) * 2u;                                   \
         int col = (C).nt * 128 + (r & 127);                                                            \
         col = col < inter ? col : 0;                                                                   \
-        boff[j] = ((uint32_t)((r < 128) ? col : inter + col) * (uint32_t)d + chunk * 8) * 2u;          \
+        boff[j] = w_off((r < 128) ? col : inter + col, d, chunk, s.wpacked);                           \
       } else {                                                                                         \
         int v = (C).v0 + r;                                                                            \
         v = v < (C).vend ? v : (C).v0;                                                                 \
         aoff[j] = ((uint32_t)v * (uint32_t)inter + chunk * 8) * 2u;                                    \
         int col = (C).nt * 256 + r;                                                                    \
         col = col < d ? col : 0;                                                                       \
-        boff[j] = ((uint32_t)col * (uint32_t)inter + chunk * 8) * 2u;                                  \
+        boff[j] = w_off(col, inter, chunk, s.wpacked);                                                 \
       }                                                                                                \
     }                                                                                                  \
   }
@@ -951,7 +966,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
   // of a K step that is KK steps into its tile
 #define DL_COPY(SLOT, KK, ISB, JJ)                                                                     \
   {                                                                                                    \
-    const uint16_t* base_ = ((ISB) ? bbase : abase) + (size_t)(KK) * DL_BK;                            \
+    const uint16_t* base_ = ((ISB) ? bbase : abase) + (size_t)(KK) * ((ISB) ? wstep : DL_BK);          \
     dl_copy16((ISB) ? boff[JJ] : aoff[JJ], base_,                                                      \
               lds_u32 + (uint32_t)(((SLOT) * DL_HALF + (wave_s * 8 + (JJ)) * 8 * DL_BK) * 2));         \
   }
@@ -1243,6 +1258,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* 
   // dl_slot(row, slot); byte offsets from the operand bases
   const uint16_t* abase = MODE == 0 ? x : static_cast<const uint16_t*>(s.amid);
   const uint16_t* bbase = w + (MODE == 0 ? (size_t)e * 2 * inter * d : (size_t)e * d * inter);
+  const int wstep = w_step(s.wpacked);  // elements one K step moves a weight row
   uint32_t aoff[2], boff[8];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1264,7 +1280,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* 
       const int c = nt * 256 + r;
       brow = (uint32_t)(c < d ? c : 0);
     }
-    boff[j] = (brow * (uint32_t)K + dl_slot(r, lane & 7) * 8) * 2u;
+    boff[j] = w_off((int)brow, K, dl_slot(r, lane & 7), s.wpacked);
   }
   // issue K step KTI into its ring stage (SK_VPS instructions per wave)
   auto issue = [&](int kti) {
@@ -1274,7 +1290,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* 
     for (int j = 0; j < 2; ++j) dl_copy16(aoff[j], abase + ko, st + (uint32_t)((wave_s * 2 + j) * 8 * DL_BK) * 2u);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      dl_copy16(boff[j], bbase + ko, st + (uint32_t)((SK_BM + (wave_s * 8 + j) * 8) * DL_BK) * 2u);
+      dl_copy16(boff[j], bbase + (size_t)kti * wstep, st + (uint32_t)((SK_BM + (wave_s * 8 + j) * 8) * DL_BK) * 2u);
   };
 
   // fragment rows: A blocks mi = 0, 1 (rows 32 mi + lane % 32); B blocks ni:
@@ -1478,9 +1494,13 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
                                         int num_groups, int E, int G, int rank, const int32_t* gather, int gather_k,
                                         int d, int inter, int dtype, const void* w13, const void* w2, void* ws,
                                         size_t ws_bytes, void* y, void* stream) {
+  const bool packed = stages & MOELB_FFN_PACKED_WEIGHTS;
+  stages &= ~MOELB_FFN_PACKED_WEIGHTS;
   if (stages < 1 || stages > MOELB_FFN_ALL) return MOELB_EINVAL;
   if (rows < 0 || rows_x < 0 || num_groups < 1 || num_groups > 32768 || E < 1 || E > MOELB_MAX_E) return MOELB_EINVAL;
   if (d <= 0 || d % 8 != 0 || inter <= 0 || inter % 8 != 0 || !moelb_dtype_ok(dtype)) return MOELB_EINVAL;
+  // packed weights: the bf16 GEMMs that stream whole 64-wide K steps read them
+  if (packed && (dtype != MOELB_BF16 || d % 64 != 0 || inter % 64 != 0)) return MOELB_EINVAL;
   if (rank >= 0 && (G < 1 || rank >= G || num_groups % E != 0)) return MOELB_EINVAL;
   if (gather && gather_k < 1) return MOELB_EINVAL;
   if (!group_off || !w13 || !w2 || (rows > 0 && (!x || !y || rows_x < 1))) return MOELB_EINVAL;
@@ -1496,6 +1516,7 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
   if (!ws || ws_bytes < need) return MOELB_EWORKSPACE;
   FfnSched sc;
   sched_layout(rows, num_groups, E, inter, dtype, &sc, static_cast<char*>(ws));
+  sc.wpacked = packed ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == MOELB_BF16;
   const bool skinny_tiles = bf && skinny_rows(rows, num_groups, E) && d % DL_BK == 0 && inter % DL_BK == 0;
@@ -1592,6 +1613,41 @@ extern "C" int moelb_grouped_ffn_stages(int stages, const void* x, int rows_x, i
       MOELB_CHECK_LAUNCH();
     }
   }
+  return MOELB_OK;
+}
+
+// ---------------------------------------------------------------- packed weights
+
+// One thread per 16-byte chunk of w ([E][rows][K] bf16, K/8 chunks per row):
+// chunk c of row (e, r) goes to chunk ((e*rows/8 + r/8)*(K/64) + c/8)*64 +
+// (r%8)*8 + c%8 of the packed array.  Reads are coalesced; each group of 8
+// threads writes 128 contiguous bytes.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ w, long long nchunks, int rows,
+                                                           int K, uint4* __restrict__ packed) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nchunks) return;
+  const int cpr = K / 8;
+  const long long row_all = i / cpr;
+  const int c = (int)(i - row_all * cpr);
+  const long long e = row_all / rows;
+  const int r = (int)(row_all - e * rows);
+  const long long dst = ((e * (rows / 8) + r / 8) * (K / 64) + c / 8) * 64 + (r % 8) * 8 + (c % 8);
+  packed[dst] = w[i];
+}
+
+extern "C" int moelb_pack_weights(const void* w, int E, int rows, int K, int dtype, void* packed, void* stream) {
+  if (E < 1 || rows < 8 || rows % 8 != 0 || K < 64 || K % 64 != 0 || dtype != MOELB_BF16) return MOELB_EINVAL;
+  if (!w || !packed) return MOELB_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(packed)) & 15) return MOELB_EINVAL;
+  const unsigned long long bytes = (unsigned long long)E * rows * K * 2ull;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(packed);
+  if (a < b + bytes && b < a + bytes) return MOELB_EINVAL;  // overlapping
+  const long long nchunks = (long long)(bytes / 16);
+  const long long blocks = (nchunks + 255) / 256;
+  if (blocks > 0x7fffffffll) return MOELB_EINVAL;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(w), nchunks, rows, K, static_cast<uint4*>(packed));
+  MOELB_CHECK_LAUNCH();
   return MOELB_OK;
 }
 

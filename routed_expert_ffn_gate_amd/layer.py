@@ -106,12 +106,15 @@ class MoELayer:
 
     def __init__(self, T, d, E, k, inter, G, N, L, dtype, device="cuda", shared_inter=0, passes=12,
                  gather_rows=True, materialize_x=False, balancer="libra", fb_tau=0, fb_gamma=None,
-                 fb_budget=None):
+                 fb_budget=None, packed_weights=False):
         """balancer "libra": replication plan (N slots, L locality imports)
         and the per-step split; "freebalance": expert swaps instead (no
         replicas; at most fb_budget swaps per rank, default N; threshold
-        fb_tau; gamma = fb_gamma (num, den), default 1 / the mean rank load)."""
+        fb_tau; gamma = fb_gamma (num, den), default 1 / the mean rank load).
+        packed_weights: the expert (and shared) weights passed to the steps
+        are in moelb_pack_weights' layout."""
         self.T, self.d, self.E, self.k, self.inter = T, d, E, k, inter
+        self.ffn_opt = M.MOELB_FFN_PACKED_WEIGHTS if packed_weights else 0
         self.G, self.N, self.L, self.passes = G, N, L, passes
         if balancer not in ("libra", "freebalance"):
             raise ValueError(balancer)
@@ -228,12 +231,18 @@ class MoELayer:
         if self.gather_rows:
             kw.update(gather=self.perm, gather_k=self.k)
         if mark is None:
-            M.moelb_grouped_ffn(x, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, **kw)
+            M.moelb_grouped_ffn_stages(M.MOELB_FFN_ALL | self.ffn_opt, x, self.P, self.group_off, self.E, w13, w2,
+                                       self.ws_ffn, self.y, **kw)
             return
         for i, stage in enumerate((M.MOELB_FFN_SCHEDULE, M.MOELB_FFN_GATE_UP, M.MOELB_FFN_DOWN)):
             mark(8 + i)
-            M.moelb_grouped_ffn_stages(stage, x, self.P, self.group_off, self.E, w13, w2, self.ws_ffn, self.y, **kw)
+            M.moelb_grouped_ffn_stages(stage | self.ffn_opt, x, self.P, self.group_off, self.E, w13, w2,
+                                       self.ws_ffn, self.y, **kw)
         mark(11)
+
+    def _shared_ffn(self, h, shared_w13, shared_w2, stream):
+        M.moelb_grouped_ffn_stages(M.MOELB_FFN_ALL | self.ffn_opt, h, self.T, self.shared_off, 1, shared_w13,
+                                   shared_w2, self.ws_shared, self.shared, stream=stream)
 
     def _out(self):
         return StepOut(self.idx, self.wts, self.gap, self.idx_next, self.counts, self.counts_next, self.replica_next,
@@ -279,8 +288,7 @@ class MoELayer:
         mark(4)
         self._ffn(h, w13, w2, mark if ev is not None else None, stream=s0)
         if self.shared is not None:
-            M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
-                                stream=s0)
+            self._shared_ffn(h, shared_w13, shared_w2, s0)
         mark(5)
         M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=s0)
         mark(6)
@@ -310,12 +318,13 @@ class MoELayer:
                 ev.record(ev_base + i, st if st is not None else s0)
 
         def ffn(off):
+            all_ = M.MOELB_FFN_ALL | self.ffn_opt
             if self.gather_rows:
-                M.moelb_grouped_ffn(h, self.P, off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                    gather=self.perm, gather_k=self.k, stream=s0)
+                M.moelb_grouped_ffn_stages(all_, h, self.P, off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
+                                           gather=self.perm, gather_k=self.k, stream=s0)
             else:
-                M.moelb_grouped_ffn(self.x_perm, self.P, off, self.E, w13, w2, self.ws_ffn, self.y, G=self.G,
-                                    stream=s0)
+                M.moelb_grouped_ffn_stages(all_, self.x_perm, self.P, off, self.E, w13, w2, self.ws_ffn, self.y,
+                                           G=self.G, stream=s0)
 
         mark(0)
         M.moelb_gate_topk(h, w_cur, b_cur, w_next, b_next, self.idx, self.wts, self.gap, self.idx_next, stream=s0)
@@ -353,8 +362,7 @@ class MoELayer:
         mark(5)
         ffn(self.group_off[GE:])  # MoE_remote
         if self.shared is not None:
-            M.moelb_grouped_ffn(h, self.T, self.shared_off, 1, shared_w13, shared_w2, self.ws_shared, self.shared,
-                                stream=s0)
+            self._shared_ffn(h, shared_w13, shared_w2, s0)
         mark(6)
         M.moelb_combine(self.y, self.pos, self.wts, self.out, shared=self.shared, stream=s0)
         mark(7)

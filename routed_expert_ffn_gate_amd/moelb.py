@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmoelb.so")
 MOELB_OK, MOELB_EINVAL, MOELB_ELAUNCH, MOELB_EWORKSPACE = 0, 1, 2, 3
 MOELB_F32, MOELB_BF16 = 0, 1
 MOELB_FFN_SCHEDULE, MOELB_FFN_GATE_UP, MOELB_FFN_DOWN, MOELB_FFN_ALL = 1, 2, 4, 7
+MOELB_FFN_PACKED_WEIGHTS = 8
 
 # name -> (restype, argtypes)
 _P, _I, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -45,6 +46,7 @@ SIGNATURES = {
     "moelb_grouped_ffn_stages": (_I, [_I, _P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P,
                                       _P]),
     "moelb_combine": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moelb_pack_weights": (_I, [_P, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -225,6 +227,14 @@ def moelb_permute_remote(h, idx, G, home, replica, host_count, ws, group_off, pe
     _check(lib().moelb_permute_remote(_p(h), _p(idx), T, d, k, E, G, N, dtype, _p(home), _p(replica),
                                       _p(host_count), _p(ws), ws.numel() * ws.element_size(), _p(group_off),
                                       _p(perm), _p(pos), _p(x_perm), _stream(stream)), "moelb_permute_remote")
+
+
+def moelb_pack_weights(w, packed, stream=None):
+    """w [E, rows, K] (or [rows, K]: one expert) bf16 -> packed (same shape and
+    dtype, the packed layout)."""
+    E, rows, K = (1, *w.shape) if w.dim() == 2 else w.shape
+    _check(lib().moelb_pack_weights(_p(w), E, rows, K, dtype_code(w), _p(packed), _stream(stream)),
+           "moelb_pack_weights")
 
 
 def moelb_grouped_ffn_workspace_bytes(rows, num_groups, E, d, inter, dtype) -> int:

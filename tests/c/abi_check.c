@@ -54,6 +54,15 @@ int main(void) {
          MOELB_EINVAL);
   EXPECT(moelb_grouped_ffn(P, 0, 8, P, 8, 2, 2, 0, NULL, 1, 8, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
          MOELB_EINVAL);
+  /* packed weights: bf16 with d and inter multiples of 64 only */
+  EXPECT(moelb_grouped_ffn_stages(MOELB_FFN_ALL | MOELB_FFN_PACKED_WEIGHTS, P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 8, 64,
+                                  MOELB_BF16, P, P, P, 1u << 30, P, NULL) == MOELB_EINVAL);
+  EXPECT(moelb_grouped_ffn_stages(MOELB_FFN_ALL | MOELB_FFN_PACKED_WEIGHTS, P, 8, 8, P, 8, 2, 2, 0, NULL, 1, 64, 64,
+                                  MOELB_F32, P, P, P, 1u << 30, P, NULL) == MOELB_EINVAL);
+  EXPECT(moelb_pack_weights(P, 2, 12, 64, MOELB_BF16, (void*)(1ull << 30), NULL) == MOELB_EINVAL);
+  EXPECT(moelb_pack_weights(P, 2, 16, 96, MOELB_BF16, (void*)(1ull << 30), NULL) == MOELB_EINVAL);
+  EXPECT(moelb_pack_weights(P, 2, 16, 64, MOELB_F32, (void*)(1ull << 30), NULL) == MOELB_EINVAL);
+  EXPECT(moelb_pack_weights(P, 2, 16, 64, MOELB_BF16, (char*)P + 64, NULL) == MOELB_EINVAL);
   /* operands whose byte offsets would not fit 32 bits */
   EXPECT(moelb_grouped_ffn(P, 1 << 20, 8, P, 8, 2, 2, 0, NULL, 1, 4096, 8, MOELB_BF16, P, P, P, 1u << 30, P, NULL) ==
          MOELB_EINVAL);

@@ -45,7 +45,7 @@ class LayerRun:
 
 def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool = True,
               materialize_x: bool = True, hs=None, weights=None, two_stage: bool = False,
-              balancer: str = "libra") -> LayerRun:
+              balancer: str = "libra", packed_weights: bool = False) -> LayerRun:
     from routed_expert_ffn_gate_amd.layer import MoELayer, to_device, to_host
     dev = torch.device("cuda")
     li = W.layer_inputs(cfg, layer, step, hs=hs)
@@ -60,8 +60,19 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
     S13 = S2 = None
     if sh is not None:
         S13, S2 = d(sh[0]), d(sh[1])
+    if packed_weights:
+        from routed_expert_ffn_gate_amd import moelb as M
+
+        def pack(t):
+            p_ = torch.empty_like(t)
+            M.moelb_pack_weights(t, p_)
+            return p_
+        W13, W2 = pack(W13), pack(W2)
+        if sh is not None:
+            S13, S2 = pack(S13), pack(S2)
     L = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype, shared_inter=cfg.shared_inter,
-                 gather_rows=gather_rows, materialize_x=materialize_x, balancer=balancer)
+                 gather_rows=gather_rows, materialize_x=materialize_x, balancer=balancer,
+                 packed_weights=packed_weights)
     home_cur = None
     if balancer == "freebalance":
         replica_cur = torch.empty((cfg.G, 0), dtype=torch.int32, device=dev)

@@ -85,6 +85,18 @@ def test_invalid_arguments_rejected_before_launch(lib):
         assert lib.moelb_grouped_ffn_stages(stages, P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 1 << 30, P,
                                             N) == 1
     assert lib.moelb_grouped_ffn_stages(2, P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 8, 1, P, P, P, 16, P, N) == 3
+    # packed weights: only bf16 with d and inter multiples of 64
+    assert lib.moelb_grouped_ffn_stages(7 | 8, P, 8, 8, P, 8, 2, 2, 0, N, 1, 8, 64, 1, P, P, P, 1 << 30, P, N) == 1
+    assert lib.moelb_grouped_ffn_stages(7 | 8, P, 8, 8, P, 8, 2, 2, 0, N, 1, 64, 64, 0, P, P, P, 1 << 30, P, N) == 1
+    assert lib.moelb_grouped_ffn_stages(16, P, 8, 8, P, 8, 2, 2, 0, N, 1, 64, 64, 1, P, P, P, 1 << 30, P, N) == 1
+    # pack: rows % 8, K % 64, dtype, null, misaligned, overlapping
+    Q = ctypes.c_void_p(1 << 30)
+    assert lib.moelb_pack_weights(P, 2, 12, 64, 1, Q, N) == 1
+    assert lib.moelb_pack_weights(P, 2, 16, 96, 1, Q, N) == 1
+    assert lib.moelb_pack_weights(P, 2, 16, 64, 0, Q, N) == 1
+    assert lib.moelb_pack_weights(N, 2, 16, 64, 1, Q, N) == 1
+    assert lib.moelb_pack_weights(P, 2, 16, 64, 1, ctypes.c_void_p((1 << 30) + 8), N) == 1
+    assert lib.moelb_pack_weights(P, 2, 16, 64, 1, ctypes.c_void_p(P.value + 64), N) == 1
     # combine: k out of range; misaligned output
     assert lib.moelb_combine(P, 8, P, P, 4, 17, 8, 1, N, P, N) == 1
     assert lib.moelb_combine(P, 8, P, P, 4, 2, 8, 1, N, ctypes.c_void_p(18), N) == 1

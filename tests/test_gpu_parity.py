@@ -679,3 +679,42 @@ def test_topk_exact_at_large_logits(moelb, E, k):
     assert np.array_equal(gi[sep], idx_o[sep])
     assert np.max(np.abs(gg[keep] - gap_o[keep])) <= 1e-4
     assert np.max(np.abs(gw[keep] - w_o[keep]) / w_o[keep]) <= 1e-4
+
+
+def test_pack_weights_layout(moelb):
+    """moelb_pack_weights against the layout written out with numpy:
+    [E][rows][K] -> [E][rows/8][K/64][8][64], bit for bit."""
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(3)
+    for E, rows, K in [(3, 16, 64), (2, 24, 192), (5, 1536, 2048)]:
+        w = rng.integers(-32768, 32768, (E, rows, K), dtype=np.int64).astype(np.int16)
+        wt = torch.from_numpy(w).to(dev).view(torch.bfloat16)
+        out = torch.empty_like(wt)
+        M.moelb_pack_weights(wt, out)
+        torch.cuda.synchronize()
+        ref = w.reshape(E, rows // 8, 8, K // 64, 64).transpose(0, 1, 3, 2, 4).reshape(E, rows, K)
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), (E, rows, K)
+
+
+@pytest.mark.parametrize("changes", [
+    dict(T=256, d=512, E=32, k=4, inter=256, G=4, N=2, L=1),    # 64-row decode tiles
+    dict(T=2048, d=512, E=8, k=2, inter=256, G=4, N=2, L=1),    # persistent GEMMs
+    dict(T=1024, d=128, E=8, k=2, inter=128, G=4, N=2, L=1),    # K/64 = 2: one workgroup per tile
+])
+def test_packed_weights_equal_row_major(moelb, changes):
+    """The layer step with weights packed by moelb_pack_weights: every output
+    equal to the row-major step's, bit for bit, and the oracle's."""
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, **changes)
+    a = run_layer(cfg)
+    b = _full_check(cfg, tokens=sample_tokens(cfg.T, 32), packed_weights=True)
+    for key in ["group_off", "perm", "pos", "y", "out"]:
+        assert np.array_equal(a.out[key], b.out[key]), key
+
+
+def test_packed_weights_shared_expert(moelb):
+    cfg = W.scaled(W.config("c4_glm45_prefill"), T=1024)
+    a = run_layer(cfg)
+    b = run_layer(cfg, packed_weights=True)
+    for key in ["y", "shared", "out"]:
+        assert np.array_equal(a.out[key], b.out[key]), key
