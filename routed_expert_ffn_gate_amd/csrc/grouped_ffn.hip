@@ -1223,7 +1223,10 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
 // five-stage ring, twice the tiles for a smaller last round (gate/up 0.135
 // against 0.125 ms); a four-stage ring (the same); a two-stage ring with two
 // workgroups per CU (the same).  The depth of the stream is not what bounds
-// these GEMMs at about 4.2 TB/s.
+// these GEMMs at about 4.2 TB/s; the weights' row-major read pattern was
+// (packed weights: 4.5 TB/s, gate/up 0.125 -> 0.114 ms).  128-column tiles
+// with packed weights, for a better-balanced last round: still slower (0.120
+// to 0.124 ms).
 constexpr int SK_BM = 64;
 constexpr int SK_BN = 256;
 constexpr int SK_STAGE = (SK_BM + SK_BN) * DL_BK;  // elements per stage
