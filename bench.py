@@ -763,6 +763,11 @@ def _rows_launches(write_rows, fw, pairs):
             for n, _, v in write_rows if n.startswith("rank_scatter_kernel")]
 
 
+# kernels of the bench's input preparation (weights packed once, as at model
+# load), listed apart in the profile table
+SETUP_KERNELS = ("pack_weights_kernel",)
+
+
 def _kernel_key(name, rows_flag):
     if name.startswith("rank_scatter_kernel"):
         return name + (" (rows)" if rows_flag else " (indices)")
@@ -865,6 +870,14 @@ def summarize_profile(workload, prof_dir, bench_json):
         if mb and len(mb) == len(gr_all) and any(v for _, v in gr_all):
             busy = sum(b for _, b in mb) / (sum(v for _, v in gr_all) / 8.0 * simds)
         base, _, tail = name.partition(" (")
+        if base.startswith(SETUP_KERNELS):
+            # run once while the bench prepares its inputs, not in the step:
+            # its measured traffic rate
+            rate = (fb + wb) / avg / 1e9
+            lines.append(f"| `{name}` | {len(durs)} | {avg * 1e6:.1f} | setup (not in the step) | - | "
+                         f"({rate:.0f} GB/s moved) | ({rate / PEAK_HBM_GBS:.3f}) | {fb / 1e9:.3f} | {wb / 1e9:.3f} "
+                         f"| - | 0 | - | {'-' if clk is None else f'{clk:.2f}'} |")
+            continue
         key = next((w for w in work if base.startswith(w.partition(" (")[0]) and
                     (not tail or w.endswith("(" + tail))), None)
         bound, amt, unit = work[key] if key else ("latency", None, "")
