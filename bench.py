@@ -914,17 +914,17 @@ def summarize_profile(workload, prof_dir, bench_json):
                      f"{'-' if not busy else f'{busy:.2f}'} | {'-' if clk is None else f'{clk:.2f}'} |")
         if name == GATE_UP_KERNEL:
             gu_row = (fb, wb)
-    lines += ["", "Commands (repository root; each counter set in a run of its own):", "", "```",
-              "export TMPDIR=/tmp",
+    lines += ["", "Commands (repository root; each counter set in a run of its own; any output directory):", "",
+              "```",
+              "export TMPDIR=/tmp; mkdir -p prof",
               "B='python -u bench.py --workload %s --steps 2 --warmup 0 --no-cpu-baseline --no-rank-times "
               "--copy-bytes %d'" % (workload, cb),
-              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/kt -o kt -- $B > "
-              "gpurun_out/prof/kt.json",
-              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/pmc_f -o p -- $B",
-              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/pmc_w -o p -- $B",
+              "rocprofv3 --kernel-trace --stats --output-format csv -d prof/kt -o kt -- $B > prof/kt.json",
+              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d prof/pmc_f -o p -- $B",
+              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d prof/pmc_w -o p -- $B",
               "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
-              "GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/prof/pmc_m -o p -- $B",
-              f"python bench.py --workload {workload} --summarize-profile gpurun_out/prof gpurun_out/prof/kt.json",
+              "GRBM_GUI_ACTIVE --output-format csv -d prof/pmc_m -o p -- $B",
+              f"python bench.py --workload {workload} --summarize-profile prof prof/kt.json",
               "```", ""]
     out = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
     with open(out, "w") as fh:
