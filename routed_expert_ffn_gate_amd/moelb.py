@@ -147,7 +147,13 @@ def moelb_split_variant(counts, home, replica, host_count, load, variant, passes
 MOELB_SPLIT_SCHEDULE_INTS = 2 + 3 * 64 * 8
 
 
+def _check_schedule(schedule, name):
+    if schedule is not None and schedule.numel() < MOELB_SPLIT_SCHEDULE_INTS:
+        raise MoelbError(f"{name}: the schedule holds {schedule.numel()} int32, not MOELB_SPLIT_SCHEDULE_INTS")
+
+
 def moelb_split_schedule(home, replica, schedule, G, stream=None):
+    _check_schedule(schedule, "moelb_split_schedule")
     E = home.shape[0]
     N = replica.shape[1]
     _check(lib().moelb_split_schedule(_p(home), _p(replica), G, E, N, _p(schedule), _stream(stream)),
@@ -156,6 +162,7 @@ def moelb_split_schedule(home, replica, schedule, G, stream=None):
 
 def moelb_split_scheduled(counts, home, replica, schedule, host_count, load, variant=0, passes=12, eps=0,
                           stream=None):
+    _check_schedule(schedule, "moelb_split_scheduled")
     G, E = counts.shape
     N = replica.shape[1]
     _check(lib().moelb_split_scheduled(_p(counts), _p(home), _p(replica), _p(schedule), G, E, N, passes, eps, variant,
