@@ -374,7 +374,7 @@ def prepare_units(cfg, layer, dev):
     import torch
     from synth import workloads as W
     from routed_expert_ffn_gate_amd.layer import to_device
-    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import pack_expert_weights
     up = lambda a: to_device(a, cfg.dtype, dev)  # noqa: E731
 
     def upw(a):
@@ -384,8 +384,7 @@ def prepare_units(cfg, layer, dev):
         t = up(a)
         if not layer.ffn_opt:
             return t
-        p = torch.empty_like(t)
-        M.moelb_pack_weights(t, p)
+        p = pack_expert_weights(t)
         torch.cuda.synchronize()
         del t
         return p

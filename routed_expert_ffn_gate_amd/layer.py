@@ -48,6 +48,15 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def pack_expert_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """A packed copy of expert weights ([E, rows, K] or one expert's [rows,
+    K], bf16) for a layer built with packed_weights=True: done once, when the
+    weights are loaded."""
+    p = torch.empty_like(w)
+    M.moelb_pack_weights(w, p, stream=stream)
+    return p
+
+
 class HipEvents:
     """hipEvent_t handles from libamdhip64, recorded on a stream between
     entry-point calls (the step's stage marks)."""

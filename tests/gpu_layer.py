@@ -61,12 +61,7 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
     if sh is not None:
         S13, S2 = d(sh[0]), d(sh[1])
     if packed_weights:
-        from routed_expert_ffn_gate_amd import moelb as M
-
-        def pack(t):
-            p_ = torch.empty_like(t)
-            M.moelb_pack_weights(t, p_)
-            return p_
+        from routed_expert_ffn_gate_amd.layer import pack_expert_weights as pack
         W13, W2 = pack(W13), pack(W2)
         if sh is not None:
             S13, S2 = pack(S13), pack(S2)
