@@ -718,3 +718,62 @@ def test_packed_weights_shared_expert(moelb):
     b = run_layer(cfg, packed_weights=True)
     for key in ["y", "shared", "out"]:
         assert np.array_equal(a.out[key], b.out[key]), key
+
+
+@pytest.mark.parametrize("T,d,E,k,dtype,look", [
+    (300, 256, 8, 8, "bf16", True),      # k = E: every expert selected, gap +inf
+    (300, 256, 64, 1, "bf16", True),     # k = 1
+    (132, 200, 40, 4, "bf16", False),    # d % 64 != 0 (register-staged kernel), no lookahead router
+    (260, 128, 256, 16, "bf16", True),   # E = 256, k = 16
+    (100, 96, 16, 16, "f32", True),      # fp32, k = E
+    (4096, 512, 128, 8, "bf16", False),  # many token blocks, current router only
+])
+def test_gate_edge_shapes(moelb, T, d, E, k, dtype, look):
+    """moelb_gate_topk alone against the oracle's route on the edges of its
+    shape space: the selected set and, where the logits are separated, its
+    order; weights to the fp32 bar; the gap (+inf when k = E); the lookahead
+    indices."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    from routed_expert_ffn_gate_amd.layer import to_device
+    from tests.gpu_layer import NEAR_TIE, TOL
+    cfg = W.scaled(W.config("c2_qwen3_30b_decode"), steps=1, T=T, d=d, E=E, k=k, inter=64, G=4, N=1, L=1,
+                   dtype=dtype)
+    li = W.layer_inputs(cfg)
+    dev = torch.device("cuda")
+    up = lambda a: to_device(a, dtype, dev)  # noqa: E731
+    h, wc, wn = up(li.h), up(li.w_cur), up(li.w_next)
+    bc, bn = up(li.b_cur), up(li.b_next)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    wts = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    gap = torch.zeros(T, dtype=torch.float32, device=dev)
+    idxn = torch.full((T, k), -7, dtype=torch.int32, device=dev) if look else None
+    M.moelb_gate_topk(h, wc, bc, wn if look else None, bn if look else None, idx, wts, gap, idxn)
+    torch.cuda.synchronize()
+    idx_o, w_o, gap_o, idxn_o, z = O.route(li.h, li.w_cur, li.b_cur, li.w_next if look else None,
+                                           li.b_next if look else None, k, dtype)
+    g_idx, g_w, g_gap = idx.cpu().numpy(), wts.cpu().numpy(), gap.cpu().numpy()
+    near = gap_o < NEAR_TIE
+    assert np.all((g_idx >= 0) & (g_idx < E))
+    zs = -np.sort(-z, axis=1)[:, :min(k + 1, E)]
+    sep = np.all(np.diff(-zs, axis=1) >= NEAR_TIE, axis=1)
+    for t in range(T):
+        if near[t]:
+            continue
+        assert set(g_idx[t].tolist()) == set(idx_o[t].tolist()), t
+        if sep[t]:
+            assert g_idx[t].tolist() == idx_o[t].tolist(), t
+        wo = dict(zip(idx_o[t].tolist(), w_o[t].tolist()))
+        for e, wg in zip(g_idx[t].tolist(), g_w[t].tolist()):
+            assert abs(wg - wo[e]) <= TOL["f32"] * wo[e], (t, e)
+    if k == E:
+        assert np.all(np.isinf(g_gap) & (g_gap > 0))
+    else:
+        assert np.max(np.abs(g_gap[~near] - gap_o[~near])) <= 1e-4
+    if look:
+        zn = O.router_logits(O.widen(li.h, dtype), O.widen(li.w_next, dtype), li.b_next)
+        _, gapn = O.topk(zn, k)
+        gn = idxn.cpu().numpy()
+        for t in range(T):
+            if gapn[t] >= NEAR_TIE:
+                assert set(gn[t].tolist()) == set(idxn_o[t].tolist()), t
