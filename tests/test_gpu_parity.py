@@ -777,3 +777,36 @@ def test_gate_edge_shapes(moelb, T, d, E, k, dtype, look):
         for t in range(T):
             if gapn[t] >= NEAR_TIE:
                 assert set(gn[t].tolist()) == set(idxn_o[t].tolist()), t
+
+
+@pytest.mark.parametrize("T,k,d,rows_y,dtype,shared", [
+    (64, 1, 8, 64, "bf16", False),
+    (100, 3, 200, 250, "bf16", True),
+    (257, 8, 4096, 1900, "bf16", False),
+    (33, 16, 136, 500, "f32", True),
+])
+def test_combine_left_out_pairs(moelb, T, k, d, rows_y, dtype, shared):
+    """moelb_combine against the oracle: positions < 0 or >= rows_y (pairs
+    left out) contribute nothing; per-row max-norm error at the dtype's bar."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    from tests.gpu_layer import TOL, _row_rel
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(T * 7 + k)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.randn((rows_y, d), device=dev).to(tdt)
+    pos = rng.integers(0, rows_y, T * k)
+    drop = rng.random(T * k)
+    pos[drop < 0.1] = -1
+    pos[(drop >= 0.1) & (drop < 0.15)] = rows_y + rng.integers(0, 5, int(((drop >= 0.1) & (drop < 0.15)).sum()))
+    wts = rng.random((T, k)).astype(np.float32)
+    sh = torch.randn((T, d), device=dev).to(tdt) if shared else None
+    out = torch.full((T, d), 3.0, device=dev).to(tdt)
+    M.moelb_combine(y, torch.from_numpy(pos.astype(np.int32)).to(dev), torch.from_numpy(wts).to(dev), out,
+                    shared=sh)
+    torch.cuda.synchronize()
+    widen = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    pos_o = np.where(pos < rows_y, pos, -1)
+    ref = O.combine(widen(y), pos_o, wts, T, k, widen(sh) if shared else None)
+    err = _row_rel(widen(out), ref)
+    assert float(np.max(err)) <= TOL[dtype], float(np.max(err))
