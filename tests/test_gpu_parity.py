@@ -810,3 +810,31 @@ def test_combine_left_out_pairs(moelb, T, k, d, rows_y, dtype, shared):
     ref = O.combine(widen(y), pos_o, wts, T, k, widen(sh) if shared else None)
     err = _row_rel(widen(out), ref)
     assert float(np.max(err)) <= TOL[dtype], float(np.max(err))
+
+
+@pytest.mark.parametrize("T,k,E,G,hot", [
+    (512, 8, 128, 8, 0.0),
+    (4096, 2, 16, 4, 0.9),       # one expert takes 90 % of the pairs
+    (64 * 100, 16, 256, 64, 0.3),
+    (12, 1, 3, 3, 0.0),
+])
+def test_histogram_invalid_ids_and_hot_expert(moelb, T, k, E, G, hot):
+    """moelb_histogram against the oracle, bit for bit: ids outside [0, E)
+    skipped, a hot expert (the one-atomic-per-wave path), column sums."""
+    from oracle import moe_oracle as O
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(T + E)
+    idx = rng.integers(0, E, (T, k))
+    idx[rng.random((T, k)) < hot] = E // 2
+    r = rng.random((T, k))
+    idx[r < 0.03] = -1
+    idx[(r >= 0.03) & (r < 0.05)] = E + 7
+    idx = idx.astype(np.int32)
+    counts = torch.full((G, E), -5, dtype=torch.int32, device=dev)
+    total = torch.full((E,), -5, dtype=torch.int32, device=dev)
+    M.moelb_histogram(torch.from_numpy(idx).to(dev), G, counts, expert_total=total)
+    torch.cuda.synchronize()
+    ref = O.histogram(idx, G, E)
+    assert np.array_equal(counts.cpu().numpy(), ref)
+    assert np.array_equal(total.cpu().numpy(), ref.sum(0))
