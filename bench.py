@@ -485,6 +485,9 @@ def main():
     ap.add_argument("--studies", action="store_true",
                     help="also measure the two-stage step, the split variants and FreeBalance's swaps "
                          "(reported beside the headline; their kernels then share the profile)")
+    ap.add_argument("--split-overlap", choices=["auto", "on", "off"], default="auto",
+                    help="the split beside the local half of the permutation (auto: where the permutation is "
+                         "not one launch anyway)")
     ap.add_argument("--weights", choices=["packed", "row-major"], default="packed",
                     help="expert weights packed once by moelb_pack_weights (where the shape allows), or row-major")
     ap.add_argument("--rows", choices=["gather", "materialized"], default="gather",
@@ -515,7 +518,8 @@ def main():
     packed = args.weights == "packed" and weights_packable(cfg)
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype,
                      shared_inter=cfg.shared_inter, gather_rows=args.rows == "gather", materialize_x=True,
-                     packed_weights=packed)
+                     packed_weights=packed,
+                     overlap_split=None if args.split_overlap == "auto" else args.split_overlap == "on")
     units, home, S13, S2 = prepare_units(cfg, layer, dev)
     n_units = len(units)
     u0 = units[0]
@@ -671,7 +675,7 @@ def main():
                    "inter": cfg.inter, "shared_inter": cfg.shared_inter, "virtual_ranks": cfg.G,
                    "replica_slots": cfg.N, "locality_imports": cfg.L, "relief_passes": 12,
                    "layer_steps_cycled": n_units, "ffn_rows": args.rows,
-                   "ffn_weights": "packed" if packed else "row-major"},
+                   "ffn_weights": "packed" if packed else "row-major", "split_overlap": layer.overlap_split},
         "ms_per_step_median": round(_median(step_ms), 4),
         "ms_per_step_marked_median": round(_median(marked_ms), 4),
         "mfma_frac_layer": round(total_flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),

@@ -115,13 +115,16 @@ class MoELayer:
 
     def __init__(self, T, d, E, k, inter, G, N, L, dtype, device="cuda", shared_inter=0, passes=12,
                  gather_rows=True, materialize_x=False, balancer="libra", fb_tau=0, fb_gamma=None,
-                 fb_budget=None, packed_weights=False):
+                 fb_budget=None, packed_weights=False, overlap_split=None):
         """balancer "libra": replication plan (N slots, L locality imports)
         and the per-step split; "freebalance": expert swaps instead (no
         replicas; at most fb_budget swaps per rank, default N; threshold
         fb_tau; gamma = fb_gamma (num, den), default 1 / the mean rank load).
         packed_weights: the expert (and shared) weights passed to the steps
-        are in moelb_pack_weights' layout."""
+        are in moelb_pack_weights' layout.  overlap_split: run the split
+        beside the local half of the permutation (default: wherever the
+        permutation is not a single launch anyway, i.e. more than 8192 pairs,
+        E*G > 2048 or rows copied)."""
         self.T, self.d, self.E, self.k, self.inter = T, d, E, k, inter
         self.ffn_opt = M.MOELB_FFN_PACKED_WEIGHTS if packed_weights else 0
         self.G, self.N, self.L, self.passes = G, N, L, passes
@@ -171,6 +174,10 @@ class MoELayer:
         self.ev_hist = torch.cuda.Event()
         self.ev_local = torch.cuda.Event()
         self.ev_remote = torch.cuda.Event()
+        self.ev_split = torch.cuda.Event()
+        if overlap_split is None:
+            overlap_split = (not gather_rows) or T * k > 8192 or E * G > 2048
+        self.overlap_split = overlap_split
         # round schedules of the split, made once per placement (Relief): for
         # the placement in force and for the next layer's
         self.sched_cur = torch.full((M.MOELB_SPLIT_SCHEDULE_INTS,), -1, **i32)
@@ -287,13 +294,33 @@ class MoELayer:
         mark(1)
         M.moelb_histogram(self.idx, self.G, self.counts, stream=s0)
         mark(2)
-        M.moelb_split_scheduled(self.counts, home, replica_cur, self.sched_cur if sched is None else sched,
-                                self.host_count, self.load, passes=self.passes, stream=s0)
-        mark(3)
+        sched_ = self.sched_cur if sched is None else sched
         copy_rows = not self.gather_rows  # the gather GEMM reads h through perm instead
-        M.moelb_permute(h if copy_rows else None, self.idx, self.G, home, replica_cur, self.host_count,
-                        self.ws_perm, self.group_off, self.perm, self.pos, self.x_perm if copy_rows else None,
-                        d=self.d, dtype=M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32, stream=s0)
+        hr, xr = (h, self.x_perm) if copy_rows else (None, None)
+        code = M.MOELB_BF16 if self.dtype == "bf16" else M.MOELB_F32
+        if self.overlap_split:
+            # the split beside the local half of the permutation (local groups
+            # and their order do not depend on it: Libra "Key Ideas", MoE_local
+            # needs no sharding decision), the remote half after both; the
+            # outputs are moelb_permute's.  Mark 3 closes the split on its
+            # stream, so "permute" is what the permutation leaves after it.
+            self.ev_hist.record(s0)
+            self.side2.wait_event(self.ev_hist)
+            M.moelb_split_scheduled(self.counts, home, replica_cur, sched_, self.host_count, self.load,
+                                    passes=self.passes, stream=self.side2)
+            mark(3, self.side2)
+            self.ev_split.record(self.side2)
+            M.moelb_permute_local(hr, self.idx, self.G, home, replica_cur, self.ws_perm, self.group_off, self.perm,
+                                  self.pos, xr, d=self.d, dtype=code, stream=s0)
+            s0.wait_event(self.ev_split)
+            M.moelb_permute_remote(hr, self.idx, self.G, home, replica_cur, self.host_count, self.ws_perm,
+                                   self.group_off, self.perm, self.pos, xr, d=self.d, dtype=code, stream=s0)
+        else:
+            M.moelb_split_scheduled(self.counts, home, replica_cur, sched_, self.host_count, self.load,
+                                    passes=self.passes, stream=s0)
+            mark(3)
+            M.moelb_permute(hr, self.idx, self.G, home, replica_cur, self.host_count, self.ws_perm, self.group_off,
+                            self.perm, self.pos, xr, d=self.d, dtype=code, stream=s0)
         mark(4)
         self._ffn(h, w13, w2, mark if ev is not None else None, stream=s0)
         if self.shared is not None:

@@ -45,7 +45,7 @@ class LayerRun:
 
 def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool = True,
               materialize_x: bool = True, hs=None, weights=None, two_stage: bool = False,
-              balancer: str = "libra", packed_weights: bool = False) -> LayerRun:
+              balancer: str = "libra", packed_weights: bool = False, overlap_split=None) -> LayerRun:
     from routed_expert_ffn_gate_amd.layer import MoELayer, to_device, to_host
     dev = torch.device("cuda")
     li = W.layer_inputs(cfg, layer, step, hs=hs)
@@ -67,7 +67,7 @@ def run_layer(cfg: W.MoEConfig, layer: int = 1, step: int = 0, gather_rows: bool
             S13, S2 = pack(S13), pack(S2)
     L = MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.G, cfg.N, cfg.L, cfg.dtype, shared_inter=cfg.shared_inter,
                  gather_rows=gather_rows, materialize_x=materialize_x, balancer=balancer,
-                 packed_weights=packed_weights)
+                 packed_weights=packed_weights, overlap_split=overlap_split)
     home_cur = None
     if balancer == "freebalance":
         replica_cur = torch.empty((cfg.G, 0), dtype=torch.int32, device=dev)

@@ -838,3 +838,18 @@ def test_histogram_invalid_ids_and_hot_expert(moelb, T, k, E, G, hot):
     ref = O.histogram(idx, G, E)
     assert np.array_equal(counts.cpu().numpy(), ref)
     assert np.array_equal(total.cpu().numpy(), ref.sum(0))
+
+
+@pytest.mark.parametrize("name,changes", [
+    ("c2_qwen3_30b_decode", dict(steps=1, **RAGGED)),
+    ("c4_glm45_prefill", dict(T=2048)),
+    ("c2_qwen3_30b_decode", dict(steps=1, T=2048, d=256, inter=256, G=64, N=8, L=4, E=256, k=4)),
+])
+def test_split_beside_local_permutation(moelb, name, changes):
+    """The step with the split on its own stream beside the local half of the
+    permutation equals the step with both in sequence, bit for bit."""
+    cfg = W.scaled(W.config(name), **changes)
+    a = run_layer(cfg, overlap_split=False)
+    b = run_layer(cfg, overlap_split=True)
+    for key in ["host_count", "load", "group_off", "perm", "pos", "y", "out"]:
+        assert np.array_equal(a.out[key], b.out[key]), key
