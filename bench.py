@@ -1000,9 +1000,9 @@ def _study_sections(r):
               f"Step {ts['ms_per_step']} ms against {r['ms_per_step']:.4f} ms in one stage.", "",
               "| stage | ms |", "|---|---|"]
         L += [f"| {k} | {v} |" for k, v in ts["stages_ms"].items()]
-        L += [f"| split + remote permutation (split stream) | {ts['side_work_ms']} |",
+        L += [f"| split stream span: split + remote permutation, waits for free CUs included | {ts['side_work_ms']} |",
               f"| exposed wait on the step's stream | {ts['exposed_ms']} |",
-              f"| hidden under MoE_local | {ts['hidden_ms']} |"]
+              f"| of the span, overlapping MoE_local | {ts['hidden_ms']} |"]
     sv = r.get("split_variants")
     if sv:
         L += ["", "### Split variants on the step's counts and placement", "",
