@@ -9,15 +9,18 @@
 //
 // Design (gfx950): one GEMM with N = 2E columns (current router rows, then the
 // lookahead router's rows), so h -- the only large operand -- is read from HBM
-// once.  A workgroup owns 128 tokens and all N columns, so every logit of a
-// token ends up in one workgroup for the epilogue.  8 waves: 2 (token halves) x
-// 4 (column quarters); each wave runs bf16 MFMA 16x16x32 on a 64 x (16*NF)
-// tile.  h tiles are staged through LDS (double buffered, one barrier per K
-// step); router rows go straight from global/L2 into registers, since each
-// wave needs only its own columns.  The epilogue writes biased fp32 logits to
-// LDS (one token half at a time) and 4 lanes per token and direction select
-// the top-(k+2) with a register insertion list, merged across the 4 lanes with
-// two xor shuffles; the selection is exact (see topk_epilogue).
+// once.  A workgroup owns BM tokens and all N columns, so every logit of a
+// token ends up in one workgroup for the epilogue: BM = 128, or 64 where the
+// batch has too few 128-token blocks to fill the CUs.  8 waves: 2 (token
+// halves) x 4 (column quarters); each wave runs bf16 MFMA 16x16x32 on a
+// (BM/2) x (16*NF) tile.  In the register-staged form, h tiles are staged
+// through LDS (double buffered, one barrier per K step) and router rows go
+// straight from global/L2 into registers, since each wave needs only its own
+// columns; the direct-to-LDS form is described above its kernel.  The
+// epilogue writes biased fp32 logits to LDS and 2-8 lanes per token and
+// direction select the top-(k+2) with a register insertion list, merged
+// across those lanes with xor shuffles; the selection is exact (see
+// topk_epilogue).
 #include "common.h"
 
 namespace {
@@ -344,7 +347,7 @@ __device__ __forceinline__ void gt_copy16(uint32_t voff, const void* sbase, uint
 // alone (its top-k indices only), so twice as many workgroups each read half
 // the router rows; N = 64 * NF then covers E columns (padding columns read row
 // 0 and are never selected).
-template <int NF, int KL, int S>
+template <int NF, int KL, int S, int BM>
 __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
     const uint16_t* __restrict__ h, int T, int d, int E, int k, const uint16_t* __restrict__ w_cur_in,
     const float* __restrict__ b_cur_in, const uint16_t* __restrict__ w_next_in, const float* __restrict__ b_next_in,
@@ -362,10 +365,12 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   int32_t* idx_next = split ? nullptr : idx_next_in;
   constexpr int BK = 64;
   constexpr int N = 64 * NF;
-  constexpr int STAGE = (GATE_BM + N) * BK;  // elements: A rows, then B rows
-  constexpr int VPS = 2 + NF;                // DMA instructions per wave and K step
-  // the logits of all 128 tokens fit in the stages' LDS
-  constexpr bool ONE_PASS = (size_t)GATE_BM * (N + 4) * 4 <= (size_t)S * STAGE * 2;
+  constexpr int AV = BM / 64;             // h-row DMA instructions per wave and K step
+  constexpr int MI = BM / 32;             // 16-row blocks of a wave's BM/2 tokens
+  constexpr int STAGE = (BM + N) * BK;    // elements: A rows, then B rows
+  constexpr int VPS = AV + NF;            // DMA instructions per wave and K step
+  // the logits of all BM tokens fit in the stages' LDS
+  constexpr bool ONE_PASS = (size_t)BM * (N + 4) * 4 <= (size_t)S * STAGE * 2;
   extern __shared__ __align__(16) char smem[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   float* Z = reinterpret_cast<float*>(smem);
@@ -373,17 +378,17 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
-  const int tok0 = blockIdx.x * GATE_BM;
+  const int tok0 = blockIdx.x * BM;
   const bool has_next = w_next != nullptr;
   const int KT = d / BK;
 
   // DMA rows of this lane: 8-row blocks, row (lane >> 3), slot (lane & 7);
   // byte offsets from a wave-uniform base (h, or the router matrix that holds
   // the whole 8-row block: E is a multiple of 32 here)
-  uint32_t aoff[2];
+  uint32_t aoff[AV];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = (wave * 2 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < AV; ++j) {
+    const int r = (wave * AV + j) * 8 + (lane >> 3);
     const int t = min(tok0 + r, T - 1);  // rows past T are computed and dropped
     aoff[j] = ((uint32_t)t * (uint32_t)d + gt_slot(r, lane & 7) * 8) * 2u;
   }
@@ -395,19 +400,19 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   }
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_u32 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  // DMA instruction U (0..VPS-1) of K step KTI: U < 2 are h rows, the rest router rows
+  // DMA instruction U (0..VPS-1) of K step KTI: U < AV are h rows, the rest router rows
 #define GT_COPY(KTI, U)                                                                            \
   {                                                                                                \
     const int kti_ = (KTI);                                                                        \
     const uint32_t st_ = lds_u32 + (uint32_t)((kti_ % S) * STAGE) * 2u;                            \
-    if ((U) < 2) {                                                                                 \
-      gt_copy16(aoff[(U) & 1], h + (size_t)kti_ * BK,                                              \
-                st_ + (uint32_t)((wave_s * 2 + ((U) & 1)) * 8 * BK) * 2u);                         \
+    if ((U) < AV) {                                                                                \
+      const int ja_ = (U) < AV ? (U) : 0;                                                          \
+      gt_copy16(aoff[ja_], h + (size_t)kti_ * BK, st_ + (uint32_t)((wave_s * AV + ja_) * 8 * BK) * 2u); \
     } else {                                                                                       \
-      const int jb_ = (U) >= 2 ? (U) - 2 : 0;                                                      \
+      const int jb_ = (U) >= AV ? (U) - AV : 0;                                                    \
       const uint16_t* m_ = (w_next == nullptr || (wave_s * NF + jb_) * 8 < E) ? w_cur : w_next;      \
       gt_copy16(boff[jb_], m_ + (size_t)kti_ * BK,                                                 \
-                st_ + (uint32_t)((GATE_BM + (wave_s * NF + jb_) * 8) * BK) * 2u);                  \
+                st_ + (uint32_t)((BM + (wave_s * NF + jb_) * 8) * BK) * 2u);                       \
     }                                                                                              \
   }
 
@@ -417,25 +422,25 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   int kofs[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) kofs[ks] = fr * BK + (((ks * 4 + (lane >> 4)) ^ swz) * 8);
-  const int arow0 = wm * 64 * BK;
-  const int brow0 = (GATE_BM + wn * NF * 16) * BK;
+  const int arow0 = wm * (BM / 2) * BK;
+  const int brow0 = (BM + wn * NF * 16) * BK;
 
-  f32x4_t acc[4][NF];
+  f32x4_t acc[MI][NF];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NF; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bf16x8_t xa[4], xb[NF], ya[4], yb[NF];
+  bf16x8_t xa[MI], xb[NF], ya[MI], yb[NF];
   // refill of a freed stage: instructions [0, H1) right after the barrier that
   // frees it, [H1, VPS) during the next step's first sub-step (two stages: all
   // at once, it is needed one step later)
   constexpr int H1 = S >= 3 ? (VPS + 1) / 2 : VPS;
-  constexpr int BPM = (NF + 3) / 4;  // router fragments read per 16-row block
+  constexpr int BPM = (NF + MI - 1) / MI;  // router fragments read per 16-row block
   // One 32-wide k sub-step: per 16-row block mi, read the next set's fragments
   // (sub-step KS of stage RS, if RD), run the block's NF MFMAs on the current
   // set, and issue a share of DMA instructions [P0, P1) of K step KI (if DO).
 #define GT_SUB(FA, FB, NA, NB, RS, KS, RD, DO, KI, P0, P1)                                         \
-  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                               \
+  _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                              \
     if (RD) {                                                                                      \
       const uint16_t* rs_ = (RS);                                                                  \
       NA[mi] = *reinterpret_cast<const bf16x8_t*>(rs_ + arow0 + mi * 16 * BK + kofs[KS]);          \
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
     _Pragma("unroll") for (int ni = 0; ni < NF; ++ni)                                              \
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0); \
     if (DO) {                                                                                      \
-      constexpr int per_ = ((P1) - (P0) + 3) / 4;                                                  \
+      constexpr int per_ = ((P1) - (P0) + MI - 1) / MI;                                            \
       _Pragma("unroll") for (int q = 0; q < per_; ++q) {                                           \
         const int u_ = (P0) + mi * per_ + q;                                                       \
         if (u_ < (P1)) GT_COPY(KI, u_)                                                             \
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
     asm volatile("" ::: "memory");
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + arow0 + i * 16 * BK + kofs[0]);
+  for (int i = 0; i < MI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + arow0 + i * 16 * BK + kofs[0]);
 #pragma unroll
   for (int i = 0; i < NF; ++i) xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + brow0 + i * 16 * BK + kofs[0]);
   for (int kt = 0; kt < KT; ++kt) {
@@ -514,43 +519,47 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   __syncthreads();  // LDS is reused for the logits
 
   const int colbase = wn * NF * 16;
-  if (ONE_PASS) {
-    // all 128 tokens' logits fit in LDS: one selection pass
+  const int dirs = has_next ? 2 : 1;
+  if constexpr (ONE_PASS) {
+    // all BM tokens' logits fit in LDS: one selection pass
 #pragma unroll
     for (int ni = 0; ni < NF; ++ni) {
       const int col = colbase + ni * 16 + (lane & 15);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
+          const int r = wm * (BM / 2) + mi * 16 + (lane >> 4) * 4 + i;
           Z[r * zstride + col] = acc[mi][ni][i] + bias[ni];
         }
     }
     __syncthreads();
-    const int ntok = min(GATE_BM, T - tok0);
-    topk_epilogue<KL>(Z, zstride, ntok, has_next ? 2 : 4, tok0, T, E, k, has_next, idx, wts, gap, idx_next);
-    return;
-  }
-  for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
+    const int ntok = min(BM, T - tok0);
+    topk_epilogue<KL>(Z, zstride, ntok, GATE_THREADS / (BM * dirs), tok0, T, E, k, has_next, idx, wts, gap,
+                      idx_next);
+  } else {
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
 #pragma unroll
-      for (int ni = 0; ni < NF; ++ni) {
-        const int col = colbase + ni * 16 + (lane & 15);
+        for (int ni = 0; ni < NF; ++ni) {
+          const int col = colbase + ni * 16 + (lane & 15);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+          for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mi * 16 + (lane >> 4) * 4 + i;
-            Z[r * zstride + col] = acc[mi][ni][i] + bias[ni];
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int r = mi * 16 + (lane >> 4) * 4 + i;
+              Z[r * zstride + col] = acc[mi][ni][i] + bias[ni];
+            }
+        }
       }
+      __syncthreads();
+      const int t0 = tok0 + half * (BM / 2);
+      const int ntok = min(BM / 2, T - t0);
+      if (ntok > 0)
+        topk_epilogue<KL>(Z, zstride, ntok, GATE_THREADS / ((BM / 2) * dirs), t0, T, E, k, has_next, idx, wts, gap,
+                          idx_next);
+      __syncthreads();
     }
-    __syncthreads();
-    const int t0 = tok0 + half * 64;
-    const int ntok = min(64, T - t0);
-    if (ntok > 0) topk_epilogue<KL>(Z, zstride, ntok, has_next ? 4 : 8, t0, T, E, k, has_next, idx, wts, gap, idx_next);
-    __syncthreads();
   }
 }
 
@@ -628,17 +637,17 @@ int launch_bf16(int NF, const void* h, int T, int d, int E, int k, const void* w
   return MOELB_OK;
 }
 
-template <int NF, int KL, int S>
+template <int NF, int KL, int S, int BM>
 int launch_dma_nf(const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur, const void* w_next,
                   const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next, bool split,
                   hipStream_t s) {
   const int N = 64 * NF;
   const int zs = zstride_for(N);
-  const size_t lds_main = (size_t)S * (GATE_BM + N) * 64 * 2;
+  const size_t lds_main = (size_t)S * (BM + N) * 64 * 2;
   const size_t lds_z = 64ull * zs * 4;
   const size_t lds = lds_main > lds_z ? lds_main : lds_z;
-  if (!moelb_allow_lds(gate_topk_dma_kernel<NF, KL, S>, lds)) return MOELB_ELAUNCH;
-  hipLaunchKernelGGL((gate_topk_dma_kernel<NF, KL, S>), dim3((T + GATE_BM - 1) / GATE_BM, split ? 2 : 1),
+  if (!moelb_allow_lds(gate_topk_dma_kernel<NF, KL, S, BM>, lds)) return MOELB_ELAUNCH;
+  hipLaunchKernelGGL((gate_topk_dma_kernel<NF, KL, S, BM>), dim3((T + BM - 1) / BM, split ? 2 : 1),
                      dim3(GATE_THREADS), lds, s,
                      static_cast<const uint16_t*>(h), T, d, E, k, static_cast<const uint16_t*>(w_cur), b_cur,
                      static_cast<const uint16_t*>(w_next), b_next, idx, wts, gap, idx_next, zs);
@@ -646,23 +655,36 @@ int launch_dma_nf(const void* h, int T, int d, int E, int k, const void* w_cur, 
   return MOELB_OK;
 }
 
-// Direct-to-LDS variant: N = 64 * NF columns (NF <= 7), d % 64 == 0.
+// Direct-to-LDS variant: N = 64 * NF columns (NF <= 7), d % 64 == 0; 64-token
+// blocks (half64) for NF <= 4 only.
 template <int KL>
-int launch_dma(int NF, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
+int launch_dma(int NF, bool half64, const void* h, int T, int d, int E, int k, const void* w_cur, const float* b_cur,
                const void* w_next, const float* b_next, int32_t* idx, float* wts, float* gap, int32_t* idx_next,
                bool split, hipStream_t s) {
+#define MOELB_DMA(nf, st, bm) \
+  return launch_dma_nf<nf, KL, st, bm>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s)
+  if (half64) {
+    switch (NF) {
+      case 1: MOELB_DMA(1, 3, 64);
+      case 2: MOELB_DMA(2, 3, 64);
+      case 3: MOELB_DMA(3, 3, 64);
+      case 4: MOELB_DMA(4, 3, 64);
+      default: return MOELB_EINVAL;
+    }
+  }
   switch (NF) {
     // (a four-stage ring for N <= 192, three steps ahead, measured no faster
     // on the decode, GLM-4.5 and OLMoE shapes)
-    case 1: return launch_dma_nf<1, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 2: return launch_dma_nf<2, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 3: return launch_dma_nf<3, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 4: return launch_dma_nf<4, KL, 3>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 5: return launch_dma_nf<5, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 6: return launch_dma_nf<6, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-    case 7: return launch_dma_nf<7, KL, 2>(h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+    case 1: MOELB_DMA(1, 3, 128);
+    case 2: MOELB_DMA(2, 3, 128);
+    case 3: MOELB_DMA(3, 3, 128);
+    case 4: MOELB_DMA(4, 3, 128);
+    case 5: MOELB_DMA(5, 2, 128);
+    case 6: MOELB_DMA(6, 2, 128);
+    case 7: MOELB_DMA(7, 2, 128);
     default: return MOELB_EINVAL;
   }
+#undef MOELB_DMA
 }
 
 template <int KL>
@@ -708,10 +730,13 @@ extern "C" int moelb_gate_topk(const void* h, int T, int d, int E, int k, int dt
     const bool fused = dma_ok && N % 64 == 0 && NF <= nfmax;
     if (split || fused) {
       const int nf = split ? NFs : NF;
-      if (k <= 2) return launch_dma<4>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      if (k <= 4) return launch_dma<6>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      if (k <= 8) return launch_dma<10>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
-      return launch_dma<18>(nf, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      // still fewer workgroups than CUs with 64-token blocks: take them (half
+      // the h rows and MFMAs per workgroup; the router rows are read as before)
+      const bool half64 = nf <= 4 && (split ? 2 : 1) * ((T + 63) / 64) <= compute_units();
+      if (k <= 2) return launch_dma<4>(nf, half64, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 4) return launch_dma<6>(nf, half64, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      if (k <= 8) return launch_dma<10>(nf, half64, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
+      return launch_dma<18>(nf, half64, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, split, s);
     }
     if (k <= 2) return launch_bf16<4>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);
     if (k <= 4) return launch_bf16<6>(NF, h, T, d, E, k, w_cur, b_cur, w_next, b_next, idx, wts, gap, idx_next, s);

@@ -726,7 +726,10 @@ def test_packed_weights_shared_expert(moelb):
     (132, 200, 40, 4, "bf16", False),    # d % 64 != 0 (register-staged kernel), no lookahead router
     (260, 128, 256, 16, "bf16", True),   # E = 256, k = 16
     (100, 96, 16, 16, "f32", True),      # fp32, k = E
-    (4096, 512, 128, 8, "bf16", False),  # many token blocks, current router only
+    (4096, 512, 128, 8, "bf16", False),  # 64-token blocks, current router only
+    (16100, 128, 64, 8, "bf16", True),   # 128-token blocks, one launch per router, ragged last block
+    (20000, 128, 32, 4, "bf16", True),   # 128-token blocks, both routers in one launch, ragged
+    (20000, 128, 64, 4, "bf16", False),  # 128-token blocks, current router only, ragged
 ])
 def test_gate_edge_shapes(moelb, T, d, E, k, dtype, look):
     """moelb_gate_topk alone against the oracle's route on the edges of its
