@@ -28,6 +28,7 @@ namespace {
 // ---------------------------------------------------------------- histogram
 
 constexpr int HIST_THREADS = 1024;
+constexpr int HIST_BATCH = 16;  // ids loaded per thread before their atomics
 
 __global__ __launch_bounds__(HIST_THREADS) void histogram_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                                   int E, int G, int32_t* __restrict__ counts) {
@@ -37,17 +38,26 @@ __global__ __launch_bounds__(HIST_THREADS) void histogram_kernel(const int32_t* 
   __syncthreads();
   const size_t per = (size_t)(T / G) * k;
   const int32_t* p = idx + (size_t)s * per;
-  const size_t n_iter = (per + blockDim.x - 1) / blockDim.x;
-  for (size_t it = 0; it < n_iter; ++it) {
-    const size_t q = it * blockDim.x + threadIdx.x;
-    const int e = q < per ? p[q] : -1;
-    const bool valid = e >= 0 && e < E;
-    // fold the lanes that share lane 0's expert into one atomic
-    const int e0 = __shfl(e, 0, MOELB_WAVE);
-    const bool same = valid && e == e0;
-    const uint64_t m = __ballot(same);
-    if (lane_id() == 0 && same) atomicAdd(&bins[e0], __popcll(m));
-    if (valid && !same) atomicAdd(&bins[e], 1);
+  // HIST_BATCH coalesced loads in flight per thread before their atomics: the
+  // loop would otherwise wait out one load latency per id
+  for (size_t base = 0; base < per; base += (size_t)HIST_BATCH * blockDim.x) {
+    int ev[HIST_BATCH];
+#pragma unroll
+    for (int u = 0; u < HIST_BATCH; ++u) {
+      const size_t q = base + (size_t)u * blockDim.x + threadIdx.x;
+      ev[u] = q < per ? p[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < HIST_BATCH; ++u) {
+      const int e = ev[u];
+      const bool valid = e >= 0 && e < E;
+      // fold the lanes that share lane 0's expert into one atomic
+      const int e0 = __shfl(e, 0, MOELB_WAVE);
+      const bool same = valid && e == e0;
+      const uint64_t m = __ballot(same);
+      if (lane_id() == 0 && same) atomicAdd(&bins[e0], __popcll(m));
+      if (valid && !same) atomicAdd(&bins[e], 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(size_t)s * E + e] = bins[e];
