@@ -1232,12 +1232,13 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_persistent_kernel(const uint16
 // these GEMMs at about 4.2 TB/s; the weights' row-major read pattern was
 // (packed weights: 4.5 TB/s, gate/up 0.125 -> 0.114 ms).  128-column tiles
 // with packed weights, for a better-balanced last round: still slower (0.120
-// to 0.124 ms).  The gate/up GEMM reads W13 non-temporally: each expert's
-// rows are wanted only by the tiles running at the same time, and the stream
-// no longer evicts the activations, so the down GEMM that follows finds its
-// inputs cached (decode step 0.280 -> 0.270 ms, down GEMM 0.070 -> 0.066 ms).
-// W2 read the same way made the down GEMM slower (a hot expert's 64-row
-// tiles share its W2 slices).
+// to 0.124 ms).  Weights are read non-temporally where one tile uses them:
+// W13 in the gate/up GEMM (the tiles of an expert that share it run at the
+// same time) and W2 of experts whose rows fit one tile.  The stream then no
+// longer evicts the activations: the down GEMM finds its inputs cached, the
+// next step's gate its hidden states and router (decode step 0.280 -> 0.265
+// ms).  All of W2 read that way made the down GEMM slower (a hot expert's
+// 64-row tiles share its W2 slices).
 constexpr int SK_BM = 64;
 constexpr int SK_BN = 256;
 constexpr int SK_STAGE = (SK_BM + SK_BN) * DL_BK;  // elements per stage
@@ -1296,6 +1297,10 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* 
     }
     boff[j] = w_off((int)brow, K, dl_slot(r, lane & 7), s.wpacked);
   }
+  // the weight rows are read by this tile alone: the gate/up GEMM's W13 (the
+  // tiles of one expert that share it run at the same time), or W2 of an
+  // expert whose rows fit one tile
+  const bool w_once = MODE == 0 || (v0 == s.eoff[e] && vend - v0 <= SK_BM);
   // issue K step KTI into its ring stage (SK_VPS instructions per wave)
   auto issue = [&](int kti) {
     const uint32_t st = lds_u32 + (uint32_t)((kti % SK_STAGES) * SK_STAGE) * 2u;
@@ -1305,7 +1310,7 @@ __global__ __launch_bounds__(MF_THREADS) void ffn_skinny_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t dst = st + (uint32_t)((SK_BM + (wave_s * 8 + j) * 8) * DL_BK) * 2u;
-      if (MODE == 0)
+      if (w_once)
         dl_copy16_nt(boff[j], bbase + (size_t)kti * wstep, dst);
       else
         dl_copy16(boff[j], bbase + (size_t)kti * wstep, dst);
