@@ -25,7 +25,7 @@
 
 namespace {
 
-constexpr int GATE_BM = 128;       // tokens per workgroup
+constexpr int GATE_BM = 128;       // tokens per workgroup (the direct-to-LDS form also takes 64)
 constexpr int GATE_BK = 64;        // K per pipeline step
 constexpr int GATE_THREADS = 512;  // 8 waves
 constexpr int A_STRIDE = GATE_BK + 8;  // bf16 elements per LDS row (16 B pad)
@@ -317,9 +317,10 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_bf16_kernel(
 
 // ---------------------------------------------------------------- bf16 MFMA kernel, direct-to-LDS
 
-// The same workgroup tile, waves and epilogue as gate_topk_bf16_kernel, for
-// N = 64 * NF columns and d % 64 == 0.  The h tile (128 x 64) and the router
-// rows (N x 64) of each 64-wide K step stream global -> LDS with
+// The same waves and epilogue as gate_topk_bf16_kernel, for N = 64 * NF
+// columns and d % 64 == 0, with BM = 128 or 64 tokens per workgroup.  The h
+// tile (BM x 64) and the router rows (N x 64) of each 64-wide K step stream
+// global -> LDS with
 // global_load_lds_dwordx4 into S swizzled stages (16-byte chunk c of row r in
 // slot c ^ (((r >> 1) ^ (r << 2)) & 7): conflict-free 16-row fragment reads).
 // A wave is held up while the texture unit accepts a burst of loads, so the
@@ -674,7 +675,9 @@ int launch_dma(int NF, bool half64, const void* h, int T, int d, int E, int k, c
   }
   switch (NF) {
     // (a four-stage ring for N <= 192, three steps ahead, measured no faster
-    // on the decode, GLM-4.5 and OLMoE shapes)
+    // on the decode, GLM-4.5 and OLMoE shapes; four waves of 64 x N/2 tiles,
+    // a quarter fewer fragment reads, slower on every shape: 113-117 against
+    // 99-110 us on Qwen3-235B's, 120 against 91 on GLM-4.5's)
     case 1: MOELB_DMA(1, 3, 128);
     case 2: MOELB_DMA(2, 3, 128);
     case 3: MOELB_DMA(3, 3, 128);
