@@ -653,7 +653,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_JSON):
         with open(TRAFFIC_JSON) as fh:
-            tr = json.load(fh)
+            tr = _traffic_records(json.load(fh)).get(cfg.name, {})
         if (tr.get("workload") == cfg.name and tr.get("kernel_source_sha") == _kernel_sha() and
                 tr.get("ffn_weights", "row-major") == ("packed" if packed else "row-major")):
             traffic = tr.get("bytes_per_launch")
@@ -771,6 +771,22 @@ def _rows_launches(write_rows, fw, pairs):
 SETUP_KERNELS = ("pack_weights_kernel",)
 
 
+FFN_GEMM_KERNELS = ("ffn_persistent_kernel", "ffn_skinny_kernel", "ffn_mfma_dma_kernel", "ffn_mfma_kernel",
+                    "ffn_simt_kernel")
+
+
+def _shared_launches(mops_rows, f):
+    """For each FFN GEMM launch in order, per kernel name: is it the shared
+    expert's (executed MFMA work under half the routed GEMM's)?"""
+    import collections
+    flags = collections.defaultdict(list)
+    for n, _, v in mops_rows:
+        if n.startswith(FFN_GEMM_KERNELS):
+            routed = f["ffn_gate_up_flop"] if n.endswith("<0>") else f["ffn_down_flop"]
+            flags[n].append(v * 512 < 0.5 * routed)
+    return flags
+
+
 def _kernel_key(name, rows_flag):
     if name.startswith("rank_scatter_kernel"):
         return name + (" (rows)" if rows_flag else " (indices)")
@@ -795,6 +811,10 @@ def kernel_work(cfg, active):
         "ffn_skinny_kernel<0>": ("mfma", f["ffn_gate_up_flop"], "FLOP"),
         "ffn_skinny_kernel<1>": ("mfma", f["ffn_down_flop"], "FLOP"),
         "combine_kernel": ("hbm", by["combine"], "B"),
+        # the shared expert's GEMMs (one group of all T tokens), after the
+        # routed ones so that plain names match those first
+        "ffn_persistent_kernel<0> (shared expert)": ("mfma", 4.0 * T * d * cfg.shared_inter, "FLOP"),
+        "ffn_persistent_kernel<1> (shared expert)": ("mfma", 2.0 * T * d * cfg.shared_inter, "FLOP"),
         "_ffn_bytes": (active * 2.0 * I * d * b + T * d * b + P * I * b, P * I * b + active * d * I * b + P * d * b),
     }
 
@@ -826,16 +846,24 @@ def summarize_profile(workload, prof_dir, bench_json):
     ff, fw = cb / (copy_f * 1024.0), cb / (copy_w * 1024.0)
 
     is_rows = _rows_launches(write, fw, cfg.T * cfg.k)
+    is_shared = _shared_launches(mops, algorithmic_work(cfg)[0]) if cfg.shared_inter else {}
 
     def per_kernel(rows):
         agg = collections.defaultdict(list)
         i = 0
+        seen = collections.Counter()
         for n, dur, v in rows:
             flag = False
             if n.startswith("rank_scatter_kernel"):
                 flag = is_rows[i] if i < len(is_rows) else False
                 i += 1
-            agg[_kernel_key(n, flag)].append((dur, v))
+            key = _kernel_key(n, flag)
+            if n in is_shared:
+                j = seen[n]
+                seen[n] += 1
+                if j < len(is_shared[n]) and is_shared[n][j]:
+                    key = n + " (shared expert)"
+            agg[key].append((dur, v))
         return agg
 
     KT, F, Wr, MO, GR, MB = (per_kernel(x) for x in (kt, fetch, write, mops, grbm, mbusy))
@@ -884,7 +912,7 @@ def summarize_profile(workload, prof_dir, bench_json):
         key = next((w for w in work if base.startswith(w.partition(" (")[0]) and
                     (not tail or w.endswith("(" + tail))), None)
         bound, amt, unit = work[key] if key else ("latency", None, "")
-        if bound == "mfma":
+        if bound == "mfma" and not tail:
             # the FFN GEMMs: HBM-bound below the ridge (decode batches stream weights)
             fb_alg = ffn_bytes[0] if name.endswith("<0>") else ffn_bytes[1]
             if amt / fb_alg < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9):
@@ -941,8 +969,19 @@ def summarize_profile(workload, prof_dir, bench_json):
               "bytes_per_launch": gu_row[0] + gu_row[1],
               "note": "FETCH_SIZE and WRITE_SIZE per launch, scaled by copy_bytes / (counter KiB x 1024) "
                       "of a plain device copy of copy_bytes"}
+        records = {}
+        if os.path.exists(TRAFFIC_JSON):
+            with open(TRAFFIC_JSON) as fh:
+                records = _traffic_records(json.load(fh))
+        records[workload] = tr
         with open(TRAFFIC_JSON, "w") as fh:
-            json.dump(tr, fh, indent=1)
+            json.dump(records, fh, indent=1)
+
+
+def _traffic_records(data):
+    """The gate/up GEMM's traffic records by workload (a file holding a single
+    record is read as one workload's)."""
+    return {data["workload"]: data} if "workload" in data else data
 
 
 def summarize_runs(paths, out_name, command):
