@@ -60,16 +60,43 @@ __device__ __forceinline__ void list_insert(Key (&l)[KL], Key x) {
   }
 }
 
+// The same for 32-bit keys in one instruction per entry: in a descending list
+// the new entry i is the median of x, the old entry i and the old entry i-1
+// (x itself where it belongs, the entry above it shifted down below that,
+// the old entry above), so every entry is computed from the old list, last
+// entry first, with no chain between them.
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <int KL>
+__device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
+#pragma unroll
+  for (int i = KL - 1; i > 0; --i) l[i] = med3_u32(x, l[i], l[i - 1]);
+  l[0] = x > l[0] ? x : l[0];
+}
+
 // The KL largest keys of a token's E logits in `row`: each of the token's lpt
-// lanes (sub = 0..lpt-1) scans every lpt-th logit, then the partial lists are
-// merged across those lanes (xor shuffles), so every lane ends with the whole
-// list.  All lanes of the wave take part (inactive tokens scan nothing).
+// lanes (sub = 0..lpt-1) scans every lpt-th logit (four loads ahead of their
+// inserts), then the partial lists are merged across those lanes (xor
+// shuffles), so every lane ends with the whole list.  All lanes of the wave
+// take part (inactive tokens scan nothing).
 template <int KL, typename Key>
 __device__ __forceinline__ void select_keys(const float* row, bool active, int E, int sub, int lpt, Key (&l)[KL]) {
 #pragma unroll
   for (int i = 0; i < KL; ++i) l[i] = 0;  // below every real key
-  if (active)
-    for (int e = sub; e < E; e += lpt) list_insert<KL>(l, make_key(row[e], e, Key(0)));
+  if (active) {
+    int e = sub;
+    for (; e + 3 * lpt < E; e += 4 * lpt) {
+      const float v0 = row[e], v1 = row[e + lpt], v2 = row[e + 2 * lpt], v3 = row[e + 3 * lpt];
+      list_insert<KL>(l, make_key(v0, e, Key(0)));
+      list_insert<KL>(l, make_key(v1, e + lpt, Key(0)));
+      list_insert<KL>(l, make_key(v2, e + 2 * lpt, Key(0)));
+      list_insert<KL>(l, make_key(v3, e + 3 * lpt, Key(0)));
+    }
+    for (; e < E; e += lpt) list_insert<KL>(l, make_key(row[e], e, Key(0)));
+  }
   for (int m = 1; m < lpt; m <<= 1) {
     Key p[KL];
 #pragma unroll
@@ -162,8 +189,18 @@ __device__ __forceinline__ void topk_epilogue(const float* z, int stride, int nt
     // a lookahead-only block of the split launch)
     const float mx = active ? row[li[0]] : 0.f;
     float s = 0.f;
-    if (active && wts)
-      for (int e = sub; e < E; e += lpt) s += __expf(row[e] - mx);
+    if (active && wts) {
+      // four loads ahead of their terms; the terms are added in scan order
+      int e = sub;
+      for (; e + 3 * lpt < E; e += 4 * lpt) {
+        const float z0 = row[e], z1 = row[e + lpt], z2 = row[e + 2 * lpt], z3 = row[e + 3 * lpt];
+        s += __expf(z0 - mx);
+        s += __expf(z1 - mx);
+        s += __expf(z2 - mx);
+        s += __expf(z3 - mx);
+      }
+      for (; e < E; e += lpt) s += __expf(row[e] - mx);
+    }
     for (int m = 1; m < lpt; m <<= 1) s += __shfl_xor(s, m, MOELB_WAVE);
     if (active && sub == 0 && t < T) {
       const float inv = 1.0f / s;
