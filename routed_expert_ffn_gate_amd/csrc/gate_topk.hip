@@ -18,9 +18,9 @@
 // straight from global/L2 into registers, since each wave needs only its own
 // columns; the direct-to-LDS form is described above its kernel.  The
 // epilogue writes biased fp32 logits to LDS and 2-8 lanes per token and
-// direction select the top-(k+2) with a register insertion list, merged
-// across those lanes with xor shuffles; the selection is exact (see
-// topk_epilogue).
+// direction select the top-(k+2) with a register insertion list (one median
+// instruction per entry), merged across those lanes by DPP; the selection is
+// exact (see topk_epilogue).
 #include "common.h"
 
 namespace {
@@ -77,11 +77,33 @@ __device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
   l[0] = x > l[0] ? x : l[0];
 }
 
+// Partner key in the merge round of lane groups of 2M: rounds 1 and 2 swap
+// within quads, round 4 mirrors each half-row of 8 lanes and round 8 each row
+// of 16 (DPP, no LDS round trip); wider groups shuffle.  Any pairing that
+// joins the two halves of every group of 2M lanes merges correctly.
+template <int M>
+__device__ __forceinline__ uint32_t merge_partner(uint32_t v) {
+  constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
+  if constexpr (M <= 8)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+  else
+    return __shfl_xor(v, M, MOELB_WAVE);
+}
+
+template <int M, int KL>
+__device__ __forceinline__ void merge_round(uint32_t (&l)[KL]) {
+  uint32_t p[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) p[i] = merge_partner<M>(l[i]);
+#pragma unroll
+  for (int i = 0; i < KL; ++i) list_insert<KL>(l, p[i]);
+}
+
 // The KL largest keys of a token's E logits in `row`: each of the token's lpt
 // lanes (sub = 0..lpt-1) scans every lpt-th logit (four loads ahead of their
-// inserts), then the partial lists are merged across those lanes (xor
-// shuffles), so every lane ends with the whole list.  All lanes of the wave
-// take part (inactive tokens scan nothing).
+// inserts), then the partial lists are merged across those lanes, so every
+// lane ends with the whole list.  All lanes of the wave take part (inactive
+// tokens scan nothing), in uniform control flow.
 template <int KL, typename Key>
 __device__ __forceinline__ void select_keys(const float* row, bool active, int E, int sub, int lpt, Key (&l)[KL]) {
 #pragma unroll
@@ -97,13 +119,12 @@ __device__ __forceinline__ void select_keys(const float* row, bool active, int E
     }
     for (; e < E; e += lpt) list_insert<KL>(l, make_key(row[e], e, Key(0)));
   }
-  for (int m = 1; m < lpt; m <<= 1) {
-    Key p[KL];
-#pragma unroll
-    for (int i = 0; i < KL; ++i) p[i] = __shfl_xor(l[i], m, MOELB_WAVE);
-#pragma unroll
-    for (int i = 0; i < KL; ++i) list_insert<KL>(l, p[i]);
-  }
+  if (lpt > 1) merge_round<1>(l);
+  if (lpt > 2) merge_round<2>(l);
+  if (lpt > 4) merge_round<4>(l);
+  if (lpt > 8) merge_round<8>(l);
+  if (lpt > 16) merge_round<16>(l);
+  if (lpt > 32) merge_round<32>(l);
 }
 
 // Epilogue over `ntok` tokens whose logits (bias included) sit in LDS rows of
