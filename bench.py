@@ -479,6 +479,9 @@ def main():
                          "(PROF_DIR/kt, pmc_f, pmc_w, pmc_m) and the bench line of the kernel-trace run")
     ap.add_argument("--summarize-runs", nargs="+", metavar="ARG",
                     help="OUT_NAME COMMAND JSON...: write profiles/OUT_NAME.md from bench result lines")
+    ap.add_argument("--summarize-counters", nargs=1, metavar="PROF_DIR",
+                    help="write profiles/counters_<workload>.md from the stall counter runs PROF_DIR/pmc_s "
+                         "(LDS and wait counters) and PROF_DIR/pmc_t (texture unit and issue counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-times", action="store_true",
                     help="skip the per-virtual-rank FFN timing (for counter runs)")
@@ -495,6 +498,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args.workload, *args.summarize_profile)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.workload, args.summarize_counters[0])
         return
     if args.summarize_runs:
         summarize_runs(args.summarize_runs[2:], args.summarize_runs[0], args.summarize_runs[1])
@@ -982,6 +988,72 @@ def _traffic_records(data):
     """The gate/up GEMM's traffic records by workload (a file holding a single
     record is read as one workload's)."""
     return {data["workload"]: data} if "workload" in data else data
+
+
+STALL_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+                  "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
+                  "GRBM_GUI_ACTIVE"]
+ISSUE_COUNTERS = ["TA_TA_BUSY", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_VMEM",
+                  "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_counters(workload, prof_dir):
+    """Where the waves of the step's long kernels spend their time, from two
+    counter runs of the same command (pmc_s: STALL_COUNTERS, pmc_t:
+    ISSUE_COUNTERS): shares of wave cycles spent waiting (any dependency; LDS
+    results), LDS bank conflicts over LDS-active cycles, and the texture
+    unit's busy cycles over the launch's cycles (GRBM_GUI_ACTIVE / 8 XCDs,
+    per TA instance, one per CU).  Ratios of counters of one run only, so no
+    unit conversion between counter blocks is assumed.  Writes
+    profiles/counters_<workload>.md."""
+    import collections
+    runs = {}
+    for sub, names in (("pmc_s", STALL_COUNTERS), ("pmc_t", ISSUE_COUNTERS)):
+        path = os.path.join(prof_dir, sub, "p_counter_collection.csv")
+        for c in names:
+            for i, (n, d, v) in enumerate(_dispatches(path, c)):
+                runs.setdefault((sub, n), collections.defaultdict(list))[c].append(v)
+    kernels = sorted({n for (_, n) in runs}, key=lambda n: n)
+    keep = [n for n in kernels if n.startswith(("gate_topk", "ffn_persistent", "combine_kernel"))]
+    lines = [f"# Wave stall counters of the step's long kernels, {workload}, one MI355X", "",
+             "Per kernel, averaged over its launches; ratios of counters of one run.  wait any: "
+             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waves waiting for any dependency: memory, LDS, barrier); "
+             "wait LDS: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; LDS conflicts: SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE; LDS active: SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES; VALU active: "
+             "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES; TA busy: TA_TA_BUSY / (GRBM_GUI_ACTIVE / 8 x CUs); "
+             "instructions per wave-launch mix from SQ_INSTS_*.", "",
+             "| kernel | launches | wait any | wait LDS | LDS active | LDS conflicts | VALU active | TA busy | "
+             "MFMA : LDS : VALU : VMEM instructions |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    cus = 256
+
+    def mean(xs):
+        return sum(xs) / len(xs) if xs else float("nan")
+
+    for n in keep:
+        s_, t_ = runs.get(("pmc_s", n)), runs.get(("pmc_t", n))
+        if not s_ or not t_:
+            continue
+        wc = s_["SQ_WAVE_CYCLES"]
+        r = lambda a, b: mean([x / y for x, y in zip(a, b) if y])  # noqa: E731
+        ta = r(t_["TA_TA_BUSY"], [g / 8 * cus for g in t_["GRBM_GUI_ACTIVE"]])
+        mix = [mean(t_[c]) for c in ("SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_VMEM")]
+        base = mix[0] if mix[0] else 1.0
+        lines.append(f"| `{n}` | {len(wc)} | {r(s_['SQ_WAIT_INST_ANY'], wc):.2f} | {r(s_['SQ_WAIT_INST_LDS'], wc):.2f} | "
+                     f"{r(s_['SQ_ACTIVE_INST_LDS'], wc):.2f} | "
+                     f"{r(s_['SQ_LDS_BANK_CONFLICT'], s_['SQ_LDS_IDX_ACTIVE']):.3f} | "
+                     f"{r(s_['SQ_ACTIVE_INST_VALU'], wc):.2f} | {ta:.2f} | "
+                     + " : ".join(f"{m / base:.2f}" for m in mix) + " |")
+    cmd = (f"python -u bench.py --workload {workload} --steps 2 --warmup 0 --no-cpu-baseline --no-rank-times")
+    lines += ["", "Commands (repository root; each counter set in a run of its own; any output directory):", "",
+              "```", "export TMPDIR=/tmp; mkdir -p prof", f"B='{cmd}'",
+              "rocprofv3 --pmc " + " ".join(STALL_COUNTERS) + " --output-format csv -d prof/pmc_s -o p -- $B",
+              "rocprofv3 --pmc " + " ".join(ISSUE_COUNTERS) + " --output-format csv -d prof/pmc_t -o p -- $B",
+              f"python bench.py --workload {workload} --summarize-counters prof", "```", ""]
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"counters_{workload}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("wrote", out)
 
 
 def summarize_runs(paths, out_name, command):

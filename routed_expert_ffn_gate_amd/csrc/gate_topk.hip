@@ -551,28 +551,39 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_topk_dma_kernel(
   for (int i = 0; i < MI; ++i) xa[i] = *reinterpret_cast<const bf16x8_t*>(lds + arow0 + i * 16 * BK + kofs[0]);
 #pragma unroll
   for (int i = 0; i < NF; ++i) xb[i] = *reinterpret_cast<const bf16x8_t*>(lds + brow0 + i * 16 * BK + kofs[0]);
-  for (int kt = 0; kt < KT; ++kt) {
-    // first sub-step; second part of the refill of the stage freed one step ago
-    const bool p2 = S >= 3 && kt >= 1 && kt - 1 + S < KT;
-    GT_SUB(xa, xb, ya, yb, lds + (kt % S) * STAGE, 1, true, p2, kt - 1 + S, H1, VPS)
-    const bool more = kt + 1 < KT;
-    if (more) {
-      // step kt+1 landed: the steps issued after it (up to kt+S-1, all of
-      // their instructions issued by now) may still be in flight; lgkmcnt(0):
-      // this wave's reads of step kt are done before its stage is refilled
-      const int ahead = min(S - 2, KT - 2 - kt);
-      if (ahead >= 2)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * VPS) : "memory");
-      else if (ahead == 1)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VPS) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
-    // second sub-step; first part of the refill of step kt's stage with step kt+S
-    GT_SUB(ya, yb, xa, xb, lds + ((kt + 1) % S) * STAGE, 0, more, more && kt + S < KT, kt + S, 0, H1)
+  // One K step.  P2: second part of the refill of the stage freed one step
+  // ago (during the first sub-step); MORE: a step follows -- wait until it
+  // landed (the AHEAD steps issued after it, all of their instructions issued
+  // by now, may still be in flight; lgkmcnt(0): this wave's reads of step kt
+  // are done before its stage is refilled), barrier; R2: first part of the
+  // refill of step kt's stage with step kt+S (during the second sub-step).
+  // The steady steps run with literal flags, so their body has no branch.
+#define GT_STEP(P2, MORE, R2, AHEAD)                                                               \
+  {                                                                                                \
+    GT_SUB(xa, xb, ya, yb, lds + (kt % S) * STAGE, 1, true, (P2), kt - 1 + S, H1, VPS)             \
+    if (MORE) {                                                                                    \
+      const int ahead_ = (AHEAD);                                                                  \
+      if (ahead_ >= 2)                                                                             \
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * VPS) : "memory");                   \
+      else if (ahead_ == 1)                                                                        \
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VPS) : "memory");                       \
+      else                                                                                         \
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                                \
+      __builtin_amdgcn_s_barrier();                                                                \
+      asm volatile("" ::: "memory");                                                               \
+    }                                                                                              \
+    GT_SUB(ya, yb, xa, xb, lds + ((kt + 1) % S) * STAGE, 0, (MORE), (R2), kt + S, 0, H1)           \
   }
+#define GT_STEP_ANY                                                                                \
+  GT_STEP(S >= 3 && kt >= 1 && kt - 1 + S < KT, kt + 1 < KT, kt + 1 < KT && kt + S < KT,          \
+          min(S - 2, KT - 2 - kt))
+  int kt = 0;
+  GT_STEP_ANY
+  // steps 1 .. KT-S-1: every refill issued, S-2 steps in flight at the wait
+  for (kt = 1; kt + S < KT; ++kt) GT_STEP(S >= 3, true, true, S - 2)
+  for (; kt < KT; ++kt) GT_STEP_ANY
+#undef GT_STEP_ANY
+#undef GT_STEP
 #undef GT_COPY
 #undef GT_SUB
   __syncthreads();  // LDS is reused for the logits
