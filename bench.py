@@ -1021,9 +1021,9 @@ def summarize_counters(workload, prof_dir):
              "wait LDS: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; LDS conflicts: SQ_LDS_BANK_CONFLICT / "
              "SQ_LDS_IDX_ACTIVE; LDS active: SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES; VALU active: "
              "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES; TA busy: TA_TA_BUSY / (GRBM_GUI_ACTIVE / 8 x CUs); "
-             "instructions per wave-launch mix from SQ_INSTS_*.", "",
+             "instruction mix: shares of SQ_INSTS_MFMA, _LDS, _VALU and _VMEM in their sum.", "",
              "| kernel | launches | wait any | wait LDS | LDS active | LDS conflicts | VALU active | TA busy | "
-             "MFMA : LDS : VALU : VMEM instructions |",
+             "MFMA / LDS / VALU / VMEM instructions |",
              "|---|---|---|---|---|---|---|---|---|"]
     cus = 256
 
@@ -1038,12 +1038,13 @@ def summarize_counters(workload, prof_dir):
         r = lambda a, b: mean([x / y for x, y in zip(a, b) if y])  # noqa: E731
         ta = r(t_["TA_TA_BUSY"], [g / 8 * cus for g in t_["GRBM_GUI_ACTIVE"]])
         mix = [mean(t_[c]) for c in ("SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_VMEM")]
-        base = mix[0] if mix[0] else 1.0
+        tot = sum(mix) or 1.0
+        conf = r(s_['SQ_LDS_BANK_CONFLICT'], s_['SQ_LDS_IDX_ACTIVE'])
         lines.append(f"| `{n}` | {len(wc)} | {r(s_['SQ_WAIT_INST_ANY'], wc):.2f} | {r(s_['SQ_WAIT_INST_LDS'], wc):.2f} | "
                      f"{r(s_['SQ_ACTIVE_INST_LDS'], wc):.2f} | "
-                     f"{r(s_['SQ_LDS_BANK_CONFLICT'], s_['SQ_LDS_IDX_ACTIVE']):.3f} | "
+                     + ("-" if conf != conf else f"{conf:.3f}") + " | "
                      f"{r(s_['SQ_ACTIVE_INST_VALU'], wc):.2f} | {ta:.2f} | "
-                     + " : ".join(f"{m / base:.2f}" for m in mix) + " |")
+                     + " / ".join(f"{m / tot:.2f}" for m in mix) + " |")
     cmd = (f"python -u bench.py --workload {workload} --steps 2 --warmup 0 --no-cpu-baseline --no-rank-times")
     lines += ["", "Commands (repository root; each counter set in a run of its own; any output directory):", "",
               "```", "export TMPDIR=/tmp; mkdir -p prof", f"B='{cmd}'",
