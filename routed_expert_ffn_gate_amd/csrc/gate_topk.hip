@@ -45,26 +45,12 @@ __device__ __forceinline__ uint32_t topk_key(float v, int id) {
 __device__ __forceinline__ uint64_t topk_key_exact(float v, int id) {
   return ((uint64_t)ordered_bits(v) << 8) | (uint64_t)(255 - id);
 }
-__device__ __forceinline__ uint32_t make_key(float v, int id, uint32_t) { return topk_key(v, id); }
-__device__ __forceinline__ uint64_t make_key(float v, int id, uint64_t) { return topk_key_exact(v, id); }
 
-// Sorted (descending) insertion into a register list of KL keys: one max and
-// one min per list entry.
-template <int KL, typename Key>
-__device__ __forceinline__ void list_insert(Key (&l)[KL], Key x) {
-#pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    const Key hi = x > l[i] ? x : l[i];
-    x = x > l[i] ? l[i] : x;
-    l[i] = hi;
-  }
-}
-
-// The same for 32-bit keys in one instruction per entry: in a descending list
-// the new entry i is the median of x, the old entry i and the old entry i-1
-// (x itself where it belongs, the entry above it shifted down below that,
-// the old entry above), so every entry is computed from the old list, last
-// entry first, with no chain between them.
+// Sorted (descending) insertion of key x into a register list of KL keys, one
+// instruction per entry: the new entry i is the median of x, the old entry i
+// and the old entry i-1 (x itself where it belongs, the entry above it
+// shifted down below that, the old entry above), so every entry is computed
+// from the old list, last entry first, with no chain between them.
 __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t r;
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -104,20 +90,20 @@ __device__ __forceinline__ void merge_round(uint32_t (&l)[KL]) {
 // inserts), then the partial lists are merged across those lanes, so every
 // lane ends with the whole list.  All lanes of the wave take part (inactive
 // tokens scan nothing), in uniform control flow.
-template <int KL, typename Key>
-__device__ __forceinline__ void select_keys(const float* row, bool active, int E, int sub, int lpt, Key (&l)[KL]) {
+template <int KL>
+__device__ __forceinline__ void select_keys(const float* row, bool active, int E, int sub, int lpt, uint32_t (&l)[KL]) {
 #pragma unroll
   for (int i = 0; i < KL; ++i) l[i] = 0;  // below every real key
   if (active) {
     int e = sub;
     for (; e + 3 * lpt < E; e += 4 * lpt) {
       const float v0 = row[e], v1 = row[e + lpt], v2 = row[e + 2 * lpt], v3 = row[e + 3 * lpt];
-      list_insert<KL>(l, make_key(v0, e, Key(0)));
-      list_insert<KL>(l, make_key(v1, e + lpt, Key(0)));
-      list_insert<KL>(l, make_key(v2, e + 2 * lpt, Key(0)));
-      list_insert<KL>(l, make_key(v3, e + 3 * lpt, Key(0)));
+      list_insert<KL>(l, topk_key(v0, e));
+      list_insert<KL>(l, topk_key(v1, e + lpt));
+      list_insert<KL>(l, topk_key(v2, e + 2 * lpt));
+      list_insert<KL>(l, topk_key(v3, e + 3 * lpt));
     }
-    for (; e < E; e += lpt) list_insert<KL>(l, make_key(row[e], e, Key(0)));
+    for (; e < E; e += lpt) list_insert<KL>(l, topk_key(row[e], e));
   }
   if (lpt > 1) merge_round<1>(l);
   if (lpt > 2) merge_round<2>(l);
