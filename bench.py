@@ -195,7 +195,10 @@ def time_split_variants(layer, home, replica_cur, stream, reps=20):
                                ("jacobi", M.MOELB_SPLIT_JACOBI, layer.passes),
                                ("libra_greedy", M.MOELB_SPLIT_LIBRA_GREEDY, layer.passes),
                                ("water_fill", M.MOELB_SPLIT_WATER_FILL, layer.passes),
+                               ("proportional", M.MOELB_SPLIT_PROPORTIONAL, layer.passes),
                                ("hash", M.MOELB_SPLIT_RELIEF, 0)):
+        if code == M.MOELB_SPLIT_PROPORTIONAL and layer.G > 16:
+            continue  # exact shares for at most 16 hosts per expert
         ev = HipEvents(2)
         ev.record(0, stream)
         for _ in range(reps):

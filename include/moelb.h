@@ -218,6 +218,12 @@ int moelb_plan_swaps(const int32_t* counts, const int32_t* home, int G, int E, i
  *                           one each to hosts with l_h <= z (ascending rank);
  *                           stops after a pass that changes nothing (eps and
  *                           the schedule are not used).
+ *  MOELB_SPLIT_PROPORTIONAL as MOELB_SPLIT_WATER_FILL, but each pool is
+ *                           re-dealt in proportion to 1 / (l_h + 1), exactly:
+ *                           host h gets the floor of its rational share, and
+ *                           the tokens left go one each to the hosts with the
+ *                           largest remainders (ties: lower rank).  Requires
+ *                           G <= 16 (else MOELB_EINVAL).
  * Same arguments, outputs and requirements as moelb_split; counts must be
  * non-negative.  An unknown variant returns MOELB_EINVAL.
  */
@@ -244,7 +250,8 @@ enum moelb_split_variant {
   MOELB_SPLIT_NO_REVERSE = 1,
   MOELB_SPLIT_JACOBI = 2,
   MOELB_SPLIT_LIBRA_GREEDY = 3,
-  MOELB_SPLIT_WATER_FILL = 4
+  MOELB_SPLIT_WATER_FILL = 4,
+  MOELB_SPLIT_PROPORTIONAL = 5
 };
 int moelb_split_variant(const int32_t* counts, const int32_t* home, const int32_t* replica,
                         int G, int E, int N, int passes, int eps, int variant,

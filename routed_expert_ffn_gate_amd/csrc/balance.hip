@@ -824,20 +824,136 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_kernel(const int32_t* __r
   for (int r = lane; r < G; r += 64) load_out[r] = load[r];
 }
 
-// ---------------------------------------------------------------- water-filling split
+// ---------------------------------------------------------------- water-filling and proportional splits
 
-// Relief's water-filling ablation ("Ablation Results (Table III)"; the rule is
-// a reading): replicated pools start from the even split; each pass, every
-// replicated expert redistributes its whole pool R over its hosts from one
-// snapshot of the loads, less its own mass on each host (levels l_h): the
-// largest level z with sum_h max(0, z - l_h) <= R is filled, and the tokens
-// left go one each to the hosts with l_h <= z in ascending rank.  Stops after
-// a pass that changes nothing.  One thread per expert; host_count holds the
-// masses between passes.
+// Unsigned integers of PW 32-bit words, least significant first, for the
+// proportional rule's exact shares: with at most PROP_MAX_HOSTS hosts, a
+// product of the other hosts' (level + 1), each at most 2^31, times a pool
+// below 2^31, stays below 2^496.
+constexpr int PW = 16;
+constexpr int PROP_MAX_HOSTS = 16;
+
+__device__ __forceinline__ void big_set(uint32_t (&a)[PW], uint32_t v) {
+#pragma unroll
+  for (int i = 0; i < PW; ++i) a[i] = i == 0 ? v : 0u;
+}
+__device__ __forceinline__ void big_copy(uint32_t (&a)[PW], const uint32_t (&b)[PW]) {
+#pragma unroll
+  for (int i = 0; i < PW; ++i) a[i] = b[i];
+}
+__device__ __forceinline__ void big_mul(uint32_t (&a)[PW], uint32_t f) {
+  uint64_t c = 0;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const uint64_t t = (uint64_t)a[i] * f + c;
+    a[i] = (uint32_t)t;
+    c = t >> 32;
+  }
+}
+__device__ __forceinline__ void big_add(uint32_t (&a)[PW], const uint32_t (&b)[PW]) {
+  uint64_t c = 0;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const uint64_t t = (uint64_t)a[i] + b[i] + c;
+    a[i] = (uint32_t)t;
+    c = t >> 32;
+  }
+}
+// a -= b, for a >= b
+__device__ __forceinline__ void big_sub(uint32_t (&a)[PW], const uint32_t (&b)[PW]) {
+  int64_t br = 0;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int64_t t = (int64_t)a[i] - (int64_t)b[i] - br;
+    a[i] = (uint32_t)t;
+    br = t < 0 ? 1 : 0;
+  }
+}
+__device__ __forceinline__ int big_cmp(const uint32_t (&a)[PW], const uint32_t (&b)[PW]) {
+#pragma unroll
+  for (int i = PW - 1; i >= 0; --i)
+    if (a[i] != b[i]) return a[i] < b[i] ? -1 : 1;
+  return 0;
+}
+// p = product of f[j] over j != r
+__device__ __forceinline__ void big_prod_except(uint32_t (&p)[PW], const uint32_t* f, int m, int r) {
+  big_set(p, 1u);
+  for (int j = 0; j < m; ++j)
+    if (j != r) big_mul(p, f[j]);
+}
+
+// Relief's proportional relaxation ("Ablation Results (Table III)"; the rule
+// is a reading): R tokens over m hosts in proportion to 1 / (l_j + 1), with
+// f[j] = l_j + 1 and hosts in ascending rank.  Host r's exact share is
+// R P_r / S, P_r the product of the other hosts' f and S the sum of the P_r;
+// each host gets the floor, and the R - sum(floors) hosts with the largest
+// remainders R P_r mod S (ties: lower rank) one more.  The floor starts from a
+// double estimate (off by at most one) and is settled by exact comparisons.
+__device__ void proportional_shares(int R, int m, const uint32_t* f, int* give) {
+  uint32_t S[PW], P[PW], RP[PW], T[PW];
+  big_set(S, 0u);
+  double tot = 0.0;
+  for (int r = 0; r < m; ++r) {
+    big_prod_except(P, f, m, r);
+    big_add(S, P);
+    tot += 1.0 / (double)f[r];
+  }
+  uint32_t rem[PROP_MAX_HOSTS][PW];
+  int sumq = 0;
+  for (int r = 0; r < m; ++r) {
+    big_prod_except(RP, f, m, r);
+    big_mul(RP, (uint32_t)R);
+    int q = (int)floor((double)R / (double)f[r] / tot);
+    q = min(max(q, 0), R);
+    for (;;) {  // q S <= R P_r (q = 0 always holds)
+      big_copy(T, S);
+      big_mul(T, (uint32_t)q);
+      if (q > 0 && big_cmp(T, RP) > 0)
+        --q;
+      else
+        break;
+    }
+    for (;;) {  // (q + 1) S > R P_r (holds by q = R, as P_r <= S)
+      big_copy(T, S);
+      big_mul(T, (uint32_t)(q + 1));
+      if (big_cmp(T, RP) <= 0)
+        ++q;
+      else
+        break;
+    }
+    big_copy(T, S);
+    big_mul(T, (uint32_t)q);
+    big_copy(rem[r], RP);
+    big_sub(rem[r], T);
+    give[r] = q;
+    sumq += q;
+  }
+  const int left = R - sumq;
+  for (int r = 0; r < m; ++r) {
+    int above = 0;  // hosts whose remainder ranks before r's
+    for (int j = 0; j < m; ++j) {
+      const int c = big_cmp(rem[j], rem[r]);
+      above += (c > 0 || (c == 0 && j < r)) ? 1 : 0;
+    }
+    if (above < left) ++give[r];
+  }
+}
+
+// Relief's water-filling and proportional ablations ("Ablation Results
+// (Table III)"; the rules are readings): replicated pools start from the even
+// split; each pass, every replicated expert redistributes its whole pool R
+// over its hosts from one snapshot of the loads, less its own mass on each
+// host (levels l_h).  Water filling (prop = 0): the largest level z with
+// sum_h max(0, z - l_h) <= R is filled, and the tokens left go one each to the
+// hosts with l_h <= z in ascending rank.  Proportional (prop = 1): shares in
+// proportion to 1 / (l_h + 1), exactly (proportional_shares; at most
+// PROP_MAX_HOSTS hosts, i.e. G <= 16).  Stops after a pass that changes
+// nothing.  One thread per expert; host_count holds the masses between passes.
 __global__ __launch_bounds__(SPLIT_THREADS) void split_water_fill_kernel(const int32_t* __restrict__ counts,
                                                                           const int32_t* __restrict__ home,
                                                                           const int32_t* __restrict__ replica,
                                                                           int G, int E, int N, int passes,
+                                                                          int prop,
                                                                           int32_t* __restrict__ host_count,
                                                                           int32_t* __restrict__ load_out) {
   __shared__ unsigned long long hostmask[MOELB_MAX_E];
@@ -888,7 +1004,26 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_water_fill_kernel(const i
     for (int r = tid; r < G; r += blockDim.x) snap[r] = load[r];
     if (tid == 0) changed = 0;
     __syncthreads();
-    if (repl) {
+    if (repl && prop) {
+      uint32_t f[PROP_MAX_HOSTS];
+      int hs[PROP_MAX_HOSTS], give[PROP_MAX_HOSTS];
+      int mh = 0;
+      for (int h = 0; h < G && mh < PROP_MAX_HOSTS; ++h)
+        if ((mask >> h) & 1ull) {
+          hs[mh] = h;
+          f[mh] = (uint32_t)(snap[h] - x[h]) + 1u;
+          ++mh;
+        }
+      proportional_shares(R, mh, f, give);
+      for (int j = 0; j < mh; ++j) {
+        const int h = hs[j];
+        if (give[j] != x[h]) {
+          changed = 1;
+          atomicAdd(&load[h], give[j] - x[h]);
+          x[h] = give[j];
+        }
+      }
+    } else if (repl) {
       int lo = INT_MAX;
       for (int h = 0; h < G; ++h)
         if ((mask >> h) & 1ull) lo = min(lo, snap[h] - x[h]);
@@ -1048,12 +1183,15 @@ extern "C" int moelb_split_scheduled(const int32_t* counts, const int32_t* home,
                                      int32_t* host_count, int32_t* load, void* stream) {
   if (G < 1 || G > MOELB_MAX_G || E < 1 || E > MOELB_MAX_E || N < 0 || N > MOELB_MAX_N) return MOELB_EINVAL;
   if (passes < 0 || passes > 1024 || eps < 0) return MOELB_EINVAL;
-  if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_WATER_FILL) return MOELB_EINVAL;
+  if (variant < MOELB_SPLIT_RELIEF || variant > MOELB_SPLIT_PROPORTIONAL) return MOELB_EINVAL;
+  // the proportional rule's exact arithmetic holds at most 16 hosts per expert
+  if (variant == MOELB_SPLIT_PROPORTIONAL && G > 16) return MOELB_EINVAL;
   if (!counts || !home || (N > 0 && !replica) || !host_count || !load) return MOELB_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (variant == MOELB_SPLIT_WATER_FILL) {
+  if (variant == MOELB_SPLIT_WATER_FILL || variant == MOELB_SPLIT_PROPORTIONAL) {
     hipLaunchKernelGGL(split_water_fill_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home,
-                       N > 0 ? replica : home, G, E, N, passes, host_count, load);
+                       N > 0 ? replica : home, G, E, N, passes, variant == MOELB_SPLIT_PROPORTIONAL ? 1 : 0,
+                       host_count, load);
     MOELB_CHECK_LAUNCH();
     return MOELB_OK;
   }

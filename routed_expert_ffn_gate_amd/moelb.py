@@ -134,7 +134,7 @@ def moelb_split(counts, home, replica, host_count, load, passes=12, eps=0, strea
 
 
 MOELB_SPLIT_RELIEF, MOELB_SPLIT_NO_REVERSE, MOELB_SPLIT_JACOBI, MOELB_SPLIT_LIBRA_GREEDY = 0, 1, 2, 3
-MOELB_SPLIT_WATER_FILL = 4
+MOELB_SPLIT_WATER_FILL, MOELB_SPLIT_PROPORTIONAL = 4, 5
 
 
 def moelb_split_variant(counts, home, replica, host_count, load, variant, passes=12, eps=0, stream=None):

@@ -61,7 +61,9 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert lib.moelb_split(P, P, P, 4, 8, 1, -1, 0, P, P, N) == 1
     assert lib.moelb_split(P, P, P, 4, 8, 1, 12, -1, P, P, N) == 1
     # unknown split variant; negative passes for a variant
-    assert lib.moelb_split_variant(P, P, P, 4, 8, 1, 12, 0, 5, P, P, N) == 1
+    assert lib.moelb_split_variant(P, P, P, 4, 8, 1, 12, 0, 6, P, P, N) == 1
+    # proportional split beyond 16 ranks
+    assert lib.moelb_split_variant(P, P, P, 32, 32, 1, 12, 0, 5, P, P, N) == 1
     assert lib.moelb_split_variant(P, P, P, 4, 8, 1, -1, 0, 3, P, P, N) == 1
     # stale split: shares written over the earlier ones; no earlier shares
     assert lib.moelb_split_stale(P, P, P, 4, 8, 1, P, P, P, N) == 1

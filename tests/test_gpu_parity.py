@@ -425,7 +425,7 @@ def test_split_variants_random_instances(moelb):
     rng = np.random.default_rng(17)
     codes = {"relief": M.MOELB_SPLIT_RELIEF, "no_reverse": M.MOELB_SPLIT_NO_REVERSE,
              "jacobi": M.MOELB_SPLIT_JACOBI, "libra_greedy": M.MOELB_SPLIT_LIBRA_GREEDY,
-             "water_fill": M.MOELB_SPLIT_WATER_FILL}
+             "water_fill": M.MOELB_SPLIT_WATER_FILL, "proportional": M.MOELB_SPLIT_PROPORTIONAL}
     for trial in range(48):
         G = int(rng.choice([2, 4, 8, 16, 64]))
         E = G * int(rng.choice([1, 2, 4])) if G < 64 else int(rng.choice([64, 128, 256]))
@@ -438,13 +438,43 @@ def test_split_variants_random_instances(moelb):
         passes = int(rng.choice([0, 1, 3, 12]))
         ct, ht, rt = (torch.from_numpy(a).to(dev) for a in (c, home, rep))
         for name, code in codes.items():
-            eps = 0 if name in ("libra_greedy", "water_fill") else int(rng.choice([0, 0, 2]))
+            if name == "proportional" and G > 16:
+                continue  # its exact arithmetic holds at most 16 hosts per expert
+            eps = 0 if name in ("libra_greedy", "water_fill", "proportional") else int(rng.choice([0, 0, 2]))
             hc = torch.empty((E, G), dtype=torch.int32, device=dev)
             ld = torch.empty(G, dtype=torch.int32, device=dev)
             M.moelb_split_variant(ct, ht, rt, hc, ld, code, passes=passes, eps=eps)
             hc_o, ld_o = V.split_variant(c, home, rep, G, E, name, passes=passes, eps=eps)
             assert np.array_equal(hc.cpu().numpy(), hc_o), (trial, name, G, E, N, passes)
             assert np.array_equal(ld.cpu().numpy(), ld_o), (trial, name)
+
+
+def test_split_proportional_large_loads(moelb):
+    """The proportional split's exact shares (products of up to 15 host loads
+    of about 2^26, several hundred bits) against the oracle's rationals, bit
+    for bit, with 16 ranks whose experts have up to 16 hosts."""
+    from oracle import moe_oracle as O
+    from oracle import split_variants as V
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(29)
+    for trial in range(6):
+        G, E, N = 16, int(rng.choice([16, 32])), 8
+        L = int(rng.integers(0, N + 1))
+        pop = 1.0 / (1 + rng.permutation(E)) ** rng.uniform(0.8, 1.4)
+        c = np.stack([rng.multinomial(int(rng.integers(1 << 24, 1 << 26)), pop / pop.sum())
+                      for _ in range(G)]).astype(np.int32)
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = O.plan(c, home, G, E, N, L)
+        hosts = 1 + np.array([(rep == e).any(axis=1).sum() for e in range(E)])
+        log(f"[split proportional] trial {trial}: E={E} L={L} max hosts {hosts.max()}")
+        ct, ht, rt = (torch.from_numpy(a).to(dev) for a in (c, home, rep))
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split_variant(ct, ht, rt, hc, ld, M.MOELB_SPLIT_PROPORTIONAL, passes=12)
+        hc_o, ld_o = V.split_variant(c, home, rep, G, E, "proportional", passes=12)
+        assert np.array_equal(hc.cpu().numpy(), hc_o), trial
+        assert np.array_equal(ld.cpu().numpy(), ld_o), trial
 
 
 def test_split_stale_random_instances(moelb):
