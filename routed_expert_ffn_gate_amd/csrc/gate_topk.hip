@@ -63,17 +63,15 @@ __device__ __forceinline__ void list_insert(uint32_t (&l)[KL], uint32_t x) {
   l[0] = x > l[0] ? x : l[0];
 }
 
-// Partner key in the merge round of lane groups of 2M: rounds 1 and 2 swap
-// within quads, round 4 mirrors each half-row of 8 lanes and round 8 each row
-// of 16 (DPP, no LDS round trip); wider groups shuffle.  Any pairing that
-// joins the two halves of every group of 2M lanes merges correctly.
+// Partner key in the merge round of lane groups of 2M (DPP, no LDS round
+// trip): rounds 1 and 2 swap within quads, round 4 mirrors each half-row of 8
+// lanes.  Any pairing that joins the two halves of every group of 2M lanes
+// merges correctly.
 template <int M>
 __device__ __forceinline__ uint32_t merge_partner(uint32_t v) {
-  constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
-  if constexpr (M <= 8)
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
-  else
-    return __shfl_xor(v, M, MOELB_WAVE);
+  static_assert(M == 1 || M == 2 || M == 4, "token groups of 2, 4 or 8 lanes");
+  constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : 0x141;
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
 }
 
 template <int M, int KL>
@@ -108,9 +106,6 @@ __device__ __forceinline__ void select_keys(const float* row, bool active, int E
   if (lpt > 1) merge_round<1>(l);
   if (lpt > 2) merge_round<2>(l);
   if (lpt > 4) merge_round<4>(l);
-  if (lpt > 8) merge_round<8>(l);
-  if (lpt > 16) merge_round<16>(l);
-  if (lpt > 32) merge_round<32>(l);
 }
 
 // Epilogue over `ntok` tokens whose logits (bias included) sit in LDS rows of
