@@ -875,12 +875,20 @@ __device__ __forceinline__ int big_cmp(const uint32_t (&a)[PW], const uint32_t (
     if (a[i] != b[i]) return a[i] < b[i] ? -1 : 1;
   return 0;
 }
-// p = product of f[j] over j != r
-__device__ __forceinline__ void big_prod_except(uint32_t (&p)[PW], const uint32_t* f, int m, int r) {
+// p = product of f[j] over j < m, j != r (f indexed by constants only, so it
+// stays in registers)
+__device__ __forceinline__ void big_prod_except(uint32_t (&p)[PW], const uint32_t (&f)[PROP_MAX_HOSTS], int m,
+                                                int r) {
   big_set(p, 1u);
-  for (int j = 0; j < m; ++j)
-    if (j != r) big_mul(p, f[j]);
+#pragma unroll
+  for (int j = 0; j < PROP_MAX_HOSTS; ++j)
+    if (j < m && j != r) big_mul(p, f[j]);
 }
+
+// A remainder estimate in double is within 1e-5 of the exact fractional share
+// (R < 2^31, about twenty roundings of 2^-53); estimates further apart than
+// this band order the remainders without the exact comparison.
+constexpr double PROP_BAND = 1e-4;
 
 // Relief's proportional relaxation ("Ablation Results (Table III)"; the rule
 // is a reading): R tokens over m hosts in proportion to 1 / (l_j + 1), with
@@ -888,23 +896,35 @@ __device__ __forceinline__ void big_prod_except(uint32_t (&p)[PW], const uint32_
 // R P_r / S, P_r the product of the other hosts' f and S the sum of the P_r;
 // each host gets the floor, and the R - sum(floors) hosts with the largest
 // remainders R P_r mod S (ties: lower rank) one more.  The floor starts from a
-// double estimate (off by at most one) and is settled by exact comparisons.
-__device__ void proportional_shares(int R, int m, const uint32_t* f, int* give) {
+// double estimate (off by at most one) and is settled by exact comparisons;
+// remainders are ordered by their double estimates, and exactly where two
+// estimates fall within PROP_BAND.
+__device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_HOSTS],
+                                    int (&give)[PROP_MAX_HOSTS]) {
   uint32_t S[PW], P[PW], RP[PW], T[PW];
   big_set(S, 0u);
-  double tot = 0.0;
   for (int r = 0; r < m; ++r) {
     big_prod_except(P, f, m, r);
     big_add(S, P);
-    tot += 1.0 / (double)f[r];
+  }
+  double tot = 0.0;
+  double frac[PROP_MAX_HOSTS];
+#pragma unroll
+  for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
+    if (j < m) tot += 1.0 / (double)f[j];
+    give[j] = 0;
+    frac[j] = 0.0;
   }
   uint32_t rem[PROP_MAX_HOSTS][PW];
   int sumq = 0;
   for (int r = 0; r < m; ++r) {
+    uint32_t fr = 1u;
+#pragma unroll
+    for (int j = 0; j < PROP_MAX_HOSTS; ++j) fr = j == r ? f[j] : fr;
     big_prod_except(RP, f, m, r);
     big_mul(RP, (uint32_t)R);
-    int q = (int)floor((double)R / (double)f[r] / tot);
-    q = min(max(q, 0), R);
+    const double ex = (double)R / (double)fr / tot;
+    int q = min(max((int)floor(ex), 0), R);
     for (;;) {  // q S <= R P_r (q = 0 always holds)
       big_copy(T, S);
       big_mul(T, (uint32_t)q);
@@ -925,17 +945,60 @@ __device__ void proportional_shares(int R, int m, const uint32_t* f, int* give) 
     big_mul(T, (uint32_t)q);
     big_copy(rem[r], RP);
     big_sub(rem[r], T);
-    give[r] = q;
+#pragma unroll
+    for (int j = 0; j < PROP_MAX_HOSTS; ++j)
+      if (j == r) {
+        give[j] = q;
+        frac[j] = ex - (double)q;
+      }
     sumq += q;
   }
   const int left = R - sumq;
-  for (int r = 0; r < m; ++r) {
+  if (left == 0) return;
+#pragma unroll
+  for (int r = 0; r < PROP_MAX_HOSTS; ++r) {
+    if (r >= m) continue;
     int above = 0;  // hosts whose remainder ranks before r's
-    for (int j = 0; j < m; ++j) {
-      const int c = big_cmp(rem[j], rem[r]);
-      above += (c > 0 || (c == 0 && j < r)) ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
+      if (j >= m || j == r) continue;
+      const double dlt = frac[j] - frac[r];
+      if (dlt > PROP_BAND) {
+        ++above;
+      } else if (dlt >= -PROP_BAND) {
+        const int c = big_cmp(rem[j], rem[r]);
+        above += (c > 0 || (c == 0 && j < r)) ? 1 : 0;
+      }
     }
     if (above < left) ++give[r];
+  }
+}
+
+// One proportional pass of one replicated expert (pool R over the m hosts in
+// mask, from the snapshot loads less its own masses x): new masses, their
+// change added to the loads; `changed` set if any mass moved.
+__device__ __forceinline__ void proportional_pass(int R, int m, uint64_t mask, const int* snap, int32_t* x, int* load,
+                                                  int& changed) {
+  // hosts in ascending rank: slot j holds the j-th set bit of mask (G <= 16)
+  uint32_t f[PROP_MAX_HOSTS];
+  int hs[PROP_MAX_HOSTS], give[PROP_MAX_HOSTS];
+  uint64_t mm = mask;
+#pragma unroll
+  for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
+    hs[j] = mm ? __ffsll(static_cast<long long>(mm)) - 1 : 0;
+    f[j] = mm ? (uint32_t)(snap[hs[j]] - x[hs[j]]) + 1u : 1u;
+    mm &= mm - 1ull;
+  }
+  proportional_shares(R, m, f, give);
+#pragma unroll
+  for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
+    if (j >= m) continue;
+    const int h = hs[j];
+    if (give[j] != x[h]) {
+      changed = 1;
+      atomicAdd(&load[h], give[j] - x[h]);
+      x[h] = give[j];
+    }
   }
 }
 
@@ -945,15 +1008,15 @@ __device__ void proportional_shares(int R, int m, const uint32_t* f, int* give) 
 // over its hosts from one snapshot of the loads, less its own mass on each
 // host (levels l_h).  Water filling (prop = 0): the largest level z with
 // sum_h max(0, z - l_h) <= R is filled, and the tokens left go one each to the
-// hosts with l_h <= z in ascending rank.  Proportional (prop = 1): shares in
+// hosts with l_h <= z in ascending rank.  Proportional (PROP): shares in
 // proportion to 1 / (l_h + 1), exactly (proportional_shares; at most
 // PROP_MAX_HOSTS hosts, i.e. G <= 16).  Stops after a pass that changes
 // nothing.  One thread per expert; host_count holds the masses between passes.
+template <bool PROP>
 __global__ __launch_bounds__(SPLIT_THREADS) void split_water_fill_kernel(const int32_t* __restrict__ counts,
                                                                           const int32_t* __restrict__ home,
                                                                           const int32_t* __restrict__ replica,
                                                                           int G, int E, int N, int passes,
-                                                                          int prop,
                                                                           int32_t* __restrict__ host_count,
                                                                           int32_t* __restrict__ load_out) {
   __shared__ unsigned long long hostmask[MOELB_MAX_E];
@@ -1004,25 +1067,8 @@ __global__ __launch_bounds__(SPLIT_THREADS) void split_water_fill_kernel(const i
     for (int r = tid; r < G; r += blockDim.x) snap[r] = load[r];
     if (tid == 0) changed = 0;
     __syncthreads();
-    if (repl && prop) {
-      uint32_t f[PROP_MAX_HOSTS];
-      int hs[PROP_MAX_HOSTS], give[PROP_MAX_HOSTS];
-      int mh = 0;
-      for (int h = 0; h < G && mh < PROP_MAX_HOSTS; ++h)
-        if ((mask >> h) & 1ull) {
-          hs[mh] = h;
-          f[mh] = (uint32_t)(snap[h] - x[h]) + 1u;
-          ++mh;
-        }
-      proportional_shares(R, mh, f, give);
-      for (int j = 0; j < mh; ++j) {
-        const int h = hs[j];
-        if (give[j] != x[h]) {
-          changed = 1;
-          atomicAdd(&load[h], give[j] - x[h]);
-          x[h] = give[j];
-        }
-      }
+    if constexpr (PROP) {
+      if (repl) proportional_pass(R, m, mask, snap, x, load, changed);
     } else if (repl) {
       int lo = INT_MAX;
       for (int h = 0; h < G; ++h)
@@ -1189,9 +1235,12 @@ extern "C" int moelb_split_scheduled(const int32_t* counts, const int32_t* home,
   if (!counts || !home || (N > 0 && !replica) || !host_count || !load) return MOELB_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (variant == MOELB_SPLIT_WATER_FILL || variant == MOELB_SPLIT_PROPORTIONAL) {
-    hipLaunchKernelGGL(split_water_fill_kernel, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home,
-                       N > 0 ? replica : home, G, E, N, passes, variant == MOELB_SPLIT_PROPORTIONAL ? 1 : 0,
-                       host_count, load);
+    if (variant == MOELB_SPLIT_PROPORTIONAL)
+      hipLaunchKernelGGL(split_water_fill_kernel<true>, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home,
+                         N > 0 ? replica : home, G, E, N, passes, host_count, load);
+    else
+      hipLaunchKernelGGL(split_water_fill_kernel<false>, dim3(1), dim3(SPLIT_THREADS), 0, s, counts, home,
+                         N > 0 ? replica : home, G, E, N, passes, host_count, load);
     MOELB_CHECK_LAUNCH();
     return MOELB_OK;
   }
