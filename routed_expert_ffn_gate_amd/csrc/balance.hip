@@ -955,14 +955,15 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
   }
   const int left = R - sumq;
   if (left == 0) return;
+  for (int r = 0; r < m; ++r) {
+    double frac_r = 0.0;  // frac[r], read with constant indexes
 #pragma unroll
-  for (int r = 0; r < PROP_MAX_HOSTS; ++r) {
-    if (r >= m) continue;
+    for (int j = 0; j < PROP_MAX_HOSTS; ++j) frac_r = j == r ? frac[j] : frac_r;
     int above = 0;  // hosts whose remainder ranks before r's
 #pragma unroll
     for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
       if (j >= m || j == r) continue;
-      const double dlt = frac[j] - frac[r];
+      const double dlt = frac[j] - frac_r;
       if (dlt > PROP_BAND) {
         ++above;
       } else if (dlt >= -PROP_BAND) {
@@ -970,7 +971,10 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
         above += (c > 0 || (c == 0 && j < r)) ? 1 : 0;
       }
     }
-    if (above < left) ++give[r];
+    if (above < left) {
+#pragma unroll
+      for (int j = 0; j < PROP_MAX_HOSTS; ++j) give[j] += j == r ? 1 : 0;
+    }
   }
 }
 
