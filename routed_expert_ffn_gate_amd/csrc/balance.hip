@@ -890,6 +890,17 @@ __device__ __forceinline__ void big_prod_except(uint32_t (&p)[PW], const uint32_
 // this band order the remainders without the exact comparison.
 constexpr double PROP_BAND = 1e-4;
 
+// out = R P_r - q S: host r's exact remainder times S, for its floor q
+__device__ __forceinline__ void big_rem(uint32_t (&out)[PW], int R, const uint32_t (&f)[PROP_MAX_HOSTS], int m,
+                                        const uint32_t (&S)[PW], int r, int q) {
+  uint32_t T[PW];
+  big_prod_except(out, f, m, r);
+  big_mul(out, (uint32_t)R);
+  big_copy(T, S);
+  big_mul(T, (uint32_t)q);
+  big_sub(out, T);
+}
+
 // Relief's proportional relaxation ("Ablation Results (Table III)"; the rule
 // is a reading): R tokens over m hosts in proportion to 1 / (l_j + 1), with
 // f[j] = l_j + 1 and hosts in ascending rank.  Host r's exact share is
@@ -897,15 +908,15 @@ constexpr double PROP_BAND = 1e-4;
 // each host gets the floor, and the R - sum(floors) hosts with the largest
 // remainders R P_r mod S (ties: lower rank) one more.  The floor starts from a
 // double estimate (off by at most one) and is settled by exact comparisons;
-// remainders are ordered by their double estimates, and exactly where two
-// estimates fall within PROP_BAND.
+// remainders are ordered by their double estimates, and where two estimates
+// fall within PROP_BAND by exact remainders, formed again for that pair.
 __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_HOSTS],
                                     int (&give)[PROP_MAX_HOSTS]) {
-  uint32_t S[PW], P[PW], RP[PW], T[PW];
+  uint32_t S[PW], RP[PW], T[PW];
   big_set(S, 0u);
   for (int r = 0; r < m; ++r) {
-    big_prod_except(P, f, m, r);
-    big_add(S, P);
+    big_prod_except(T, f, m, r);
+    big_add(S, T);
   }
   double tot = 0.0;
   double frac[PROP_MAX_HOSTS];
@@ -915,7 +926,6 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
     give[j] = 0;
     frac[j] = 0.0;
   }
-  uint32_t rem[PROP_MAX_HOSTS][PW];
   int sumq = 0;
   for (int r = 0; r < m; ++r) {
     uint32_t fr = 1u;
@@ -941,10 +951,6 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
       else
         break;
     }
-    big_copy(T, S);
-    big_mul(T, (uint32_t)q);
-    big_copy(rem[r], RP);
-    big_sub(rem[r], T);
 #pragma unroll
     for (int j = 0; j < PROP_MAX_HOSTS; ++j)
       if (j == r) {
@@ -955,27 +961,43 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
   }
   const int left = R - sumq;
   if (left == 0) return;
+  uint32_t plus = 0;  // hosts that get one more
   for (int r = 0; r < m; ++r) {
-    double frac_r = 0.0;  // frac[r], read with constant indexes
+    double frac_r = 0.0;  // frac[r] and give[r], read with constant indexes
+    int q_r = 0;
 #pragma unroll
-    for (int j = 0; j < PROP_MAX_HOSTS; ++j) frac_r = j == r ? frac[j] : frac_r;
-    int above = 0;  // hosts whose remainder ranks before r's
+    for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
+      frac_r = j == r ? frac[j] : frac_r;
+      q_r = j == r ? give[j] : q_r;
+    }
+    int above = 0;      // hosts whose remainder ranks before r's
+    uint32_t near = 0;  // hosts whose estimate lies within the band of r's
 #pragma unroll
     for (int j = 0; j < PROP_MAX_HOSTS; ++j) {
       if (j >= m || j == r) continue;
       const double dlt = frac[j] - frac_r;
-      if (dlt > PROP_BAND) {
+      if (dlt > PROP_BAND)
         ++above;
-      } else if (dlt >= -PROP_BAND) {
-        const int c = big_cmp(rem[j], rem[r]);
+      else if (dlt >= -PROP_BAND)
+        near |= 1u << j;
+    }
+    if (near) {
+      big_rem(RP, R, f, m, S, r, q_r);
+      while (near) {
+        const int j = __ffs(near) - 1;
+        near &= near - 1u;
+        int q_j = 0;
+#pragma unroll
+        for (int i = 0; i < PROP_MAX_HOSTS; ++i) q_j = i == j ? give[i] : q_j;
+        big_rem(T, R, f, m, S, j, q_j);
+        const int c = big_cmp(T, RP);
         above += (c > 0 || (c == 0 && j < r)) ? 1 : 0;
       }
     }
-    if (above < left) {
-#pragma unroll
-      for (int j = 0; j < PROP_MAX_HOSTS; ++j) give[j] += j == r ? 1 : 0;
-    }
+    if (above < left) plus |= 1u << r;
   }
+#pragma unroll
+  for (int j = 0; j < PROP_MAX_HOSTS; ++j) give[j] += (int)((plus >> j) & 1u);
 }
 
 // One proportional pass of one replicated expert (pool R over the m hosts in

@@ -477,6 +477,35 @@ def test_split_proportional_large_loads(moelb):
         assert np.array_equal(ld.cpu().numpy(), ld_o), trial
 
 
+def test_split_proportional_ties(moelb):
+    """The proportional split where remainders tie or nearly tie, so that the
+    ranking of the leftover tokens rests on exact remainders: equal counts on
+    every rank (hosts with equal loads, equal remainders, ties to the lower
+    rank), and counts near 2^22 that differ by 0-2 between cells (fractional
+    shares within 1e-4 of each other whose exact remainders differ).  Bit for
+    bit against the oracle's rationals."""
+    from oracle import moe_oracle as O
+    from oracle import split_variants as V
+    from routed_expert_ffn_gate_amd import moelb as M
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(31)
+    cases = []
+    for G, E, N, L, v in ((8, 16, 4, 2, 1000), (16, 32, 8, 4, 37), (4, 8, 3, 1, 5)):
+        cases.append((G, E, N, L, np.full((G, E), v, dtype=np.int32)))
+    for G, E, N, L in ((16, 16, 8, 4), (16, 32, 8, 8), (8, 16, 6, 3)):
+        cases.append((G, E, N, L, ((1 << 22) + rng.integers(0, 3, size=(G, E))).astype(np.int32)))
+    for i, (G, E, N, L, c) in enumerate(cases):
+        home = (np.arange(E) // (E // G)).astype(np.int32)
+        rep = O.plan(c, home, G, E, N, L)
+        log(f"[split proportional ties] case {i}: G={G} E={E} N={N} L={L}")
+        ct, ht, rt = (torch.from_numpy(a).to(dev) for a in (c, home, rep))
+        hc = torch.empty((E, G), dtype=torch.int32, device=dev)
+        ld = torch.empty(G, dtype=torch.int32, device=dev)
+        M.moelb_split_variant(ct, ht, rt, hc, ld, M.MOELB_SPLIT_PROPORTIONAL, passes=12)
+        hc_o, ld_o = V.split_variant(c, home, rep, G, E, "proportional", passes=12)
+        assert np.array_equal(hc.cpu().numpy(), hc_o), i
+        assert np.array_equal(ld.cpu().numpy(), ld_o), i
+
 def test_split_stale_random_instances(moelb):
     """The stale split (an earlier step's shares dealt on new counts) against
     its oracle, bit for bit: earlier shares from the split of other counts on
