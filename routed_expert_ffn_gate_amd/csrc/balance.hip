@@ -901,23 +901,32 @@ __device__ __forceinline__ void big_rem(uint32_t (&out)[PW], int R, const uint32
   big_sub(out, T);
 }
 
-// Relief's proportional relaxation ("Ablation Results (Table III)"; the rule
-// is a reading): R tokens over m hosts in proportion to 1 / (l_j + 1), with
-// f[j] = l_j + 1 and hosts in ascending rank.  Host r's exact share is
-// R P_r / S, P_r the product of the other hosts' f and S the sum of the P_r;
-// each host gets the floor, and the R - sum(floors) hosts with the largest
-// remainders R P_r mod S (ties: lower rank) one more.  The floor starts from a
-// double estimate (off by at most one) and is settled by exact comparisons;
-// remainders are ordered by their double estimates, and where two estimates
-// fall within PROP_BAND by exact remainders, formed again for that pair.
-__device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_HOSTS],
-                                    int (&give)[PROP_MAX_HOSTS]) {
-  uint32_t S[PW], RP[PW], T[PW];
+// S = sum over r < m of P_r, the product of the f other than f[r]
+__device__ __forceinline__ void big_pool_sum(uint32_t (&S)[PW], const uint32_t (&f)[PROP_MAX_HOSTS], int m) {
+  uint32_t T[PW];
   big_set(S, 0u);
   for (int r = 0; r < m; ++r) {
     big_prod_except(T, f, m, r);
     big_add(S, T);
   }
+}
+
+// Relief's proportional relaxation ("Ablation Results (Table III)"; the rule
+// is a reading): R tokens over m hosts in proportion to 1 / (l_j + 1), with
+// f[j] = l_j + 1 and hosts in ascending rank.  Host r's exact share is
+// R P_r / S, P_r the product of the other hosts' f and S the sum of the P_r;
+// each host gets the floor, and the R - sum(floors) hosts with the largest
+// remainders R P_r mod S (ties: lower rank) one more.  Each share is first
+// estimated in double.  Where the estimate's fractional part lies at least
+// PROP_BAND from a whole number, its floor is the exact floor; otherwise the
+// floor is settled by exact comparisons.  Remainders are ordered by their
+// estimates, and where two estimates fall within PROP_BAND by exact
+// remainders, formed again for that pair.  S is formed only when one of
+// these exact steps needs it.
+__device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_HOSTS],
+                                    int (&give)[PROP_MAX_HOSTS]) {
+  uint32_t S[PW], RP[PW], T[PW];
+  bool have_s = false;
   double tot = 0.0;
   double frac[PROP_MAX_HOSTS];
 #pragma unroll
@@ -931,25 +940,32 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
     uint32_t fr = 1u;
 #pragma unroll
     for (int j = 0; j < PROP_MAX_HOSTS; ++j) fr = j == r ? f[j] : fr;
-    big_prod_except(RP, f, m, r);
-    big_mul(RP, (uint32_t)R);
     const double ex = (double)R / (double)fr / tot;
     int q = min(max((int)floor(ex), 0), R);
-    for (;;) {  // q S <= R P_r (q = 0 always holds)
-      big_copy(T, S);
-      big_mul(T, (uint32_t)q);
-      if (q > 0 && big_cmp(T, RP) > 0)
-        --q;
-      else
-        break;
-    }
-    for (;;) {  // (q + 1) S > R P_r (holds by q = R, as P_r <= S)
-      big_copy(T, S);
-      big_mul(T, (uint32_t)(q + 1));
-      if (big_cmp(T, RP) <= 0)
-        ++q;
-      else
-        break;
+    const double part = ex - floor(ex);
+    if (part < PROP_BAND || part > 1.0 - PROP_BAND) {
+      if (!have_s) {
+        big_pool_sum(S, f, m);
+        have_s = true;
+      }
+      big_prod_except(RP, f, m, r);
+      big_mul(RP, (uint32_t)R);
+      for (;;) {  // q S <= R P_r (q = 0 always holds)
+        big_copy(T, S);
+        big_mul(T, (uint32_t)q);
+        if (q > 0 && big_cmp(T, RP) > 0)
+          --q;
+        else
+          break;
+      }
+      for (;;) {  // (q + 1) S > R P_r (holds by q = R, as P_r <= S)
+        big_copy(T, S);
+        big_mul(T, (uint32_t)(q + 1));
+        if (big_cmp(T, RP) <= 0)
+          ++q;
+        else
+          break;
+      }
     }
 #pragma unroll
     for (int j = 0; j < PROP_MAX_HOSTS; ++j)
@@ -982,6 +998,10 @@ __device__ void proportional_shares(int R, int m, const uint32_t (&f)[PROP_MAX_H
         near |= 1u << j;
     }
     if (near) {
+      if (!have_s) {
+        big_pool_sum(S, f, m);
+        have_s = true;
+      }
       big_rem(RP, R, f, m, S, r, q_r);
       while (near) {
         const int j = __ffs(near) - 1;

@@ -1,11 +1,14 @@
-"""The proportional split's ordering shortcut (CPU): each pool's remainders
-are ordered by double estimates, R / f_r / sum_j (1 / f_j) less the exact
-floor, and compared exactly only where two estimates lie within 1e-4 of each
-other.  That is sound if every estimate lies within 1e-5 of the exact
-fractional share R P_r / S - floor.  Checked on pools below 2^31 over up to 16
-hosts whose loads are below 2^31 -- equal loads (exact ties), loads that make
-the shares whole numbers, and random ones -- and the resulting shares are
-compared with the exact largest-remainder deal."""
+"""The proportional split's shortcuts (CPU).  Each share is estimated in
+double as R / f_r / sum_j (1 / f_j).  Where the estimate's fractional part
+lies at least 1e-4 from a whole number, its floor is taken as the floor;
+otherwise the floor is settled exactly.  The remainders are ordered by the
+estimates less the floors, and compared exactly only where two estimates lie
+within 1e-4 of each other.  Both shortcuts are sound if every estimate lies
+within 1e-5 of the exact share R P_r / S.  Checked on pools below 2^31 over
+up to 16 hosts whose loads are below 2^31 -- equal loads (exact ties), loads
+that make the shares whole numbers, and random ones: the floors taken from
+estimates equal the exact floors, and the resulting shares equal the exact
+largest-remainder deal."""
 from fractions import Fraction
 import math
 import random
@@ -27,10 +30,15 @@ def _exact(R, f):
 
 
 def _deal(R, f):
-    """Shares as the kernel deals them: exact floors, then the remainders
-    ordered by the estimates, exactly where two are within the band."""
+    """Shares as the kernel deals them: floors from the estimates away from
+    whole numbers (exact ones near them), then the remainders ordered by the
+    estimates, exactly where two are within the band."""
     ex, est = _exact(R, f), _estimates(R, f)
-    q = [math.floor(v) for v in ex]
+    q = []
+    for e, v in zip(est, ex):
+        part = e - math.floor(e)
+        q.append(math.floor(v) if part < BAND or part > 1.0 - BAND else min(max(math.floor(e), 0), R))
+    assert q == [math.floor(v) for v in ex], (R, f)
     frac = [e - qi for e, qi in zip(est, q)]
     rem = [v - qi for v, qi in zip(ex, q)]
     left = R - sum(q)
